@@ -1,0 +1,264 @@
+"""Benchmark of the LongFlow fused decode + score + evict step on one MI355X.
+
+Default workload: the DeepSeek-R1-Distill-Llama-8B-shaped attention layer
+(batch 64, 32 query heads over 8 KV heads, head_dim 128, bfloat16, budget
+3277 = 20% of 16384) in its steady state: every pair holds 3277 tokens and
+every step scores all of them, evicts one per pair and writes the new token
+in place. One step = one lf_decode_step over the whole batch.
+
+Prints ONE JSON line with the throughput, the roofline of the fused kernel
+(algorithmic HBM bytes per launch / average launch time, against the 8 TB/s
+HBM3E peak), the full-KV baseline on the same GPU (same kernel family with
+no eviction over a growing cache) and the CPU oracle on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused decode+evict steps/sec (tokens/s) and achieved HBM GB/s vs MI355X peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, AMD public specification
+KERNEL_SOURCE = os.path.join(ROOT, "decode_kv_cache_02_amd", "csrc", "lf_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama8b_layer.json")
+RING = 64
+
+
+def algorithmic_bytes_per_pair(n: int, G: int, d: int, e: int, evict: bool) -> int:
+    """HBM bytes the method itself must move for one pair and one step.
+
+    Read K and V of the n valid slots, read the query group, write the output
+    group, read k_new and v_new, write the new token's K, V and ||v||_1, write
+    the evicted slot. The ||v||_1 sidecar reads (4 bytes per slot) are
+    excluded: the method could derive them from the V rows it already reads.
+    """
+    return (n * 2 * d * e          # K, V of the valid slots
+            + 2 * G * d * e         # q in, out
+            + 2 * d * e             # k_new, v_new in
+            + 2 * d * e + 4         # slot write: K, V, ||v||_1
+            + (4 if evict else 0))  # evicted slot
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(bytes_alg_per_launch: float):
+    """HBM traffic from committed rocprofv3 --pmc counters, if the kernel is unchanged."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return float(t["hbm_bytes_per_launch"])
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="llama8b_layer")
+    ap.add_argument("--budget", type=int, default=0, help="override the budget")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-kv", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def time_steps(cache, ring, out, ev, steps, warmup):
+    """Run warmup + timed steps on the current stream; returns ms per step."""
+    import torch
+    for t in range(warmup):
+        q, kn, vn = ring[t % RING]
+        cache.decode_step(0, q, kn, vn, out, ev)
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for t in range(steps):
+        q, kn, vn = ring[t % RING]
+        cache.decode_step(0, q, kn, vn, out, ev)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def make_ring(wl, dtype):
+    import torch
+    from decode_kv_cache_02_amd.synth import step_ring
+    q, k, v = step_ring(wl, RING)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = lambda x: torch.from_numpy(x).cuda().to(dt)
+    return [(dev(q[i]), dev(k[i]), dev(v[i])) for i in range(RING)]
+
+
+def cpu_baseline(wl, seconds: float):
+    """The float64 oracle on a bounded sample of the same workload (all pairs,
+    cache full, as many whole-batch steps as fit in ~`seconds`, at least 1)."""
+    from threadpoolctl import threadpool_limits
+    from decode_kv_cache_02_amd.synth import TokenStream
+    from oracle.longflow_oracle import LayerCache
+    with threadpool_limits(limits=1):
+        ts = TokenStream(wl, seed_offset=99)
+        pf = ts.prefill(n_max=wl.budget)
+        layer = LayerCache(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget)
+        layer.prefill(pf.k, pf.v, pf.n_per_seq)
+        del pf
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            st = ts.step()
+            layer.step(st.q, st.k_new, st.v_new)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or steps >= 64:
+                break
+    sps = steps / el
+    return {"value": sps * wl.batch, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "steps_per_s": sps,
+            "sample": f"{steps} whole-batch steps of {wl.name} with every pair full "
+                      f"({wl.batch * wl.num_kv_heads} pairs x {wl.budget} slots), float64 NumPy, "
+                      f"one BLAS thread, {el:.1f} s"}
+
+
+def full_kv_baseline(wl, steps, warmup, fills=(8704, 16384)):
+    """LF_MODE_FULL at the same batch: no eviction, the cache keeps growing."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import device_prefill
+    cap = max(fills) + steps + warmup + 64
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, cap,
+                          dtype=wl.dtype, mode="full")
+    ring = make_ring(wl, wl.dtype)
+    dt = ring[0][0].dtype
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=dt, device="cuda")
+    ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+    res = {}
+    try:
+        for n in fills:
+            k, v = device_prefill(wl, n, seed=7 + n)
+            cache.prefill(0, k, v, np.full(wl.batch, n, dtype=np.int32))
+            del k, v
+            torch.cuda.synchronize()
+            ms = time_steps(cache, ring, out, ev, steps, warmup)
+            nb = wl.batch * wl.num_kv_heads * algorithmic_bytes_per_pair(
+                n + warmup + steps // 2, wl.group, wl.head_dim, 2 if wl.dtype == "bf16" else 4,
+                False)
+            res[str(n)] = {"ms_per_step": ms, "tokens_per_s": wl.batch / ms * 1e3,
+                           "achieved_GBs": nb / ms / 1e6}
+    finally:
+        cache.close()
+    return {"mode": "full-KV decode attention (no eviction, growing cache), same GPU, same batch",
+            "capacity": cap, "at_fill": res}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(each (sequence, KV head) pair is independent: a multi-GPU run would shard "
+              f"the batch with no exchange).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import WORKLOADS, device_prefill
+
+    wl = WORKLOADS[args.workload]
+    if args.budget:
+        wl = wl.with_(budget=args.budget)
+    if args.batch:
+        wl = wl.with_(batch=args.batch)
+    e = 2 if wl.dtype == "bf16" else 4
+    torch.cuda.set_device(0)
+    print(f"[bench] {wl.name}: batch {wl.batch}, {wl.num_q_heads}/{wl.num_kv_heads} heads, "
+          f"d {wl.head_dim}, B {wl.budget}, {wl.dtype}", file=sys.stderr, flush=True)
+
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                          dtype=wl.dtype, mode="evict")
+    k, v = device_prefill(wl, wl.budget, seed=wl.cfg_id)
+    cache.prefill(0, k, v, np.full(wl.batch, wl.budget, dtype=np.int32))
+    del k, v
+    ring = make_ring(wl, wl.dtype)
+    dt = ring[0][0].dtype
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=dt, device="cuda")
+    ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    ms = time_steps(cache, ring, out, ev, args.steps, args.warmup)
+    ev_host = ev.cpu().numpy()
+    assert np.all(ev_host >= 0), "steady state must evict on every pair"
+    pairs = wl.batch * wl.num_kv_heads
+    bytes_launch = pairs * algorithmic_bytes_per_pair(wl.budget, wl.group, wl.head_dim, e, True)
+    achieved = bytes_launch / ms / 1e6            # GB/s
+    steps_per_s = 1e3 / ms
+    traffic = load_traffic(bytes_launch)
+    print(f"[bench] {ms * 1e3:.1f} us/step, {achieved:.0f} GB/s algorithmic", file=sys.stderr,
+          flush=True)
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cache.close()
+    full = None
+    if not args.no_full_kv:
+        full = full_kv_baseline(wl, min(args.steps, 200), 10)
+        print(f"[bench] full-KV: {json.dumps(full['at_fill'])}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        print(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": steps_per_s * wl.batch,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "budget": wl.budget, "fill": wl.budget,
+                   "phase": "steady state: every pair full, one eviction per pair per step"},
+        "steps_per_s": steps_per_s,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bytes_launch,
+                     "kernel": "decode_kernel (lf_decode_step)", "kernel_sha": kernel_sha()},
+        "cpu_baseline": cpu,
+        "full_kv": full,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

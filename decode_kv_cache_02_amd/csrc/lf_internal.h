@@ -1,0 +1,55 @@
+// Internal interface between the host runtime (lf_runtime.cpp) and the
+// gfx950 kernels (lf_kernels.hip). Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lf {
+
+// Shapes and parameters of one cache, fixed at create time.
+struct Geometry {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;        // num_q_heads / num_kv_heads
+  int32_t head_dim;
+  int32_t budget;       // EVICT: slots; FULL: capacity
+  int32_t sink_size;
+  int32_t slots_pad;    // budget rounded up to 64
+  int32_t dtype;        // lf_dtype
+  int32_t mode;         // lf_mode
+  int64_t pair_elems;   // slots_pad * head_dim
+  float scale;          // tau
+};
+
+// Device regions of one layer.
+struct LayerPtrs {
+  void* k;
+  void* v;
+  float* vnorm1;
+  int32_t* fill;
+};
+
+// Dynamic LDS bytes the decode kernel needs for this geometry, or 0 if the
+// combination (dtype, head_dim, group, slots) is not built.
+size_t decode_lds_bytes(const Geometry& g);
+
+// LDS bytes one workgroup may use on the current device.
+size_t device_lds_limit();
+
+hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const void* q,
+                         const void* k_new, const void* v_new, void* out,
+                         int32_t* evicted, hipStream_t stream);
+
+// Copies rows [0, n_b) of each sequence into slots 0..n_b-1 and clears the
+// rest; n_host is a host array of `count` lengths for sequences
+// [seq0, seq0 + count).
+hipError_t launch_fill(const Geometry& g, const LayerPtrs& L, const void* k,
+                       const void* v, const int32_t* n_host, int32_t seq0,
+                       int32_t count, int32_t n_max, hipStream_t stream);
+
+constexpr int kFillSeqPerLaunch = 256;
+
+}  // namespace lf

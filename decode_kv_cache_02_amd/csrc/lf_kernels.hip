@@ -1,0 +1,666 @@
+// gfx950 (MI355X) kernels of the LongFlow fused decode + score + evict step.
+//
+// The step is defined on the LongFlow pages: attention weights and output
+// (LongFlow Guide, §Mathematical Derivation of the LongFlow Score, alpha and
+// o_t equations), the score alpha_i * ||v_i||_1 (same section, c_{t,i} and
+// Score equations; gist.science summary of arXiv 2603.11504, §2.1) and the
+// static buffer with argmin eviction and in-place overwrite (LongFlow Guide,
+// §Static Memory Pre-Allocation and In-Place Eviction). The pages' own kernel
+// (LongFlow Guide, §Fused High-Performance Triton Attention Kernel; summary
+// §2.3) is a single pass that scores tokens from tiles already on chip; the
+// design below keeps that property for gfx950:
+//
+//   one workgroup = one pair (sequence, KV head); 8 waves of 64 lanes.
+//   Phase A  K stream: 128-bit loads straight into the B operand of
+//            v_mfma_f32_16x16x32_bf16 (16x16x4 f32 for float32 caches),
+//            with the query group replicated over the 16 A rows, so every
+//            lane ends up with all G logits of one slot. Logits go to LDS.
+//   A2       group max (new token included), p = exp2(s - M) in place in
+//            LDS, row sums L.
+//   Phase B  V stream: 128-bit loads, 16 lanes per 256-byte row, float32
+//            FMAs against p broadcast from LDS.
+//   Phase C  (cache full) score_i = ||v_i||_1 * sum_g p_{g,i}/L_g from LDS
+//            and the float32 sidecar, then (score, slot) argmin through
+//            wave shuffles and LDS; lowest slot wins ties.
+//   Phase D  cross-wave output reduction, the new token's own term, output
+//            write, then the new token's K/V/||v||_1 written in place.
+//
+// Every cached byte is read once; the score needs no second pass because the
+// probabilities of the whole pair stay in LDS until the argmin is known.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lf_internal.h"
+
+namespace lf {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Storage types: float32 is `float`, bfloat16 is its 16-bit pattern.
+template <typename T> struct Elem;
+template <> struct Elem<float> { static constexpr int kBytes = 4; };
+template <> struct Elem<uint16_t> { static constexpr int kBytes = 2; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+__device__ __forceinline__ void from_f32(float x, float* dst) { *dst = x; }
+__device__ __forceinline__ void from_f32(float x, uint16_t* dst) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
+    *dst = 0x7fc0;  // quiet NaN
+    return;
+  }
+  u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even
+  *dst = static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4_t x) {
+  *reinterpret_cast<u32x4_t*>(p) = x;
+}
+
+// Raw buffer resource over `bytes` bytes at `base`: 32-bit offsets, and any
+// 16-byte load that starts at or beyond `bytes` returns zeros.
+constexpr int kRsrcWord3 = 0x00020000;  // raw, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcWord3);
+}
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+}
+
+// G consecutive floats of LDS as one vector access.
+template <int G> struct PVec;
+template <> struct PVec<1> { typedef float type; };
+template <> struct PVec<2> { typedef float type __attribute__((ext_vector_type(2))); };
+template <> struct PVec<4> { typedef float type __attribute__((ext_vector_type(4))); };
+
+template <int G>
+__device__ __forceinline__ void lds_get(const float* base, int i, float (&x)[G]) {
+  const typename PVec<G>::type v = *reinterpret_cast<const typename PVec<G>::type*>(base + i * G);
+  if constexpr (G == 1) {
+    x[0] = v;
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) x[g] = v[g];
+  }
+}
+template <int G>
+__device__ __forceinline__ void lds_put(float* base, int i, const float (&x)[G]) {
+  typename PVec<G>::type v;
+  if constexpr (G == 1) {
+    v = x[0];
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = x[g];
+  }
+  *reinterpret_cast<typename PVec<G>::type*>(base + i * G) = v;
+}
+
+// 16 loaded bytes -> float32 values.
+__device__ __forceinline__ void unpack16(u32x4_t w, float (&x)[8], uint16_t) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(u32x4_t w, float (&x)[4], float) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
+}
+
+// One 16-byte chunk of a query row times the matching chunk of 16 key rows.
+// A operand = query (row i of the 16x16 tile = query head i % G),
+// B operand = keys (column j = slot j of the tile).
+__device__ __forceinline__ f32x4_t mfma_chunk(u32x4_t qa, u32x4_t kb, f32x4_t acc, uint16_t) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa),
+                                                 __builtin_bit_cast(bf16x8_t, kb), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_chunk(u32x4_t qa, u32x4_t kb, f32x4_t acc, float) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(qa[m]), __uint_as_float(kb[m]),
+                                               acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+// ||row||_1 in float32 in one fixed order, evaluated by a whole wave; the
+// result is lane 0's. The fill and the decode kernels both use this routine,
+// so equal stored rows always get bit-equal sidecar values.
+template <typename T, int D>
+__device__ __forceinline__ float wave_l1(const T* row, int lane) {
+  float x = 0.0f;
+#pragma unroll
+  for (int k = 0; k < D / kWave; ++k) x += fabsf(to_f32(row[lane + k * kWave]));
+  x = wave_sum(x);
+  return __shfl(x, 0, kWave);
+}
+
+struct DecodeParams {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* out;
+  int32_t* evicted;
+  const void* kc;
+  const void* vc;
+  void* kc_w;
+  void* vc_w;
+  float* vnorm1;
+  int32_t* fill;
+  int64_t pair_elems;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t budget;
+  int32_t sink;
+  int32_t chunk;        // slots per LDS-resident chunk (EVICT: the whole buffer)
+  float scale_log2;     // tau * log2(e)
+};
+
+template <typename T, int D, int G, bool EVICT, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P) {
+  constexpr int kBytes = Elem<T>::kBytes;
+  constexpr int NT = WAVES * kWave;
+  constexpr int kChunks = D * kBytes / 64;  // 16-byte K loads per lane per 16-slot tile
+  constexpr int EPL = 16 / kBytes;          // elements per 16-byte load
+  constexpr int LPS = D / EPL;              // lanes per V row
+  constexpr int SPI = kWave / LPS;          // V rows per wave-wide load
+  constexpr int UA = 2;                     // K tiles in flight per wave
+  constexpr int UB = 8;                     // V loads in flight per lane
+  static_assert(G == 1 || G == 2 || G == 4, "group width");
+  static_assert(LPS <= kWave && SPI * LPS == kWave, "row split");
+
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [chunk][G] logits -> p
+  __shared__ float sh_part[WAVES][G];
+  __shared__ float sh_part2[WAVES][G];
+  __shared__ float sh_m[G];
+  __shared__ float sh_l[G];
+  __shared__ float sh_w[G];
+  __shared__ float sh_snew[G];
+  __shared__ float sh_vn_new;
+  __shared__ float sh_best_score[WAVES];
+  __shared__ int sh_best_slot[WAVES];
+  __shared__ int sh_victim;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int pair = blockIdx.x;
+  const int b = pair / P.num_kv_heads;
+  const int h = pair - b * P.num_kv_heads;
+
+  const T* K = static_cast<const T*>(P.kc) + pair * P.pair_elems;
+  const T* V = static_cast<const T*>(P.vc) + pair * P.pair_elems;
+  const T* qg = static_cast<const T*>(P.q) + (static_cast<int64_t>(b) * P.num_q_heads + h * G) * D;
+  const T* kn = static_cast<const T*>(P.k_new) + static_cast<int64_t>(pair) * D;
+  const T* vn = static_cast<const T*>(P.v_new) + static_cast<int64_t>(pair) * D;
+  // The host keeps 0 <= n <= budget (and n < budget in FULL mode); clamping
+  // keeps every access inside the pair's region even if that were broken.
+  const int n = min(max(P.fill[pair], 0), P.budget);
+  constexpr uint32_t kRowBytes = D * kBytes;
+  // Reads stop at the n valid rows: rows at or beyond n load as zeros.
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K, static_cast<uint32_t>(n) * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(n) * kRowBytes);
+
+  // New token: its logits and ||v_new||_1 (wave 0).
+  if (wave == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float x = 0.0f;
+#pragma unroll
+      for (int k = 0; k < D / kWave; ++k) {
+        const int d = lane + k * kWave;
+        x = fmaf(to_f32(qg[g * D + d]), to_f32(kn[d]), x);
+      }
+      x = wave_sum(x);
+      if (lane == 0) sh_snew[g] = x * P.scale_log2;
+    }
+    const float l1 = wave_l1<T, D>(vn, lane);
+    if (lane == 0) sh_vn_new = l1;
+  }
+
+  // Query operand in the MFMA A layout: lane = row (query head row % G) +
+  // 16 * (16-byte chunk group); the same byte offsets as the key loads.
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  u32x4_t qa[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    qa[c] = load16(qg + (r16 % G) * D + (64 * c + 16 * grp) / kBytes);
+
+  // V-phase lane roles.
+  const int vcol = (lane % LPS) * EPL;
+  const int vsub = lane / LPS;
+
+  float acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+
+  // Running softmax state of the pair, one lane per query head updates it:
+  // the new token opens it with weight exp2(s_new - s_new) = 1.
+  if (tid < G) {
+    sh_m[tid] = sh_snew[tid];
+    sh_l[tid] = 1.0f;
+    sh_w[tid] = 1.0f;
+  }
+  __syncthreads();
+
+  for (int c0 = 0; c0 < n; c0 += P.chunk) {
+    const int cn = min(P.chunk, n - c0);
+    const int ntiles = (cn + 15) >> 4;
+
+    // ---------------- Phase A: logits of the chunk ----------------
+    float wmax[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) wmax[g] = -INFINITY;
+    const uint32_t base_off = static_cast<uint32_t>(c0) * kRowBytes + r16 * kRowBytes + 16 * grp;
+    for (int t0 = wave * UA; t0 < ntiles; t0 += WAVES * UA) {
+      u32x4_t kr[UA][kChunks];
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const uint32_t off = base_off + static_cast<uint32_t>(t0 + u) * 16u * kRowBytes;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) kr[u][c] = bload16(rK, off + 64 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        if (t0 + u < ntiles) {
+          f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c) s4 = mfma_chunk(qa[c], kr[u][c], s4, T());
+          const int i = (t0 + u) * 16 + r16;
+          float s[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            s[g] = (i < cn) ? s4[g] * P.scale_log2 : -INFINITY;
+            wmax[g] = fmaxf(wmax[g], s[g]);
+          }
+          if (grp == 0) lds_put<G>(lds, i, s);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m = wave_max(wmax[g]);
+      if (lane == 0) sh_part[wave][g] = m;
+    }
+    __syncthreads();
+
+    // ---------------- A2: running max, p = exp2(s - M), sums ----------------
+    float m_new[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m_old = sh_m[g];
+      float m = m_old;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) m = fmaxf(m, sh_part[w][g]);
+      m_new[g] = m;
+      const float fac = exp2f(m_old - m);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= fac;
+    }
+    float lpart[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
+    for (int i = tid; i < ntiles * 16; i += NT) {  // masked slots hold -inf -> p = 0
+      float x[G];
+      lds_get<G>(lds, i, x);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        x[g] = exp2f(x[g] - m_new[g]);
+        lpart[g] += x[g];
+      }
+      lds_put<G>(lds, i, x);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sum = wave_sum(lpart[g]);
+      if (lane == 0) sh_part2[wave][g] = sum;
+    }
+    __syncthreads();  // p visible; partial sums visible; sh_m reads done
+    if (tid < G) {
+      const float m_old = sh_m[tid];
+      float m = m_old;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) m = fmaxf(m, sh_part[w][tid]);
+      const float fac = exp2f(m_old - m);
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) sum += sh_part2[w][tid];
+      sh_l[tid] = fmaf(sh_l[tid], fac, sum);
+      sh_w[tid] *= fac;
+      sh_m[tid] = m;
+    }
+
+    // ---------------- Phase B: o += p * v over the chunk ----------------
+    const int nq = (cn + SPI - 1) / SPI;
+    const uint32_t vbase = static_cast<uint32_t>(c0 + vsub) * kRowBytes + vcol * kBytes;
+    for (int q0 = wave * UB; q0 < nq; q0 += WAVES * UB) {
+      u32x4_t vr[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        vr[u] = bload16(rV, vbase + static_cast<uint32_t>((q0 + u) * SPI) * kRowBytes);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        if (q0 + u < nq) {  // rows past the chunk have p = 0 (and load as 0 past n)
+          const int r = (q0 + u) * SPI + vsub;
+          float x[EPL];
+          unpack16(vr[u], x, T());
+          float p[G];
+          lds_get<G>(lds, r, p);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g], x[e], acc[g][e]);
+        }
+      }
+    }
+    __syncthreads();  // LDS p and the softmax state are settled before reuse
+  }
+
+  // ---------------- Phase C: score + argmin (cache full) ----------------
+  const bool evicting = EVICT && n >= P.budget;
+  if (EVICT && evicting) {
+    float inv_l[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / sh_l[g];
+    float best = INFINITY;
+    int best_i = 0x7fffffff;
+    for (int i = P.sink + tid; i < n; i += NT) {
+      float p[G];
+      lds_get<G>(lds, i, p);
+      float sc = p[0] * inv_l[0];
+#pragma unroll
+      for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
+      sc = sc * P.vnorm1[static_cast<int64_t>(pair) * (P.pair_elems / D) + i];
+      if (sc < best) {  // slots visited in increasing order: first minimum kept
+        best = sc;
+        best_i = i;
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float os = __shfl_xor(best, off, kWave);
+      const int oi = __shfl_xor(best_i, off, kWave);
+      if (os < best || (os == best && oi < best_i)) {
+        best = os;
+        best_i = oi;
+      }
+    }
+    if (lane == 0) {
+      sh_best_score[wave] = best;
+      sh_best_slot[wave] = best_i;
+    }
+  }
+  __syncthreads();  // LDS probabilities no longer needed after this point
+  if (EVICT && evicting && tid == 0) {
+    float best = sh_best_score[0];
+    int best_i = sh_best_slot[0];
+    for (int w = 1; w < WAVES; ++w) {
+      if (sh_best_score[w] < best || (sh_best_score[w] == best && sh_best_slot[w] < best_i)) {
+        best = sh_best_score[w];
+        best_i = sh_best_slot[w];
+      }
+    }
+    sh_victim = best_i;
+  }
+
+  // ---------------- Phase D: output ----------------
+#pragma unroll
+  for (int off = LPS; off < kWave; off <<= 1)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off, kWave);
+  float* red = lds;  // [WAVES][G][D], reuses the logit area
+  if (lane < LPS) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[(wave * G + g) * D + vcol + e] = acc[g][e];
+  }
+  __syncthreads();
+  T* out = static_cast<T*>(P.out) + (static_cast<int64_t>(b) * P.num_q_heads + h * G) * D;
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) o += red[(w * G + g) * D + d];
+    o = fmaf(sh_w[g], to_f32(vn[d]), o);
+    from_f32(o / sh_l[g], out + g * D + d);
+  }
+
+  // ---------------- Phase D: in-place write of the new token ----------------
+  const int slot = evicting ? sh_victim : n;
+  if (slot >= P.budget) return;  // FULL cache already at capacity: nothing to store
+  constexpr int kRowLoads = D * kBytes / 16;
+  T* Kw = static_cast<T*>(P.kc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
+  T* Vw = static_cast<T*>(P.vc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
+  if (tid < kRowLoads) {
+    store16(Kw + tid * EPL, load16(kn + tid * EPL));
+  } else if (tid < 2 * kRowLoads) {
+    const int j = tid - kRowLoads;
+    store16(Vw + j * EPL, load16(vn + j * EPL));
+  }
+  if (tid == 0) {
+    P.vnorm1[static_cast<int64_t>(pair) * (P.pair_elems / D) + slot] = sh_vn_new;
+    P.evicted[pair] = evicting ? slot : -1;
+    if (!evicting) P.fill[pair] = n + 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Initial fill: one wave per (pair, slot); copies the row or clears it.
+// ---------------------------------------------------------------------------
+struct FillParams {
+  const void* k;
+  const void* v;
+  void* kc;
+  void* vc;
+  float* vnorm1;
+  int32_t* fill;
+  int64_t pair_elems;
+  int32_t slots_pad;
+  int32_t num_kv_heads;
+  int32_t n_max;
+  int32_t seq0;
+  int32_t n[kFillSeqPerLaunch];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int local_pair = blockIdx.y;
+  const int bl = local_pair / P.num_kv_heads;
+  const int h = local_pair - bl * P.num_kv_heads;
+  const int b = P.seq0 + bl;
+  const int64_t pair = static_cast<int64_t>(b) * P.num_kv_heads + h;
+  const int nb = P.n[bl];
+  if (slot >= P.slots_pad) return;
+  T* Kd = static_cast<T*>(P.kc) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
+  T* Vd = static_cast<T*>(P.vc) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
+  float l1 = 0.0f;
+  if (slot < nb) {
+    const int64_t src = ((static_cast<int64_t>(b) * P.n_max + slot) * P.num_kv_heads + h) * D;
+    const T* ks = static_cast<const T*>(P.k) + src;
+    const T* vs = static_cast<const T*>(P.v) + src;
+#pragma unroll
+    for (int k = 0; k < D / kWave; ++k) {
+      Kd[lane + k * kWave] = ks[lane + k * kWave];
+      Vd[lane + k * kWave] = vs[lane + k * kWave];
+    }
+    l1 = wave_l1<T, D>(vs, lane);
+  } else {
+#pragma unroll
+    for (int k = 0; k < D / kWave; ++k) {
+      Kd[lane + k * kWave] = T(0);
+      Vd[lane + k * kWave] = T(0);
+    }
+  }
+  if (lane == 0) {
+    P.vnorm1[pair * P.slots_pad + slot] = l1;
+    if (slot == 0) P.fill[pair] = nb;
+  }
+}
+
+template <typename T, int D, int G, bool EVICT>
+hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const void* q,
+                           const void* k_new, const void* v_new, void* out,
+                           int32_t* evicted, hipStream_t stream) {
+  constexpr int WAVES = 8;
+  DecodeParams P;
+  P.q = q;
+  P.k_new = k_new;
+  P.v_new = v_new;
+  P.out = out;
+  P.evicted = evicted;
+  P.kc = L.k;
+  P.vc = L.v;
+  P.kc_w = L.k;
+  P.vc_w = L.v;
+  P.vnorm1 = L.vnorm1;
+  P.fill = L.fill;
+  P.pair_elems = geo.pair_elems;
+  P.num_q_heads = geo.num_q_heads;
+  P.num_kv_heads = geo.num_kv_heads;
+  P.budget = geo.budget;
+  P.sink = geo.sink_size;
+  P.scale_log2 = geo.scale * kLog2e;
+  const size_t lds = decode_lds_bytes(geo);
+  P.chunk = static_cast<int32_t>(lds / (sizeof(float) * G));
+  if (EVICT) P.chunk = geo.slots_pad;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, G, EVICT, WAVES>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  const int pairs = geo.batch * geo.num_kv_heads;
+  hipLaunchKernelGGL((decode_kernel<T, D, G, EVICT, WAVES>), dim3(pairs), dim3(WAVES * kWave), lds,
+                     stream, P);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_fill_t(const Geometry& geo, const LayerPtrs& L, const void* k, const void* v,
+                         const int32_t* n_host, int32_t seq0, int32_t count, int32_t n_max,
+                         hipStream_t stream) {
+  FillParams P;
+  P.k = k;
+  P.v = v;
+  P.kc = L.k;
+  P.vc = L.v;
+  P.vnorm1 = L.vnorm1;
+  P.fill = L.fill;
+  P.pair_elems = geo.pair_elems;
+  P.slots_pad = geo.slots_pad;
+  P.num_kv_heads = geo.num_kv_heads;
+  P.n_max = n_max;
+  P.seq0 = seq0;
+  for (int i = 0; i < kFillSeqPerLaunch; ++i) P.n[i] = i < count ? n_host[i] : 0;
+  dim3 grid((geo.slots_pad + 3) / 4, count * geo.num_kv_heads);
+  hipLaunchKernelGGL((fill_kernel<T, D>), grid, dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
+constexpr size_t kEvictLdsCap = 160 * 1024 - 4096;  // leave room for static LDS
+constexpr size_t kFullChunkSlots = 2048;
+
+}  // namespace
+
+size_t device_lds_limit() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return 0;
+  return static_cast<size_t>(v);
+}
+
+size_t decode_lds_bytes(const Geometry& g) {
+  if (g.head_dim != 64 && g.head_dim != 128) return 0;
+  if (g.group != 1 && g.group != 2 && g.group != 4) return 0;
+  if (g.dtype != 0 && g.dtype != 1) return 0;
+  constexpr size_t kWaves = 8;
+  const size_t red = kWaves * g.group * g.head_dim * sizeof(float);
+  size_t logits;
+  if (g.mode == 0) {
+    logits = static_cast<size_t>(g.slots_pad) * g.group * sizeof(float);
+    if (logits > kEvictLdsCap) return 0;
+  } else {
+    const size_t slots = g.slots_pad < static_cast<int>(kFullChunkSlots) ? g.slots_pad : kFullChunkSlots;
+    logits = slots * g.group * sizeof(float);
+  }
+  return logits > red ? logits : red;
+}
+
+hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const void* q,
+                         const void* k_new, const void* v_new, void* out, int32_t* evicted,
+                         hipStream_t stream) {
+#define LF_CASE(T, D, G)                                                                    \
+  if (g.head_dim == D && g.group == G) {                                                   \
+    return g.mode == 0 ? launch_decode_t<T, D, G, true>(g, L, q, k_new, v_new, out, evicted, stream) \
+                       : launch_decode_t<T, D, G, false>(g, L, q, k_new, v_new, out, evicted, stream); \
+  }
+  if (g.dtype == 1) {
+    LF_CASE(uint16_t, 128, 1)
+    LF_CASE(uint16_t, 128, 2)
+    LF_CASE(uint16_t, 128, 4)
+    LF_CASE(uint16_t, 64, 1)
+    LF_CASE(uint16_t, 64, 2)
+    LF_CASE(uint16_t, 64, 4)
+  } else {
+    LF_CASE(float, 128, 1)
+    LF_CASE(float, 128, 2)
+    LF_CASE(float, 128, 4)
+    LF_CASE(float, 64, 1)
+    LF_CASE(float, 64, 2)
+    LF_CASE(float, 64, 4)
+  }
+#undef LF_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill(const Geometry& g, const LayerPtrs& L, const void* k, const void* v,
+                       const int32_t* n_host, int32_t seq0, int32_t count, int32_t n_max,
+                       hipStream_t stream) {
+  if (count <= 0 || count > kFillSeqPerLaunch) return hipErrorInvalidValue;
+  if (g.dtype == 1) {
+    if (g.head_dim == 128) return launch_fill_t<uint16_t, 128>(g, L, k, v, n_host, seq0, count, n_max, stream);
+    if (g.head_dim == 64) return launch_fill_t<uint16_t, 64>(g, L, k, v, n_host, seq0, count, n_max, stream);
+  } else {
+    if (g.head_dim == 128) return launch_fill_t<float, 128>(g, L, k, v, n_host, seq0, count, n_max, stream);
+    if (g.head_dim == 64) return launch_fill_t<float, 64>(g, L, k, v, n_host, seq0, count, n_max, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lf

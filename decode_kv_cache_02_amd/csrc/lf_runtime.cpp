@@ -1,0 +1,313 @@
+// Host runtime of liblongflow.so: the C ABI declared in include/longflow.h.
+//
+// Static cache allocator (LongFlow Guide, §Static Memory Pre-Allocation and
+// In-Place Eviction: one fixed buffer of B slots, never compacted): one
+// hipMalloc at create time holds, for every (layer, sequence, KV head) pair,
+//   K      [slots_pad][head_dim]  cache dtype
+//   V      [slots_pad][head_dim]  cache dtype
+//   ||v||_1 [slots_pad]           float32 sidecar
+//   fill                          int32 tokens held
+// and nothing is allocated afterwards. Validation happens on the host before
+// anything is queued; fill levels are mirrored on the host (every decode step
+// adds exactly one token per pair) so no call has to read the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/longflow.h"
+#include "lf_internal.h"
+
+struct lf_cache {
+  lf_config cfg;
+  lf::Geometry geo;
+  int device;
+  size_t bytes;
+  void* base;
+  char* k;
+  char* v;
+  float* vnorm1;
+  int32_t* fill;
+  int64_t layer_pairs;   // batch * num_kv_heads
+  size_t elem_bytes;
+  std::vector<int32_t> fill_host;  // [num_layers][batch]
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kSlotAlign = 64;
+
+struct Layout {
+  size_t k_off, v_off, vn_off, fill_off, total;
+  int32_t slots_pad;
+  int64_t pair_elems;
+};
+
+bool mul_ok(size_t a, size_t b, size_t* r) { return !__builtin_mul_overflow(a, b, r); }
+bool add_ok(size_t a, size_t b, size_t* r) { return !__builtin_add_overflow(a, b, r); }
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+lf_status validate(const lf_config* c) {
+  if (!c) return LF_ERR_INVALID_ARG;
+  if (c->num_layers < 1 || c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 ||
+      c->head_dim < 1 || c->budget < 1)
+    return LF_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads) return LF_ERR_INVALID_ARG;
+  if (c->sink_size < 0 || c->sink_size >= c->budget) return LF_ERR_INVALID_ARG;
+  if (!(c->softmax_scale >= 0.0f) || !std::isfinite(c->softmax_scale)) return LF_ERR_INVALID_ARG;
+  if (c->dtype != LF_DTYPE_F32 && c->dtype != LF_DTYPE_BF16) return LF_ERR_INVALID_ARG;
+  if (c->mode != LF_MODE_EVICT && c->mode != LF_MODE_FULL) return LF_ERR_INVALID_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return LF_ERR_UNSUPPORTED;
+  const int g = c->num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4) return LF_ERR_UNSUPPORTED;
+  if (c->budget > (1 << 30) - kSlotAlign) return LF_ERR_UNSUPPORTED;
+  return LF_OK;
+}
+
+lf::Geometry geometry(const lf_config* c) {
+  lf::Geometry g;
+  g.batch = c->batch;
+  g.num_q_heads = c->num_q_heads;
+  g.num_kv_heads = c->num_kv_heads;
+  g.group = c->num_q_heads / c->num_kv_heads;
+  g.head_dim = c->head_dim;
+  g.budget = c->budget;
+  g.sink_size = c->sink_size;
+  g.slots_pad = (c->budget + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
+  g.dtype = c->dtype;
+  g.mode = c->mode;
+  g.pair_elems = static_cast<int64_t>(g.slots_pad) * c->head_dim;
+  g.scale = c->softmax_scale > 0.0f ? c->softmax_scale
+                                    : static_cast<float>(1.0 / std::sqrt(static_cast<double>(c->head_dim)));
+  return g;
+}
+
+lf_status layout(const lf_config* c, Layout* L) {
+  const lf::Geometry g = geometry(c);
+  const size_t elem = c->dtype == LF_DTYPE_F32 ? 4 : 2;
+  size_t pairs, kv, vn, fl, t;
+  if (!mul_ok(static_cast<size_t>(c->num_layers), static_cast<size_t>(c->batch), &pairs) ||
+      !mul_ok(pairs, static_cast<size_t>(c->num_kv_heads), &pairs))
+    return LF_ERR_UNSUPPORTED;
+  if (!mul_ok(pairs, static_cast<size_t>(g.pair_elems), &kv) || !mul_ok(kv, elem, &kv))
+    return LF_ERR_UNSUPPORTED;
+  if (!mul_ok(pairs, static_cast<size_t>(g.slots_pad), &vn) || !mul_ok(vn, 4, &vn))
+    return LF_ERR_UNSUPPORTED;
+  if (!mul_ok(pairs, 4, &fl)) return LF_ERR_UNSUPPORTED;
+  L->slots_pad = g.slots_pad;
+  L->pair_elems = g.pair_elems;
+  L->k_off = 0;
+  if (!add_ok(align_up(kv), 0, &t)) return LF_ERR_UNSUPPORTED;
+  L->v_off = t;
+  if (!add_ok(L->v_off, align_up(kv), &t)) return LF_ERR_UNSUPPORTED;
+  L->vn_off = t;
+  if (!add_ok(L->vn_off, align_up(vn), &t)) return LF_ERR_UNSUPPORTED;
+  L->fill_off = t;
+  if (!add_ok(L->fill_off, align_up(fl), &t)) return LF_ERR_UNSUPPORTED;
+  L->total = t;
+  return LF_OK;
+}
+
+lf::LayerPtrs layer_ptrs(const lf_cache* c, int32_t layer) {
+  lf::LayerPtrs p;
+  const int64_t pair0 = static_cast<int64_t>(layer) * c->layer_pairs;
+  p.k = c->k + pair0 * c->geo.pair_elems * static_cast<int64_t>(c->elem_bytes);
+  p.v = c->v + pair0 * c->geo.pair_elems * static_cast<int64_t>(c->elem_bytes);
+  p.vnorm1 = c->vnorm1 + pair0 * c->geo.slots_pad;
+  p.fill = c->fill + pair0;
+  return p;
+}
+
+lf_status use_device(const lf_cache* c) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return LF_ERR_HIP;
+  if (cur != c->device && hipSetDevice(c->device) != hipSuccess) return LF_ERR_HIP;
+  return LF_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lf_status_str(lf_status s) {
+  switch (s) {
+    case LF_OK: return "LF_OK";
+    case LF_ERR_INVALID_ARG: return "LF_ERR_INVALID_ARG";
+    case LF_ERR_UNSUPPORTED: return "LF_ERR_UNSUPPORTED";
+    case LF_ERR_CAPACITY: return "LF_ERR_CAPACITY";
+    case LF_ERR_OOM: return "LF_ERR_OOM";
+    case LF_ERR_HIP: return "LF_ERR_HIP";
+  }
+  return "LF_ERR_UNKNOWN";
+}
+
+lf_status lf_cache_bytes(const lf_config* cfg, size_t* bytes) {
+  if (!bytes) return LF_ERR_INVALID_ARG;
+  lf_status s = validate(cfg);
+  if (s != LF_OK) return s;
+  Layout L;
+  s = layout(cfg, &L);
+  if (s != LF_OK) return s;
+  *bytes = L.total;
+  return LF_OK;
+}
+
+lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
+  if (!out) return LF_ERR_INVALID_ARG;
+  *out = nullptr;
+  lf_status s = validate(cfg);
+  if (s != LF_OK) return s;
+  Layout L;
+  s = layout(cfg, &L);
+  if (s != LF_OK) return s;
+  const lf::Geometry geo = geometry(cfg);
+  const size_t lds = lf::decode_lds_bytes(geo);
+  if (lds == 0) return LF_ERR_UNSUPPORTED;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) {
+    (void)hipGetLastError();
+    return LF_ERR_HIP;
+  }
+  if (lds > lf::device_lds_limit()) return LF_ERR_UNSUPPORTED;
+
+  lf_cache* c = new (std::nothrow) lf_cache();
+  if (!c) return LF_ERR_OOM;
+  try {
+    c->fill_host.assign(static_cast<size_t>(cfg->num_layers) * cfg->batch, 0);
+  } catch (...) {
+    delete c;
+    return LF_ERR_OOM;
+  }
+  c->cfg = *cfg;
+  c->geo = geo;
+  c->bytes = L.total;
+  c->elem_bytes = cfg->dtype == LF_DTYPE_F32 ? 4 : 2;
+  c->layer_pairs = static_cast<int64_t>(cfg->batch) * cfg->num_kv_heads;
+  c->device = device;
+  void* base = nullptr;
+  hipError_t e = hipMalloc(&base, L.total);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return e == hipErrorOutOfMemory ? LF_ERR_OOM : LF_ERR_HIP;
+  }
+  e = hipMemsetAsync(base, 0, L.total, nullptr);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) {
+    (void)hipFree(base);
+    delete c;
+    return LF_ERR_HIP;
+  }
+  c->base = base;
+  c->k = static_cast<char*>(base) + L.k_off;
+  c->v = static_cast<char*>(base) + L.v_off;
+  c->vnorm1 = reinterpret_cast<float*>(static_cast<char*>(base) + L.vn_off);
+  c->fill = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.fill_off);
+  *out = c;
+  return LF_OK;
+}
+
+void lf_cache_destroy(lf_cache* c) {
+  if (!c) return;
+  if (c->base) {
+    int cur = -1;
+    if (hipGetDevice(&cur) == hipSuccess && cur != c->device) (void)hipSetDevice(c->device);
+    (void)hipFree(c->base);
+    if (cur >= 0 && cur != c->device) (void)hipSetDevice(cur);
+  }
+  delete c;
+}
+
+lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view) {
+  if (!c || !view || layer < 0 || layer >= c->cfg.num_layers) return LF_ERR_INVALID_ARG;
+  const lf::LayerPtrs p = layer_ptrs(c, layer);
+  view->k = p.k;
+  view->v = p.v;
+  view->vnorm1 = p.vnorm1;
+  view->fill = p.fill;
+  view->pair_stride = c->geo.pair_elems;
+  view->slots_padded = c->geo.slots_pad;
+  view->elem_bytes = static_cast<int32_t>(c->elem_bytes);
+  return LF_OK;
+}
+
+lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm1,
+                            int32_t* fill, void* stream) {
+  if (!c || layer < 0 || layer >= c->cfg.num_layers) return LF_ERR_INVALID_ARG;
+  lf_status s = use_device(c);
+  if (s != LF_OK) return s;
+  const lf::LayerPtrs p = layer_ptrs(c, layer);
+  const size_t kv_bytes = static_cast<size_t>(c->layer_pairs) * c->geo.pair_elems * c->elem_bytes;
+  const size_t vn_bytes = static_cast<size_t>(c->layer_pairs) * c->geo.slots_pad * sizeof(float);
+  const size_t fill_bytes = static_cast<size_t>(c->layer_pairs) * sizeof(int32_t);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const struct { void* dst; const void* src; size_t n; } copies[] = {
+      {k, p.k, kv_bytes}, {v, p.v, kv_bytes}, {vnorm1, p.vnorm1, vn_bytes}, {fill, p.fill, fill_bytes}};
+  for (const auto& cp : copies) {
+    if (!cp.dst) continue;
+    if (hipMemcpyAsync(cp.dst, cp.src, cp.n, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return LF_ERR_HIP;
+  }
+  return LF_OK;
+}
+
+lf_status lf_fill_levels(const lf_cache* c, int32_t layer, int32_t* fill_host) {
+  if (!c || !fill_host || layer < 0 || layer >= c->cfg.num_layers) return LF_ERR_INVALID_ARG;
+  std::memcpy(fill_host, c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch,
+              sizeof(int32_t) * c->cfg.batch);
+  return LF_OK;
+}
+
+lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void* v,
+                          const int32_t* n_per_seq, int32_t n_max, void* stream) {
+  if (!c || !n_per_seq || layer < 0 || layer >= c->cfg.num_layers || n_max < 0)
+    return LF_ERR_INVALID_ARG;
+  if (n_max > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return LF_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < c->cfg.batch; ++b) {
+    if (n_per_seq[b] < 0 || n_per_seq[b] > n_max) return LF_ERR_INVALID_ARG;
+    if (n_per_seq[b] > c->cfg.budget) return LF_ERR_CAPACITY;
+  }
+  lf_status s = use_device(c);
+  if (s != LF_OK) return s;
+  const lf::LayerPtrs p = layer_ptrs(c, layer);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t b0 = 0; b0 < c->cfg.batch; b0 += lf::kFillSeqPerLaunch) {
+    const int32_t count = std::min<int32_t>(lf::kFillSeqPerLaunch, c->cfg.batch - b0);
+    if (lf::launch_fill(c->geo, p, k, v, n_per_seq + b0, b0, count, n_max, st) != hipSuccess)
+      return LF_ERR_HIP;
+  }
+  std::memcpy(c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch, n_per_seq,
+              sizeof(int32_t) * c->cfg.batch);
+  return LF_OK;
+}
+
+lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_new,
+                         const void* v_new, void* out, int32_t* evicted_slot, void* stream) {
+  if (!c || !q || !k_new || !v_new || !out || !evicted_slot || layer < 0 ||
+      layer >= c->cfg.num_layers)
+    return LF_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+    return LF_ERR_INVALID_ARG;
+  int32_t* fh = c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch;
+  if (c->cfg.mode == LF_MODE_FULL) {
+    for (int32_t b = 0; b < c->cfg.batch; ++b)
+      if (fh[b] >= c->cfg.budget) return LF_ERR_CAPACITY;
+  }
+  lf_status s = use_device(c);
+  if (s != LF_OK) return s;
+  const lf::LayerPtrs p = layer_ptrs(c, layer);
+  if (lf::launch_decode(c->geo, p, q, k_new, v_new, out, evicted_slot,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LF_ERR_HIP;
+  for (int32_t b = 0; b < c->cfg.batch; ++b)
+    if (fh[b] < c->cfg.budget) ++fh[b];
+  return LF_OK;
+}
+
+}  // extern "C"

@@ -269,3 +269,24 @@ def step_ring(wl: Workload, count: int, layer: int = 0, seed_offset: int = 0):
     k = np.stack([s.k_new for s in steps])
     v = np.stack([s.v_new for s in steps])
     return q, k, v
+
+
+def device_prefill(wl: Workload, n: int, seed: int, device: str = "cuda"):
+    """Prefill K, V [batch][n][num_kv_heads][head_dim] drawn on the device.
+
+    Same value recipe as TokenStream (K, V entries N(0,1), one lognormal(0,0.5)
+    scale per V row, one rounding to the storage dtype) but drawn with torch's
+    device generator seeded by `seed`, so multi-gigabyte caches can be filled
+    in well under a second. Used where only the cost of a step matters.
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    shape = (wl.batch, n, wl.num_kv_heads, wl.head_dim)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    k = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dt)
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    scale = torch.empty(shape[:3] + (1,), device=device, dtype=torch.float32)
+    scale.log_normal_(0.0, V_LOGNORMAL_SIGMA, generator=g)
+    v = (v * scale).to(dt)
+    return k, v

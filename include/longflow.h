@@ -1,0 +1,159 @@
+/*
+ * longflow.h -- C ABI of the LongFlow fused decode + score + evict library
+ * (liblongflow.so, HIP for AMD Instinct MI355X / gfx950).
+ *
+ * What the library computes is defined on the LongFlow pages:
+ *   - attention weights and output: LongFlow Guide (aifetchly blog),
+ *     §Mathematical Derivation of the LongFlow Score, the alpha and o_t
+ *     equations;
+ *   - the token score ||c_{t,i}||_1 = alpha_{t,i} ||v_i||_1: same section, the
+ *     c_{t,i} and Score equations; gist.science summary of arXiv 2603.11504,
+ *     §2.1 (LongFlowScore);
+ *   - the static buffer, initial fill, argmin eviction and in-place overwrite:
+ *     LongFlow Guide, §Static Memory Pre-Allocation and In-Place Eviction,
+ *     items 1-3; gist.science summary, §2.3 (static KV cache, one fused pass).
+ *
+ * Unit of work: a "pair" is one (layer, sequence b, KV head h). Query head j
+ * belongs to KV head j / G, G = num_q_heads / num_kv_heads. Pairs never
+ * interact.
+ *
+ * One decode step of one pair, with n tokens cached (n <= budget):
+ *   s_{g,i} = tau * <q_g, k_i> over the n cached tokens and the new token,
+ *   alpha   = softmax over those n+1 tokens (per query head g),
+ *   out_g   = sum_i alpha_{g,i} v_i (new token included),
+ *   if n < budget (or mode FULL): the new token is appended at slot n;
+ *   else: score_i = ||v_i||_1 * sum_g alpha_{g,i} for i in [sink_size, budget),
+ *         the slot with the smallest score (lowest index on ties) is
+ *         overwritten in place by k_new, v_new, ||v_new||_1.
+ * ||v||_1 is kept per slot in a float32 sidecar, computed once when the token
+ * is stored, from the stored (dtype-rounded) values.
+ *
+ * Conventions for every call:
+ *   - The handle owns all cache memory (K, V, ||v||_1, fill counters): one
+ *     device allocation made by lf_cache_create, freed by lf_cache_destroy,
+ *     never resized. No call allocates device memory after create.
+ *   - The caller owns every I/O pointer. They are contiguous DEVICE buffers in
+ *     cfg.dtype (float32 or bfloat16) unless stated, and must stay valid until
+ *     the work queued on `stream` has completed.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are stream-ordered and asynchronous; the library never
+ *     synchronises the device and never copies device -> host.
+ *   - Arguments are validated on the host before anything is queued. A call
+ *     that returns an error has changed nothing.
+ *   - Inputs must be finite; NaN or Inf make the results undefined.
+ *   - A handle is not thread-safe; serialise its calls on one stream.
+ */
+#ifndef LONGFLOW_H
+#define LONGFLOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lf_cache lf_cache; /* opaque */
+
+typedef enum {
+  LF_OK = 0,
+  LF_ERR_INVALID_ARG = 1, /* null pointer, out-of-range index, bad config   */
+  LF_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, group, sizes    */
+  LF_ERR_CAPACITY = 3,    /* prefill longer than the budget; FULL cache full */
+  LF_ERR_OOM = 4,         /* the one device allocation failed               */
+  LF_ERR_HIP = 5          /* a HIP runtime or launch error                  */
+} lf_status;
+
+typedef enum { LF_DTYPE_F32 = 0, LF_DTYPE_BF16 = 1 } lf_dtype;
+
+typedef enum {
+  LF_MODE_EVICT = 0, /* LongFlow: `budget` slots, score + argmin + in-place write */
+  LF_MODE_FULL = 1   /* full-KV baseline: capacity `budget`, never evicts         */
+} lf_mode;
+
+typedef struct {
+  int32_t num_layers;   /* >= 1                                                  */
+  int32_t batch;        /* sequences, >= 1                                       */
+  int32_t num_q_heads;  /* multiple of num_kv_heads; G = num_q_heads/num_kv_heads */
+  int32_t num_kv_heads; /* >= 1                                                  */
+  int32_t head_dim;     /* 64 or 128                                             */
+  int32_t budget;       /* slots per pair (EVICT) or capacity (FULL), >= 1       */
+  int32_t sink_size;    /* slots [0, sink_size) are never evicted; < budget      */
+  float softmax_scale;  /* tau; 0 selects 1/sqrt(head_dim)                      */
+  int32_t dtype;        /* lf_dtype: of the cache and of q, k_new, v_new, out    */
+  int32_t mode;         /* lf_mode                                               */
+} lf_config;
+
+/* Device addresses and strides of one layer's region (for tests, snapshots). */
+typedef struct {
+  void* k;              /* [batch][num_kv_heads][slots_padded][head_dim] cfg.dtype */
+  void* v;              /* same layout                                              */
+  float* vnorm1;        /* [batch][num_kv_heads][slots_padded] float32              */
+  int32_t* fill;        /* [batch][num_kv_heads] int32: tokens held per pair        */
+  int64_t pair_stride;  /* elements between consecutive pairs in k / v             */
+  int32_t slots_padded; /* budget rounded up to a multiple of 64                    */
+  int32_t elem_bytes;   /* 4 (float32) or 2 (bfloat16)                              */
+} lf_view;
+
+/* Bytes lf_cache_create would allocate for `cfg` (nothing is allocated).
+ * Lets a caller size the batch to the device memory. */
+lf_status lf_cache_bytes(const lf_config* cfg, size_t* bytes);
+
+/* Validate `cfg`, make the one device allocation on the current device, zero
+ * it (every fill level starts at 0) and return the handle in *out. On error
+ * *out is set to NULL and nothing stays allocated. */
+lf_status lf_cache_create(const lf_config* cfg, lf_cache** out);
+
+/* Initial fill of one layer (LongFlow Guide, §Static Memory..., item 1).
+ *   k, v          device, [batch][n_max][num_kv_heads][head_dim], cfg.dtype
+ *   n_per_seq     HOST array [batch]; sequence b stores its first n_b rows in
+ *                 slots 0..n_b-1 of each of its pairs; 0 <= n_b <= n_max
+ * Slots n_b..budget-1 are cleared. Errors: LF_ERR_CAPACITY if some
+ * n_b > budget, LF_ERR_INVALID_ARG on null pointers, a bad layer or n_b > n_max. */
+lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void* v,
+                          const int32_t* n_per_seq, int32_t n_max, void* stream);
+
+/* One fused decode step of every pair of one layer (the hot path).
+ *   q             device [batch][num_q_heads][head_dim], cfg.dtype
+ *   k_new, v_new  device [batch][num_kv_heads][head_dim], cfg.dtype
+ *   out           device [batch][num_q_heads][head_dim], cfg.dtype; written
+ *                 (bfloat16 outputs are rounded to nearest even from float32)
+ *   evicted_slot  device [batch][num_kv_heads] int32; written: the slot that
+ *                 was overwritten, or -1 when the token was appended
+ * Accumulation is float32. Errors: LF_ERR_INVALID_ARG on null pointers or a
+ * bad layer; LF_ERR_CAPACITY in FULL mode when a pair already holds
+ * `budget` tokens; LF_ERR_HIP if the launch fails. */
+lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_new,
+                         const void* v_new, void* out, int32_t* evicted_slot,
+                         void* stream);
+
+/* Fill the view of one layer. */
+lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view);
+
+/* Snapshot of one layer into caller-owned DEVICE buffers, stream-ordered
+ * device-to-device copies (tests, checkpoints; the static layout makes each a
+ * single contiguous copy):
+ *   k, v    [batch][num_kv_heads][slots_padded][head_dim] cfg.dtype
+ *   vnorm1  [batch][num_kv_heads][slots_padded] float32
+ *   fill    [batch][num_kv_heads] int32
+ * Any of the four may be NULL to skip it. */
+lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm1,
+                            int32_t* fill, void* stream);
+
+/* Host-side copy of the fill levels of one layer, [batch] int32 into the
+ * caller's HOST array. Tracked on the host from the calls made (no device
+ * access, no synchronisation). */
+lf_status lf_fill_levels(const lf_cache* c, int32_t layer, int32_t* fill_host);
+
+/* Release the handle and its device memory. NULL is a no-op. The caller must
+ * make sure no queued work still uses the cache. */
+void lf_cache_destroy(lf_cache* c);
+
+/* Static string naming a status code. */
+const char* lf_status_str(lf_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LONGFLOW_H */

@@ -1,0 +1,138 @@
+"""Lockstep driver: the HIP library and the CPU oracle step side by side.
+
+Both consume the same seeded inputs (decode_kv_cache_02_amd.synth). After every
+step the GPU output is compared row by row with the oracle (max abs error over
+the row divided by the row's max |oracle|) and the evicted slot must equal the
+oracle's, except at a near-tie (two lowest oracle scores within 1e-4
+relative), where it must be one of the near-tie slots; the oracle then adopts
+the GPU's choice so the two caches stay identical.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+from decode_kv_cache_02_amd.synth import TokenStream, Workload
+from oracle.longflow_oracle import LayerCache
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def torch_dtype(dtype: str):
+    import torch
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(torch_dtype(dtype))
+
+
+def row_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of max_k |gpu - ref| / max(max_k |ref|, 1e-30)."""
+    num = np.abs(gpu - ref).max(axis=-1)
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return float((num / den).max())
+
+
+@dataclass
+class LockstepReport:
+    steps: int = 0
+    evictions: int = 0
+    appends: int = 0
+    near_ties: int = 0
+    tie_lowest_index: int = 0
+    exact_ties: int = 0
+    max_rel_err: float = 0.0
+    notes: list = field(default_factory=list)
+
+
+def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
+                 prefill_n=None, mode: str = "evict", capacity: Optional[int] = None,
+                 sink_size: int = 0, seed_offset: int = 0, layer: int = 0,
+                 num_layers: int = 1, check_cache_every: int = 0) -> LockstepReport:
+    """Run `steps` decode steps of one layer on the GPU and in the oracle."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+
+    budget = wl.budget if capacity is None else capacity
+    cache = LongFlowCache(num_layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                          budget, sink_size=sink_size, dtype=wl.dtype, mode=mode)
+    try:
+        ts = TokenStream(wl, layer=layer, seed_offset=seed_offset)
+        if prefill_n is None:
+            prefill_n = np.full(wl.batch, wl.prefill, dtype=np.int32)
+        prefill_n = np.asarray(prefill_n, dtype=np.int32)
+        pf = ts.prefill(n_max=int(prefill_n.max(initial=0)), n_per_seq=prefill_n)
+        oracle = LayerCache(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, budget,
+                            sink_size=sink_size, evict=(mode == "evict"), pairs=pairs)
+        oracle.prefill(pf.k, pf.v, pf.n_per_seq)
+        if pf.k.shape[1] > 0:
+            cache.prefill(layer, to_device(pf.k, wl.dtype), to_device(pf.v, wl.dtype), prefill_n)
+        else:
+            cache.prefill(layer, None, None, prefill_n)
+        del pf
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch_dtype(wl.dtype),
+                          device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        rep = LockstepReport()
+        g = wl.group
+        for t in range(steps):
+            st = ts.step()
+            cache.decode_step(layer, to_device(st.q, wl.dtype), to_device(st.k_new, wl.dtype),
+                              to_device(st.v_new, wl.dtype), out, ev)
+            gout = out.float().cpu().numpy()
+            gev = ev.cpu().numpy()
+            res = oracle.attend(st.q, st.k_new, st.v_new)
+            chosen = {}
+            for (b, h), r in res.items():
+                err = row_rel_err(gout[b, h * g:(h + 1) * g], r.out)
+                rep.max_rel_err = max(rep.max_rel_err, err)
+                assert err <= TOL[wl.dtype], (
+                    f"step {t} pair {(b, h)}: out rel err {err:.3g} > {TOL[wl.dtype]}")
+                e = int(gev[b, h])
+                if r.evicted < 0:
+                    assert e == -1, f"step {t} pair {(b, h)}: expected append, GPU evicted {e}"
+                    rep.appends += 1
+                    continue
+                rep.evictions += 1
+                if r.near_tie:
+                    rep.near_ties += 1
+                    s = r.scores
+                    finite = np.sort(s[np.isfinite(s)])
+                    if finite.size >= 2 and finite[0] == finite[1]:
+                        rep.exact_ties += 1
+                        rep.tie_lowest_index += int(e == r.evicted)
+                    assert e in r.legal, (
+                        f"step {t} pair {(b, h)}: GPU slot {e} outside near-tie set {r.legal}")
+                    chosen[(b, h)] = e
+                else:
+                    assert e == r.evicted, (
+                        f"step {t} pair {(b, h)}: GPU evicted {e}, oracle {r.evicted} "
+                        f"(scores {r.scores[e]:.9g} vs {r.scores[r.evicted]:.9g})")
+            oracle.commit(res, st.k_new, st.v_new, chosen)
+            rep.steps += 1
+            if check_cache_every and (t + 1) % check_cache_every == 0:
+                compare_cache(cache, oracle, layer, wl)
+        if check_cache_every:
+            compare_cache(cache, oracle, layer, wl)
+        return rep
+    finally:
+        cache.close()
+
+
+def compare_cache(cache, oracle: LayerCache, layer: int, wl: Workload) -> None:
+    """The GPU cache holds exactly the oracle's rows, fill levels and ||v||_1."""
+    k, v, vn, fill = cache.snapshot(layer)
+    k = k.float().cpu().numpy()
+    v = v.float().cpu().numpy()
+    vn = vn.cpu().numpy()
+    fill = fill.cpu().numpy()
+    for (b, h), c in oracle.cache.items():
+        n = c.n
+        assert fill[b, h] == n, f"pair {(b, h)}: fill {fill[b, h]} != {n}"
+        assert np.array_equal(k[b, h, :n], c.K[:n]), f"pair {(b, h)}: K rows differ"
+        assert np.array_equal(v[b, h, :n], c.V[:n]), f"pair {(b, h)}: V rows differ"
+        np.testing.assert_allclose(vn[b, h, :n], c.vnorm1[:n], rtol=2e-6, atol=0)
