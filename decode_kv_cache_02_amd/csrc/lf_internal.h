@@ -35,6 +35,7 @@ struct LayerPtrs {
 // Dynamic LDS bytes the decode kernel needs for this geometry, or 0 if the
 // combination (dtype, head_dim, group, slots) is not built.
 size_t decode_lds_bytes(const Geometry& g);
+size_t decode_lds_bytes_for(const Geometry& g, int waves);
 
 // LDS bytes one workgroup may use on the current device.
 size_t device_lds_limit();

@@ -40,6 +40,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kDecodeWaves = 4;                     // waves per decode workgroup
+constexpr size_t kEvictLdsCap = 160 * 1024 - 4096;  // logits of one pair; room for static LDS
+constexpr size_t kFullChunkSlots = 2048;            // FULL mode: slots per LDS-resident chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Storage types: float32 is `float`, bfloat16 is its 16-bit pattern.
@@ -181,16 +184,16 @@ struct DecodeParams {
   float scale_log2;     // tau * log2(e)
 };
 
-template <typename T, int D, int G, bool EVICT, int WAVES>
-__global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P) {
+template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB>
+__global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(DecodeParams P) {
   constexpr int kBytes = Elem<T>::kBytes;
   constexpr int NT = WAVES * kWave;
   constexpr int kChunks = D * kBytes / 64;  // 16-byte K loads per lane per 16-slot tile
   constexpr int EPL = 16 / kBytes;          // elements per 16-byte load
   constexpr int LPS = D / EPL;              // lanes per V row
   constexpr int SPI = kWave / LPS;          // V rows per wave-wide load
-  constexpr int UA = 2;                     // K tiles in flight per wave
-  constexpr int UB = 8;                     // V loads in flight per lane
+  constexpr uint32_t kRowBytes = D * kBytes;
+  constexpr int kScoreBatch = 16;           // sidecar loads in flight per thread
   static_assert(G == 1 || G == 2 || G == 4, "group width");
   static_assert(LPS <= kWave && SPI * LPS == kWave, "row split");
 
@@ -200,7 +203,6 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
   __shared__ float sh_m[G];
   __shared__ float sh_l[G];
   __shared__ float sh_w[G];
-  __shared__ float sh_snew[G];
   __shared__ float sh_vn_new;
   __shared__ float sh_best_score[WAVES];
   __shared__ int sh_best_slot[WAVES];
@@ -212,6 +214,7 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
   const int pair = blockIdx.x;
   const int b = pair / P.num_kv_heads;
   const int h = pair - b * P.num_kv_heads;
+  const int64_t slots_pad = P.pair_elems / D;
 
   const T* K = static_cast<const T*>(P.kc) + pair * P.pair_elems;
   const T* V = static_cast<const T*>(P.vc) + pair * P.pair_elems;
@@ -221,12 +224,41 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
   // The host keeps 0 <= n <= budget (and n < budget in FULL mode); clamping
   // keeps every access inside the pair's region even if that were broken.
   const int n = min(max(P.fill[pair], 0), P.budget);
-  constexpr uint32_t kRowBytes = D * kBytes;
   // Reads stop at the n valid rows: rows at or beyond n load as zeros.
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(K, static_cast<uint32_t>(n) * kRowBytes);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(n) * kRowBytes);
 
-  // New token: its logits and ||v_new||_1 (wave 0).
+  // Lane roles. K phase: r16 = slot within a 16-slot tile, grp = 16-byte
+  // chunk group. V phase: vcol = first element of the lane's 16 bytes of the
+  // row, vsub = which of the SPI rows of a wave-wide load.
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const int vcol = (lane % LPS) * EPL;
+  const int vsub = lane / LPS;
+
+  // First K tiles go out before anything else.
+  int cn = min(P.chunk, n);
+  int ntiles = (cn + 15) >> 4;
+  u32x4_t kr[UA][kChunks];
+  {
+    const uint32_t off0 = r16 * kRowBytes + 16 * grp;
+#pragma unroll
+    for (int u = 0; u < UA; ++u)
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c)
+        kr[u][c] = bload16(rK, off0 + static_cast<uint32_t>(wave * UA + u) * 16u * kRowBytes + 64 * c);
+  }
+
+  // Query operand in the MFMA A layout: lane = row (query head row % G) +
+  // 16 * (16-byte chunk group); the same byte offsets as the key loads.
+  u32x4_t qa[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    qa[c] = load16(qg + (r16 % G) * D + (64 * c + 16 * grp) / kBytes);
+
+  // Wave 0: the new token's logits open the running softmax state with
+  // weight exp2(s_new - s_new) = 1; its ||v||_1 for the write-back. Visible
+  // to the other waves after the first barrier below.
   if (wave == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -237,24 +269,15 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
         x = fmaf(to_f32(qg[g * D + d]), to_f32(kn[d]), x);
       }
       x = wave_sum(x);
-      if (lane == 0) sh_snew[g] = x * P.scale_log2;
+      if (lane == 0) {
+        sh_m[g] = x * P.scale_log2;
+        sh_l[g] = 1.0f;
+        sh_w[g] = 1.0f;
+      }
     }
     const float l1 = wave_l1<T, D>(vn, lane);
     if (lane == 0) sh_vn_new = l1;
   }
-
-  // Query operand in the MFMA A layout: lane = row (query head row % G) +
-  // 16 * (16-byte chunk group); the same byte offsets as the key loads.
-  const int r16 = lane & 15;
-  const int grp = lane >> 4;
-  u32x4_t qa[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c)
-    qa[c] = load16(qg + (r16 % G) * D + (64 * c + 16 * grp) / kBytes);
-
-  // V-phase lane roles.
-  const int vcol = (lane % LPS) * EPL;
-  const int vsub = lane / LPS;
 
   float acc[G][EPL];
 #pragma unroll
@@ -262,32 +285,36 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
 
-  // Running softmax state of the pair, one lane per query head updates it:
-  // the new token opens it with weight exp2(s_new - s_new) = 1.
-  if (tid < G) {
-    sh_m[tid] = sh_snew[tid];
-    sh_l[tid] = 1.0f;
-    sh_w[tid] = 1.0f;
+  // Sidecar of the slots this thread scores, requested now so the score
+  // phase finds it in registers (the first kScoreBatch of them).
+  const bool evicting = EVICT && n >= P.budget;
+  const __amdgpu_buffer_rsrc_t rN =
+      make_rsrc(P.vnorm1 + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
+  float vnb[kScoreBatch];
+  if (evicting) {
+#pragma unroll
+    for (int k = 0; k < kScoreBatch; ++k)
+      vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rN, static_cast<int>((P.sink + tid + k * NT) * 4), 0, 0));
   }
-  __syncthreads();
 
   for (int c0 = 0; c0 < n; c0 += P.chunk) {
-    const int cn = min(P.chunk, n - c0);
-    const int ntiles = (cn + 15) >> 4;
+    cn = min(P.chunk, n - c0);
+    ntiles = (cn + 15) >> 4;
 
     // ---------------- Phase A: logits of the chunk ----------------
     float wmax[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) wmax[g] = -INFINITY;
-    const uint32_t base_off = static_cast<uint32_t>(c0) * kRowBytes + r16 * kRowBytes + 16 * grp;
+    const uint32_t base_off = static_cast<uint32_t>(c0 + r16) * kRowBytes + 16 * grp;
+    if (c0 > 0) {  // first tiles of a later chunk (the first chunk's are already in flight)
+#pragma unroll
+      for (int u = 0; u < UA; ++u)
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c)
+          kr[u][c] = bload16(rK, base_off + static_cast<uint32_t>(wave * UA + u) * 16u * kRowBytes + 64 * c);
+    }
     for (int t0 = wave * UA; t0 < ntiles; t0 += WAVES * UA) {
-      u32x4_t kr[UA][kChunks];
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const uint32_t off = base_off + static_cast<uint32_t>(t0 + u) * 16u * kRowBytes;
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) kr[u][c] = bload16(rK, off + 64 * c);
-      }
 #pragma unroll
       for (int u = 0; u < UA; ++u) {
         if (t0 + u < ntiles) {
@@ -304,7 +331,24 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
           if (grp == 0) lds_put<G>(lds, i, s);
         }
       }
+      const int tn = t0 + WAVES * UA;
+      if (tn < ntiles) {
+#pragma unroll
+        for (int u = 0; u < UA; ++u)
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c)
+            kr[u][c] = bload16(rK, base_off + static_cast<uint32_t>(tn + u) * 16u * kRowBytes + 64 * c);
+      }
     }
+
+    // First V rows of the chunk go out before the softmax bookkeeping.
+    const int nq = (cn + SPI - 1) / SPI;
+    const uint32_t vbase = static_cast<uint32_t>(c0 + vsub) * kRowBytes + vcol * kBytes;
+    u32x4_t vr[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      vr[u] = bload16(rV, vbase + static_cast<uint32_t>((wave * UB + u) * SPI) * kRowBytes);
+
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float m = wave_max(wmax[g]);
@@ -359,13 +403,7 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
     }
 
     // ---------------- Phase B: o += p * v over the chunk ----------------
-    const int nq = (cn + SPI - 1) / SPI;
-    const uint32_t vbase = static_cast<uint32_t>(c0 + vsub) * kRowBytes + vcol * kBytes;
     for (int q0 = wave * UB; q0 < nq; q0 += WAVES * UB) {
-      u32x4_t vr[UB];
-#pragma unroll
-      for (int u = 0; u < UB; ++u)
-        vr[u] = bload16(rV, vbase + static_cast<uint32_t>((q0 + u) * SPI) * kRowBytes);
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         if (q0 + u < nq) {  // rows past the chunk have p = 0 (and load as 0 past n)
@@ -380,28 +418,45 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
             for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g], x[e], acc[g][e]);
         }
       }
+      const int qn = q0 + WAVES * UB;
+      if (qn < nq) {
+#pragma unroll
+        for (int u = 0; u < UB; ++u)
+          vr[u] = bload16(rV, vbase + static_cast<uint32_t>((qn + u) * SPI) * kRowBytes);
+      }
     }
     __syncthreads();  // LDS p and the softmax state are settled before reuse
   }
 
   // ---------------- Phase C: score + argmin (cache full) ----------------
-  const bool evicting = EVICT && n >= P.budget;
   if (EVICT && evicting) {
     float inv_l[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / sh_l[g];
     float best = INFINITY;
     int best_i = 0x7fffffff;
-    for (int i = P.sink + tid; i < n; i += NT) {
-      float p[G];
-      lds_get<G>(lds, i, p);
-      float sc = p[0] * inv_l[0];
+    for (int i0 = P.sink + tid; i0 < n; i0 += NT * kScoreBatch) {
+      if (i0 != P.sink + tid) {  // later batches (the first one was prefetched)
 #pragma unroll
-      for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
-      sc = sc * P.vnorm1[static_cast<int64_t>(pair) * (P.pair_elems / D) + i];
-      if (sc < best) {  // slots visited in increasing order: first minimum kept
-        best = sc;
-        best_i = i;
+        for (int k = 0; k < kScoreBatch; ++k)
+          vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rN, static_cast<int>((i0 + k * NT) * 4), 0, 0));
+      }
+#pragma unroll
+      for (int k = 0; k < kScoreBatch; ++k) {
+        const int i = i0 + k * NT;
+        if (i < n) {
+          float p[G];
+          lds_get<G>(lds, i, p);
+          float sc = p[0] * inv_l[0];
+#pragma unroll
+          for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
+          sc = sc * vnb[k];
+          if (sc < best) {  // slots visited in increasing order: first minimum kept
+            best = sc;
+            best_i = i;
+          }
+        }
       }
     }
 #pragma unroll
@@ -470,7 +525,7 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void decode_kernel(DecodeParams P
     store16(Vw + j * EPL, load16(vn + j * EPL));
   }
   if (tid == 0) {
-    P.vnorm1[static_cast<int64_t>(pair) * (P.pair_elems / D) + slot] = sh_vn_new;
+    P.vnorm1[static_cast<int64_t>(pair) * slots_pad + slot] = sh_vn_new;
     P.evicted[pair] = evicting ? slot : -1;
     if (!evicting) P.fill[pair] = n + 1;
   }
@@ -531,11 +586,10 @@ __global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
   }
 }
 
-template <typename T, int D, int G, bool EVICT>
+template <typename T, int D, int G, bool EVICT, int WAVES = kDecodeWaves, int UA = 1, int UB = 8>
 hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const void* q,
                            const void* k_new, const void* v_new, void* out,
                            int32_t* evicted, hipStream_t stream) {
-  constexpr int WAVES = 8;
   DecodeParams P;
   P.q = q;
   P.k_new = k_new;
@@ -554,17 +608,17 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const void* 
   P.budget = geo.budget;
   P.sink = geo.sink_size;
   P.scale_log2 = geo.scale * kLog2e;
-  const size_t lds = decode_lds_bytes(geo);
+  const size_t lds = decode_lds_bytes_for(geo, WAVES);
   P.chunk = static_cast<int32_t>(lds / (sizeof(float) * G));
   if (EVICT) P.chunk = geo.slots_pad;
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, G, EVICT, WAVES>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, G, EVICT, WAVES, UA, UB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
   const int pairs = geo.batch * geo.num_kv_heads;
-  hipLaunchKernelGGL((decode_kernel<T, D, G, EVICT, WAVES>), dim3(pairs), dim3(WAVES * kWave), lds,
+  hipLaunchKernelGGL((decode_kernel<T, D, G, EVICT, WAVES, UA, UB>), dim3(pairs), dim3(WAVES * kWave), lds,
                      stream, P);
   return hipGetLastError();
 }
@@ -591,9 +645,6 @@ hipError_t launch_fill_t(const Geometry& geo, const LayerPtrs& L, const void* k,
   return hipGetLastError();
 }
 
-constexpr size_t kEvictLdsCap = 160 * 1024 - 4096;  // leave room for static LDS
-constexpr size_t kFullChunkSlots = 2048;
-
 }  // namespace
 
 size_t device_lds_limit() {
@@ -605,12 +656,11 @@ size_t device_lds_limit() {
   return static_cast<size_t>(v);
 }
 
-size_t decode_lds_bytes(const Geometry& g) {
+size_t decode_lds_bytes_for(const Geometry& g, int waves) {
   if (g.head_dim != 64 && g.head_dim != 128) return 0;
   if (g.group != 1 && g.group != 2 && g.group != 4) return 0;
   if (g.dtype != 0 && g.dtype != 1) return 0;
-  constexpr size_t kWaves = 8;
-  const size_t red = kWaves * g.group * g.head_dim * sizeof(float);
+  const size_t red = static_cast<size_t>(waves) * g.group * g.head_dim * sizeof(float);
   size_t logits;
   if (g.mode == 0) {
     logits = static_cast<size_t>(g.slots_pad) * g.group * sizeof(float);
@@ -621,6 +671,8 @@ size_t decode_lds_bytes(const Geometry& g) {
   }
   return logits > red ? logits : red;
 }
+
+size_t decode_lds_bytes(const Geometry& g) { return decode_lds_bytes_for(g, kDecodeWaves); }
 
 hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const void* q,
                          const void* k_new, const void* v_new, void* out, int32_t* evicted,
