@@ -41,7 +41,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kDecodeWaves = 4;                     // waves per decode workgroup
-constexpr size_t kEvictLdsCap = 160 * 1024 - 4096;  // logits of one pair; room for static LDS
+constexpr int kStream = 3;                          // cache policy: non-temporal (nt) + sc0
+constexpr size_t kEvictLdsCap = 144 * 1024;        // logits of one pair; the rest is static LDS
 constexpr size_t kFullChunkSlots = 2048;            // FULL mode: slots per LDS-resident chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -80,8 +81,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), kRsrcWord3);
 }
+// POLICY is the instruction's cache-policy field; kStream marks the K/V rows
+// as non-temporal (each is read once per step, and a step's rows do not fit
+// in the caches).
+template <int POLICY = 0>
 __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, POLICY);
 }
 
 // G consecutive floats of LDS as one vector access.
@@ -140,15 +145,69 @@ __device__ __forceinline__ f32x4_t mfma_chunk(u32x4_t qa, u32x4_t kb, f32x4_t ac
   return acc;
 }
 
+// Wave-wide reductions: DPP butterflies inside each row of 16 lanes (xor 1,
+// xor 2, rotate 4, rotate 8), then the four row results combined from lanes
+// 0, 16, 32 and 48 in that order. The result is the same in every lane.
+constexpr int kDppXor1 = 0xB1;   // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;   // quad_perm(2,3,0,1)
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
-  return x;
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppRor4>(x);
+  x += dpp_f<kDppRor8>(x);
+  return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
 }
 __device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppRor4>(x));
+  x = fmaxf(x, dpp_f<kDppRor8>(x));
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+
+// Lexicographic (score, slot) minimum over the wave. Scores are >= 0, so
+// their float bits order like unsigned integers and (bits, slot) compares as
+// one 64-bit key: the smallest score wins, then the lowest slot.
+__device__ __forceinline__ void key_min(uint32_t& hi, uint32_t& lo, uint32_t h2, uint32_t l2) {
+  if (h2 < hi || (h2 == hi && l2 < lo)) {
+    hi = h2;
+    lo = l2;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ void key_min_dpp(uint32_t& hi, uint32_t& lo) {
+  const uint32_t h2 = dpp_u<CTRL>(hi);
+  const uint32_t l2 = dpp_u<CTRL>(lo);
+  key_min(hi, lo, h2, l2);
+}
+__device__ __forceinline__ void wave_argmin(float& score, int& slot) {
+  uint32_t hi = __float_as_uint(score);
+  uint32_t lo = static_cast<uint32_t>(slot);
+  key_min_dpp<kDppXor1>(hi, lo);
+  key_min_dpp<kDppXor2>(hi, lo);
+  key_min_dpp<kDppRor4>(hi, lo);
+  key_min_dpp<kDppRor8>(hi, lo);
+  uint32_t bh = __builtin_amdgcn_readlane(hi, 0), bl = __builtin_amdgcn_readlane(lo, 0);
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-  return x;
+  for (int r = 16; r < kWave; r += 16)
+    key_min(bh, bl, __builtin_amdgcn_readlane(hi, r), __builtin_amdgcn_readlane(lo, r));
+  score = __uint_as_float(bh);
+  slot = static_cast<int>(bl);
 }
 
 // ||row||_1 in float32 in one fixed order, evaluated by a whole wave; the
@@ -159,8 +218,7 @@ __device__ __forceinline__ float wave_l1(const T* row, int lane) {
   float x = 0.0f;
 #pragma unroll
   for (int k = 0; k < D / kWave; ++k) x += fabsf(to_f32(row[lane + k * kWave]));
-  x = wave_sum(x);
-  return __shfl(x, 0, kWave);
+  return wave_sum(x);
 }
 
 struct DecodeParams {
@@ -184,7 +242,7 @@ struct DecodeParams {
   float scale_log2;     // tau * log2(e)
 };
 
-template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB>
+template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY>
 __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(DecodeParams P) {
   constexpr int kBytes = Elem<T>::kBytes;
   constexpr int NT = WAVES * kWave;
@@ -198,15 +256,13 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   static_assert(LPS <= kWave && SPI * LPS == kWave, "row split");
 
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [chunk][G] logits -> p
+  __shared__ float sh_red[WAVES][G][D];     // per-wave output partials
   __shared__ float sh_part[WAVES][G];
   __shared__ float sh_part2[WAVES][G];
-  __shared__ float sh_m[G];
-  __shared__ float sh_l[G];
-  __shared__ float sh_w[G];
+  __shared__ float sh_snew[G];
   __shared__ float sh_vn_new;
   __shared__ float sh_best_score[WAVES];
   __shared__ int sh_best_slot[WAVES];
-  __shared__ int sh_victim;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -246,7 +302,8 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     for (int u = 0; u < UA; ++u)
 #pragma unroll
       for (int c = 0; c < kChunks; ++c)
-        kr[u][c] = bload16(rK, off0 + static_cast<uint32_t>(wave * UA + u) * 16u * kRowBytes + 64 * c);
+        kr[u][c] = bload16<POLICY>(
+            rK, off0 + static_cast<uint32_t>(wave * UA + u) * 16u * kRowBytes + 64 * c);
   }
 
   // Query operand in the MFMA A layout: lane = row (query head row % G) +
@@ -256,37 +313,8 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   for (int c = 0; c < kChunks; ++c)
     qa[c] = load16(qg + (r16 % G) * D + (64 * c + 16 * grp) / kBytes);
 
-  // Wave 0: the new token's logits open the running softmax state with
-  // weight exp2(s_new - s_new) = 1; its ||v||_1 for the write-back. Visible
-  // to the other waves after the first barrier below.
-  if (wave == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float x = 0.0f;
-#pragma unroll
-      for (int k = 0; k < D / kWave; ++k) {
-        const int d = lane + k * kWave;
-        x = fmaf(to_f32(qg[g * D + d]), to_f32(kn[d]), x);
-      }
-      x = wave_sum(x);
-      if (lane == 0) {
-        sh_m[g] = x * P.scale_log2;
-        sh_l[g] = 1.0f;
-        sh_w[g] = 1.0f;
-      }
-    }
-    const float l1 = wave_l1<T, D>(vn, lane);
-    if (lane == 0) sh_vn_new = l1;
-  }
-
-  float acc[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
-
-  // Sidecar of the slots this thread scores, requested now so the score
-  // phase finds it in registers (the first kScoreBatch of them).
+  // Sidecar of the slots this thread scores (the first kScoreBatch of them),
+  // requested now so the score phase finds it in registers.
   const bool evicting = EVICT && n >= P.budget;
   const __amdgpu_buffer_rsrc_t rN =
       make_rsrc(P.vnorm1 + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
@@ -297,6 +325,38 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           rN, static_cast<int>((P.sink + tid + k * NT) * 4), 0, 0));
   }
+
+  // Wave 0: the new token's logits and ||v_new||_1 (visible after the first
+  // barrier).
+  if (wave == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float x = 0.0f;
+#pragma unroll
+      for (int k = 0; k < D / kWave; ++k) {
+        const int d = lane + k * kWave;
+        x = fmaf(to_f32(qg[g * D + d]), to_f32(kn[d]), x);
+      }
+      x = wave_sum(x);
+      if (lane == 0) sh_snew[g] = x * P.scale_log2;
+    }
+    const float l1 = wave_l1<T, D>(vn, lane);
+    if (lane == 0) sh_vn_new = l1;
+  }
+
+  // Running softmax state, identical in every thread: the new token opens
+  // it with weight exp2(s_new - s_new) = 1.
+  float m_run[G], l_run[G], w_run[G];
+  float acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    l_run[g] = 1.0f;
+    w_run[g] = 1.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+  }
+  float best = INFINITY;
+  int best_i = 0x7fffffff;
 
   for (int c0 = 0; c0 < n; c0 += P.chunk) {
     cn = min(P.chunk, n - c0);
@@ -312,15 +372,18 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       for (int u = 0; u < UA; ++u)
 #pragma unroll
         for (int c = 0; c < kChunks; ++c)
-          kr[u][c] = bload16(rK, base_off + static_cast<uint32_t>(wave * UA + u) * 16u * kRowBytes + 64 * c);
+          kr[u][c] = bload16<POLICY>(
+              rK, base_off + static_cast<uint32_t>(wave * UA + u) * 16u * kRowBytes + 64 * c);
     }
-    for (int t0 = wave * UA; t0 < ntiles; t0 += WAVES * UA) {
+    // Two register sets of UA tiles: the next set is requested before the
+    // current one is multiplied, so every wave keeps K loads in flight.
+    auto qk_tiles = [&](const u32x4_t (&kt)[UA][kChunks], int t0) {
 #pragma unroll
       for (int u = 0; u < UA; ++u) {
         if (t0 + u < ntiles) {
           f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int c = 0; c < kChunks; ++c) s4 = mfma_chunk(qa[c], kr[u][c], s4, T());
+          for (int c = 0; c < kChunks; ++c) s4 = mfma_chunk(qa[c], kt[u][c], s4, T());
           const int i = (t0 + u) * 16 + r16;
           float s[G];
 #pragma unroll
@@ -331,43 +394,56 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
           if (grp == 0) lds_put<G>(lds, i, s);
         }
       }
-      const int tn = t0 + WAVES * UA;
-      if (tn < ntiles) {
+    };
+    auto load_tiles = [&](u32x4_t (&kt)[UA][kChunks], int t0) {
 #pragma unroll
-        for (int u = 0; u < UA; ++u)
+      for (int u = 0; u < UA; ++u)
 #pragma unroll
-          for (int c = 0; c < kChunks; ++c)
-            kr[u][c] = bload16(rK, base_off + static_cast<uint32_t>(tn + u) * 16u * kRowBytes + 64 * c);
-      }
+        for (int c = 0; c < kChunks; ++c)
+          kt[u][c] = bload16<POLICY>(
+              rK, base_off + static_cast<uint32_t>(t0 + u) * 16u * kRowBytes + 64 * c);
+    };
+    constexpr int kStepA = WAVES * UA;
+    u32x4_t kr2[UA][kChunks];
+    for (int t0 = wave * UA; t0 < ntiles; t0 += 2 * kStepA) {
+      if (t0 + kStepA < ntiles) load_tiles(kr2, t0 + kStepA);
+      qk_tiles(kr, t0);
+      if (t0 + 2 * kStepA < ntiles) load_tiles(kr, t0 + 2 * kStepA);
+      if (t0 + kStepA < ntiles) qk_tiles(kr2, t0 + kStepA);
     }
 
     // First V rows of the chunk go out before the softmax bookkeeping.
     const int nq = (cn + SPI - 1) / SPI;
     const uint32_t vbase = static_cast<uint32_t>(c0 + vsub) * kRowBytes + vcol * kBytes;
-    u32x4_t vr[UB];
+    constexpr int kStepB = WAVES * UB;
+    u32x4_t vr[UB], vr2[UB];
 #pragma unroll
     for (int u = 0; u < UB; ++u)
-      vr[u] = bload16(rV, vbase + static_cast<uint32_t>((wave * UB + u) * SPI) * kRowBytes);
+      vr[u] = bload16<POLICY>(rV, vbase + static_cast<uint32_t>((wave * UB + u) * SPI) * kRowBytes);
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      vr2[u] = bload16<POLICY>(
+          rV, vbase + static_cast<uint32_t>((wave * UB + kStepB + u) * SPI) * kRowBytes);
 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float m = wave_max(wmax[g]);
       if (lane == 0) sh_part[wave][g] = m;
     }
-    __syncthreads();
+    __syncthreads();  // logits, wave maxima and (first chunk) the new token visible
 
     // ---------------- A2: running max, p = exp2(s - M), sums ----------------
-    float m_new[G];
+    float fac[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float m_old = sh_m[g];
+      const float m_old = c0 == 0 ? sh_snew[g] : m_run[g];
       float m = m_old;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) m = fmaxf(m, sh_part[w][g]);
-      m_new[g] = m;
-      const float fac = exp2f(m_old - m);
+      m_run[g] = m;
+      fac[g] = exp2f(m_old - m);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= fac;
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= fac[g];
     }
     float lpart[G];
 #pragma unroll
@@ -377,7 +453,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       lds_get<G>(lds, i, x);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        x[g] = exp2f(x[g] - m_new[g]);
+        x[g] = __builtin_amdgcn_exp2f(x[g] - m_run[g]);  // v_exp_f32; -inf -> 0
         lpart[g] += x[g];
       }
       lds_put<G>(lds, i, x);
@@ -387,29 +463,63 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       const float sum = wave_sum(lpart[g]);
       if (lane == 0) sh_part2[wave][g] = sum;
     }
-    __syncthreads();  // p visible; partial sums visible; sh_m reads done
-    if (tid < G) {
-      const float m_old = sh_m[tid];
-      float m = m_old;
+    __syncthreads();  // p and the partial sums visible
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) m = fmaxf(m, sh_part[w][tid]);
-      const float fac = exp2f(m_old - m);
+    for (int g = 0; g < G; ++g) {
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) sum += sh_part2[w][tid];
-      sh_l[tid] = fmaf(sh_l[tid], fac, sum);
-      sh_w[tid] *= fac;
-      sh_m[tid] = m;
+      for (int w = 0; w < WAVES; ++w) sum += sh_part2[w][g];
+      l_run[g] = fmaf(l_run[g], fac[g], sum);
+      w_run[g] *= fac[g];
+    }
+
+    // ---------------- Phase C: score + argmin (cache full) ----------------
+    // Runs while the first V rows are in flight. Only a full cache evicts,
+    // and then the whole buffer is one chunk, so M and L are final here.
+    if (EVICT && evicting) {
+      float inv_l[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
+      for (int i0 = P.sink + tid; i0 < n; i0 += NT * kScoreBatch) {
+        if (i0 != P.sink + tid) {  // later batches (the first one was prefetched)
+#pragma unroll
+          for (int k = 0; k < kScoreBatch; ++k)
+            vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rN, static_cast<int>((i0 + k * NT) * 4), 0, 0));
+        }
+#pragma unroll
+        for (int k = 0; k < kScoreBatch; ++k) {
+          const int i = i0 + k * NT;
+          if (i < n) {
+            float p[G];
+            lds_get<G>(lds, i, p);
+            float sc = p[0] * inv_l[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
+            sc = sc * vnb[k];
+            if (sc < best) {  // slots visited in increasing order: first minimum kept
+              best = sc;
+              best_i = i;
+            }
+          }
+        }
+      }
+      wave_argmin(best, best_i);
+      if (lane == 0) {
+        sh_best_score[wave] = best;
+        sh_best_slot[wave] = best_i;
+      }
     }
 
     // ---------------- Phase B: o += p * v over the chunk ----------------
-    for (int q0 = wave * UB; q0 < nq; q0 += WAVES * UB) {
+    // Two register sets of UB rows, as for K.
+    auto pv_rows = [&](const u32x4_t (&vt)[UB], int q0) {
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         if (q0 + u < nq) {  // rows past the chunk have p = 0 (and load as 0 past n)
           const int r = (q0 + u) * SPI + vsub;
           float x[EPL];
-          unpack16(vr[u], x, T());
+          unpack16(vt[u], x, T());
           float p[G];
           lds_get<G>(lds, r, p);
 #pragma unroll
@@ -418,72 +528,19 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
             for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g], x[e], acc[g][e]);
         }
       }
-      const int qn = q0 + WAVES * UB;
-      if (qn < nq) {
+    };
+    auto load_rows = [&](u32x4_t (&vt)[UB], int q0) {
 #pragma unroll
-        for (int u = 0; u < UB; ++u)
-          vr[u] = bload16(rV, vbase + static_cast<uint32_t>((qn + u) * SPI) * kRowBytes);
-      }
+      for (int u = 0; u < UB; ++u)
+        vt[u] = bload16<POLICY>(rV, vbase + static_cast<uint32_t>((q0 + u) * SPI) * kRowBytes);
+    };
+    for (int q0 = wave * UB; q0 < nq; q0 += 2 * kStepB) {
+      pv_rows(vr, q0);
+      if (q0 + 2 * kStepB < nq) load_rows(vr, q0 + 2 * kStepB);
+      if (q0 + kStepB < nq) pv_rows(vr2, q0 + kStepB);
+      if (q0 + 3 * kStepB < nq) load_rows(vr2, q0 + 3 * kStepB);
     }
-    __syncthreads();  // LDS p and the softmax state are settled before reuse
-  }
-
-  // ---------------- Phase C: score + argmin (cache full) ----------------
-  if (EVICT && evicting) {
-    float inv_l[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / sh_l[g];
-    float best = INFINITY;
-    int best_i = 0x7fffffff;
-    for (int i0 = P.sink + tid; i0 < n; i0 += NT * kScoreBatch) {
-      if (i0 != P.sink + tid) {  // later batches (the first one was prefetched)
-#pragma unroll
-        for (int k = 0; k < kScoreBatch; ++k)
-          vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              rN, static_cast<int>((i0 + k * NT) * 4), 0, 0));
-      }
-#pragma unroll
-      for (int k = 0; k < kScoreBatch; ++k) {
-        const int i = i0 + k * NT;
-        if (i < n) {
-          float p[G];
-          lds_get<G>(lds, i, p);
-          float sc = p[0] * inv_l[0];
-#pragma unroll
-          for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
-          sc = sc * vnb[k];
-          if (sc < best) {  // slots visited in increasing order: first minimum kept
-            best = sc;
-            best_i = i;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const float os = __shfl_xor(best, off, kWave);
-      const int oi = __shfl_xor(best_i, off, kWave);
-      if (os < best || (os == best && oi < best_i)) {
-        best = os;
-        best_i = oi;
-      }
-    }
-    if (lane == 0) {
-      sh_best_score[wave] = best;
-      sh_best_slot[wave] = best_i;
-    }
-  }
-  __syncthreads();  // LDS probabilities no longer needed after this point
-  if (EVICT && evicting && tid == 0) {
-    float best = sh_best_score[0];
-    int best_i = sh_best_slot[0];
-    for (int w = 1; w < WAVES; ++w) {
-      if (sh_best_score[w] < best || (sh_best_score[w] == best && sh_best_slot[w] < best_i)) {
-        best = sh_best_score[w];
-        best_i = sh_best_slot[w];
-      }
-    }
-    sh_victim = best_i;
+    if (c0 + P.chunk < n) __syncthreads();  // the next chunk overwrites the LDS logits
   }
 
   // ---------------- Phase D: output ----------------
@@ -493,12 +550,11 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off, kWave);
-  float* red = lds;  // [WAVES][G][D], reuses the logit area
   if (lane < LPS) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) red[(wave * G + g) * D + vcol + e] = acc[g][e];
+      for (int e = 0; e < EPL; ++e) sh_red[wave][g][vcol + e] = acc[g][e];
   }
   __syncthreads();
   T* out = static_cast<T*>(P.out) + (static_cast<int64_t>(b) * P.num_q_heads + h * G) * D;
@@ -507,20 +563,32 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     const int d = idx - g * D;
     float o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) o += red[(w * G + g) * D + d];
-    o = fmaf(sh_w[g], to_f32(vn[d]), o);
-    from_f32(o / sh_l[g], out + g * D + d);
+    for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
+    o = fmaf(w_run[g], to_f32(vn[d]), o);
+    from_f32(o / l_run[g], out + g * D + d);
   }
 
   // ---------------- Phase D: in-place write of the new token ----------------
-  const int slot = evicting ? sh_victim : n;
-  if (slot >= P.budget) return;  // FULL cache already at capacity: nothing to store
   constexpr int kRowLoads = D * kBytes / 16;
+  if (tid >= 2 * kRowLoads) return;
+  int slot = n;
+  if (evicting) {  // cross-wave argmin, lowest slot on ties
+    float bs = sh_best_score[0];
+    slot = sh_best_slot[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      if (sh_best_score[w] < bs || (sh_best_score[w] == bs && sh_best_slot[w] < slot)) {
+        bs = sh_best_score[w];
+        slot = sh_best_slot[w];
+      }
+    }
+  }
+  if (slot >= P.budget) return;  // FULL cache already at capacity: nothing to store
   T* Kw = static_cast<T*>(P.kc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
   T* Vw = static_cast<T*>(P.vc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
   if (tid < kRowLoads) {
     store16(Kw + tid * EPL, load16(kn + tid * EPL));
-  } else if (tid < 2 * kRowLoads) {
+  } else {
     const int j = tid - kRowLoads;
     store16(Vw + j * EPL, load16(vn + j * EPL));
   }
@@ -586,7 +654,8 @@ __global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
   }
 }
 
-template <typename T, int D, int G, bool EVICT, int WAVES = kDecodeWaves, int UA = 1, int UB = 8>
+template <typename T, int D, int G, bool EVICT, int WAVES = kDecodeWaves, int UA = 1, int UB = 4,
+          int POLICY = kStream>
 hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const void* q,
                            const void* k_new, const void* v_new, void* out,
                            int32_t* evicted, hipStream_t stream) {
@@ -612,13 +681,13 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const void* 
   P.chunk = static_cast<int32_t>(lds / (sizeof(float) * G));
   if (EVICT) P.chunk = geo.slots_pad;
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, G, EVICT, WAVES, UA, UB>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
   const int pairs = geo.batch * geo.num_kv_heads;
-  hipLaunchKernelGGL((decode_kernel<T, D, G, EVICT, WAVES, UA, UB>), dim3(pairs), dim3(WAVES * kWave), lds,
+  hipLaunchKernelGGL((decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY>), dim3(pairs), dim3(WAVES * kWave), lds,
                      stream, P);
   return hipGetLastError();
 }
@@ -657,19 +726,16 @@ size_t device_lds_limit() {
 }
 
 size_t decode_lds_bytes_for(const Geometry& g, int waves) {
+  (void)waves;  // the per-wave output partials are static LDS
   if (g.head_dim != 64 && g.head_dim != 128) return 0;
   if (g.group != 1 && g.group != 2 && g.group != 4) return 0;
   if (g.dtype != 0 && g.dtype != 1) return 0;
-  const size_t red = static_cast<size_t>(waves) * g.group * g.head_dim * sizeof(float);
-  size_t logits;
   if (g.mode == 0) {
-    logits = static_cast<size_t>(g.slots_pad) * g.group * sizeof(float);
-    if (logits > kEvictLdsCap) return 0;
-  } else {
-    const size_t slots = g.slots_pad < static_cast<int>(kFullChunkSlots) ? g.slots_pad : kFullChunkSlots;
-    logits = slots * g.group * sizeof(float);
+    const size_t logits = static_cast<size_t>(g.slots_pad) * g.group * sizeof(float);
+    return logits > kEvictLdsCap ? 0 : logits;
   }
-  return logits > red ? logits : red;
+  const size_t slots = g.slots_pad < static_cast<int>(kFullChunkSlots) ? g.slots_pad : kFullChunkSlots;
+  return slots * g.group * sizeof(float);
 }
 
 size_t decode_lds_bytes(const Geometry& g) { return decode_lds_bytes_for(g, kDecodeWaves); }
