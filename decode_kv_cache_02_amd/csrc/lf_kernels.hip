@@ -89,6 +89,18 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, POLICY);
 }
 
+// K is stored in 16-slot tiles laid out in the order the MFMA B operand is
+// loaded: within tile t (16 rows of D elements), 1 KB block c holds, at byte
+// 16 * (16 * j + r), the 16 bytes of slot 16t + r that cover 16-byte chunk
+// 4c + j of the row. One wave-wide 16-byte load per block then reads 1 KB
+// contiguously and lands in operand order. V stays row-major.
+template <int ROW_BYTES>
+__device__ __forceinline__ uint32_t k_chunk_offset(int slot, int chunk) {
+  return static_cast<uint32_t>(slot >> 4) * (16u * ROW_BYTES) +
+         static_cast<uint32_t>(chunk >> 2) * 1024u +
+         static_cast<uint32_t>(((chunk & 3) << 4) + (slot & 15)) * 16u;
+}
+
 // G consecutive floats of LDS as one vector access.
 template <int G> struct PVec;
 template <> struct PVec<1> { typedef float type; };
@@ -281,7 +293,9 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   // keeps every access inside the pair's region even if that were broken.
   const int n = min(max(P.fill[pair], 0), P.budget);
   // Reads stop at the n valid rows: rows at or beyond n load as zeros.
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K, static_cast<uint32_t>(n) * kRowBytes);
+  constexpr uint32_t kTileBytes = 16 * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rK =
+      make_rsrc(K, static_cast<uint32_t>((n + 15) >> 4) * kTileBytes);  // whole tiles
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(n) * kRowBytes);
 
   // Lane roles. K phase: r16 = slot within a 16-slot tile, grp = 16-byte
@@ -297,13 +311,13 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   int ntiles = (cn + 15) >> 4;
   u32x4_t kr[UA][kChunks];
   {
-    const uint32_t off0 = r16 * kRowBytes + 16 * grp;
+    const uint32_t off0 = lane * 16u;
 #pragma unroll
     for (int u = 0; u < UA; ++u)
 #pragma unroll
       for (int c = 0; c < kChunks; ++c)
         kr[u][c] = bload16<POLICY>(
-            rK, off0 + static_cast<uint32_t>(wave * UA + u) * 16u * kRowBytes + 64 * c);
+            rK, off0 + static_cast<uint32_t>(wave * UA + u) * kTileBytes + 1024u * c);
   }
 
   // Query operand in the MFMA A layout: lane = row (query head row % G) +
@@ -366,14 +380,14 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     float wmax[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) wmax[g] = -INFINITY;
-    const uint32_t base_off = static_cast<uint32_t>(c0 + r16) * kRowBytes + 16 * grp;
+    const uint32_t base_off = static_cast<uint32_t>(c0 >> 4) * kTileBytes + lane * 16u;
     if (c0 > 0) {  // first tiles of a later chunk (the first chunk's are already in flight)
 #pragma unroll
       for (int u = 0; u < UA; ++u)
 #pragma unroll
         for (int c = 0; c < kChunks; ++c)
           kr[u][c] = bload16<POLICY>(
-              rK, base_off + static_cast<uint32_t>(wave * UA + u) * 16u * kRowBytes + 64 * c);
+              rK, base_off + static_cast<uint32_t>(wave * UA + u) * kTileBytes + 1024u * c);
     }
     // Two register sets of UA tiles: the next set is requested before the
     // current one is multiplied, so every wave keeps K loads in flight.
@@ -401,7 +415,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
 #pragma unroll
         for (int c = 0; c < kChunks; ++c)
           kt[u][c] = bload16<POLICY>(
-              rK, base_off + static_cast<uint32_t>(t0 + u) * 16u * kRowBytes + 64 * c);
+              rK, base_off + static_cast<uint32_t>(t0 + u) * kTileBytes + 1024u * c);
     };
     constexpr int kStepA = WAVES * UA;
     u32x4_t kr2[UA][kChunks];
@@ -584,10 +598,10 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     }
   }
   if (slot >= P.budget) return;  // FULL cache already at capacity: nothing to store
-  T* Kw = static_cast<T*>(P.kc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
+  char* Kw = reinterpret_cast<char*>(static_cast<T*>(P.kc_w) + pair * P.pair_elems);
   T* Vw = static_cast<T*>(P.vc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
   if (tid < kRowLoads) {
-    store16(Kw + tid * EPL, load16(kn + tid * EPL));
+    store16(Kw + k_chunk_offset<kRowBytes>(slot, tid), load16(kn + tid * EPL));
   } else {
     const int j = tid - kRowLoads;
     store16(Vw + j * EPL, load16(vn + j * EPL));
@@ -619,6 +633,10 @@ struct FillParams {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
+  constexpr int kBytes = Elem<T>::kBytes;
+  constexpr int kRowBytes = D * kBytes;
+  constexpr int kRowChunks = kRowBytes / 16;  // 16-byte chunks per row (<= 32)
+  constexpr int EPL = 16 / kBytes;
   const int lane = threadIdx.x & (kWave - 1);
   const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int local_pair = blockIdx.y;
@@ -628,25 +646,22 @@ __global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
   const int64_t pair = static_cast<int64_t>(b) * P.num_kv_heads + h;
   const int nb = P.n[bl];
   if (slot >= P.slots_pad) return;
-  T* Kd = static_cast<T*>(P.kc) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
+  char* Kd = reinterpret_cast<char*>(static_cast<T*>(P.kc) + pair * P.pair_elems);
   T* Vd = static_cast<T*>(P.vc) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
   float l1 = 0.0f;
   if (slot < nb) {
     const int64_t src = ((static_cast<int64_t>(b) * P.n_max + slot) * P.num_kv_heads + h) * D;
     const T* ks = static_cast<const T*>(P.k) + src;
     const T* vs = static_cast<const T*>(P.v) + src;
-#pragma unroll
-    for (int k = 0; k < D / kWave; ++k) {
-      Kd[lane + k * kWave] = ks[lane + k * kWave];
-      Vd[lane + k * kWave] = vs[lane + k * kWave];
+    if (lane < kRowChunks) {
+      store16(Kd + k_chunk_offset<kRowBytes>(slot, lane), load16(ks + lane * EPL));
+      store16(Vd + lane * EPL, load16(vs + lane * EPL));
     }
     l1 = wave_l1<T, D>(vs, lane);
-  } else {
-#pragma unroll
-    for (int k = 0; k < D / kWave; ++k) {
-      Kd[lane + k * kWave] = T(0);
-      Vd[lane + k * kWave] = T(0);
-    }
+  } else if (lane < kRowChunks) {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    store16(Kd + k_chunk_offset<kRowBytes>(slot, lane), zero);
+    store16(Vd + lane * EPL, zero);
   }
   if (lane == 0) {
     P.vnorm1[pair * P.slots_pad + slot] = l1;

@@ -202,6 +202,20 @@ def lf_status_str(status: int) -> str:
     return status_str(status)
 
 
+def untile_k(k_tiled, head_dim: int):
+    """Row-major view of a K snapshot [..., slots_padded * head_dim] stored in
+    the tiled MFMA-operand layout documented in include/longflow.h."""
+    elem_bytes = k_tiled.element_size()
+    per_chunk = 16 // elem_bytes                  # elements per 16-byte chunk
+    blocks = head_dim * elem_bytes // 64          # 1 KB blocks per 16-slot tile
+    lead = tuple(k_tiled.shape[:-1])
+    tiles = k_tiled.shape[-1] // (16 * head_dim)
+    t = k_tiled.reshape(lead + (tiles, blocks, 4, 16, per_chunk))
+    nd = len(lead)
+    t = t.permute(*range(nd), nd, nd + 3, nd + 1, nd + 2, nd + 4)   # tile, slot, block, j, elem
+    return t.reshape(lead + (tiles * 16, head_dim))
+
+
 # ----------------------------------------------------------------------------
 # Convenience owner of one handle, with tensor checks
 # ----------------------------------------------------------------------------
@@ -258,17 +272,19 @@ class LongFlowCache:
         return lf_fill_levels(self.handle, layer, self.batch)
 
     def snapshot(self, layer):
-        """Copies of one layer: K, V [batch][hkv][slots_pad][d], ||v||_1 [batch][hkv][slots_pad],
-        fill [batch][hkv] (device tensors, stream-ordered)."""
+        """Copies of one layer: K, V [batch][hkv][slots_pad][d] (K un-tiled to
+        row-major), ||v||_1 [batch][hkv][slots_pad], fill [batch][hkv]; device
+        tensors, stream-ordered."""
         import torch
         slots = self.view(layer).slots_padded
-        k = torch.empty((self.batch, self.hkv, slots, self.head_dim), dtype=self.torch_dtype,
+        k = torch.empty((self.batch, self.hkv, slots * self.head_dim), dtype=self.torch_dtype,
                         device="cuda")
         v = torch.empty_like(k)
         vn = torch.empty((self.batch, self.hkv, slots), dtype=torch.float32, device="cuda")
         fill = torch.empty((self.batch, self.hkv), dtype=torch.int32, device="cuda")
         lf_cache_snapshot(self.handle, layer, k, v, vn, fill)
-        return k, v, vn, fill
+        return (untile_k(k, self.head_dim), v.view(self.batch, self.hkv, slots, self.head_dim),
+                vn, fill)
 
     def close(self):
         if getattr(self, "handle", None):

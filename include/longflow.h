@@ -84,10 +84,17 @@ typedef struct {
   int32_t mode;         /* lf_mode                                               */
 } lf_config;
 
-/* Device addresses and strides of one layer's region (for tests, snapshots). */
+/* Device addresses and strides of one layer's region (for tests, snapshots).
+ *
+ * K layout (MFMA operand order). Each pair's K region holds slots_padded/16
+ * tiles of 16 slots x head_dim elements (16 * head_dim * elem_bytes bytes).
+ * A row is cut into 16-byte chunks (E = 16/elem_bytes elements each). Inside
+ * tile t, chunk k of slot 16t + r (r in 0..15) is stored at byte offset
+ *     1024 * (k / 4) + 16 * (16 * (k % 4) + r).
+ * V is row-major: element (slot i, dim d) of a pair is at i * head_dim + d. */
 typedef struct {
-  void* k;              /* [batch][num_kv_heads][slots_padded][head_dim] cfg.dtype */
-  void* v;              /* same layout                                              */
+  void* k;              /* [batch][num_kv_heads][slots_padded/16 tiles] cfg.dtype, tiled as above */
+  void* v;              /* [batch][num_kv_heads][slots_padded][head_dim] cfg.dtype                */
   float* vnorm1;        /* [batch][num_kv_heads][slots_padded] float32              */
   int32_t* fill;        /* [batch][num_kv_heads] int32: tokens held per pair        */
   int64_t pair_stride;  /* elements between consecutive pairs in k / v             */
@@ -133,7 +140,8 @@ lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view);
 /* Snapshot of one layer into caller-owned DEVICE buffers, stream-ordered
  * device-to-device copies (tests, checkpoints; the static layout makes each a
  * single contiguous copy):
- *   k, v    [batch][num_kv_heads][slots_padded][head_dim] cfg.dtype
+ *   k, v    [batch][num_kv_heads][slots_padded*head_dim] cfg.dtype, in the
+ *           layouts of lf_view (K tiled, V row-major)
  *   vnorm1  [batch][num_kv_heads][slots_padded] float32
  *   fill    [batch][num_kv_heads] int32
  * Any of the four may be NULL to skip it. */
