@@ -80,6 +80,8 @@ def parse_args():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--suite", action="store_true",
+                    help="measure every workload shape (one JSON line each) instead of the bench line")
     return ap.parse_args()
 
 
@@ -171,8 +173,118 @@ def full_kv_baseline(wl, steps, warmup, fills=(8704, 16384)):
             "capacity": cap, "at_fill": res}
 
 
+def steady_state(wl, steps, warmup, fill=None, mode="evict", layers=1, capacity=None,
+                 ragged=None, seed=0):
+    """Time `steps` model steps (one lf_decode_step per layer) at the given
+    fill levels; returns (ms per model step, algorithmic bytes per model step)."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import device_prefill
+    e = 2 if wl.dtype == "bf16" else 4
+    cap = wl.budget if capacity is None else capacity
+    torch.cuda.empty_cache()
+    cache = LongFlowCache(layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, cap,
+                          dtype=wl.dtype, mode=mode)
+    try:
+        n = np.full(wl.batch, wl.budget if fill is None else fill, dtype=np.int64)
+        if ragged is not None:
+            n = np.asarray(ragged, dtype=np.int64)
+        n_max = int(n.max(initial=0))
+        for layer in range(layers):
+            if n_max > 0:
+                k, v = device_prefill(wl.with_(), n_max, seed=seed * 1000 + layer)
+                cache.prefill(layer, k, v, n.astype(np.int32))
+                del k, v
+            else:
+                cache.prefill(layer, None, None, n.astype(np.int32))
+        ring = make_ring(wl, wl.dtype)
+        dt = ring[0][0].dtype
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=dt, device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        for t in range(warmup):
+            q, kn, vn = ring[t % RING]
+            for layer in range(layers):
+                cache.decode_step(layer, q, kn, vn, out, ev)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for t in range(steps):
+            q, kn, vn = ring[t % RING]
+            for layer in range(layers):
+                cache.decode_step(layer, q, kn, vn, out, ev)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        # fill levels during the timed window (EVICT caps at the budget)
+        n_mid = n + warmup + steps // 2
+        if mode == "evict":
+            n_mid = np.minimum(n_mid, wl.budget)
+        evict_flags = (n + warmup >= wl.budget) if mode == "evict" else np.zeros_like(n, bool)
+        per_layer = sum(algorithmic_bytes_per_pair(int(nb), wl.group, wl.head_dim, e, bool(ev_))
+                        for nb, ev_ in zip(n_mid, evict_flags)) * wl.num_kv_heads
+        return ms, per_layer * layers
+    finally:
+        cache.close()
+
+
+def suite(args):
+    """One JSON line per workload shape (steady state unless stated)."""
+    import torch
+    from decode_kv_cache_02_amd.native import lf_cache_bytes, make_config
+    from decode_kv_cache_02_amd.synth import WORKLOADS, TokenStream
+
+    def emit(name, wl, ms, nbytes, layers=1, extra=None):
+        line = {"workload": name, "batch": wl.batch, "heads": f"{wl.num_q_heads}/{wl.num_kv_heads}",
+                "head_dim": wl.head_dim, "budget": wl.budget, "layers": layers,
+                "ms_per_model_step": ms, "tokens_per_s": wl.batch / ms * 1e3,
+                "achieved_GBs": nbytes / ms / 1e6,
+                "frac_of_peak": nbytes / ms / 1e6 / HBM_PEAK_GBS}
+        line.update(extra or {})
+        print(json.dumps(line), flush=True)
+
+    steps, warmup = min(args.steps, 300), 20
+    wl2 = WORKLOADS["qwen3_0p6b_layer"]
+    ms, nb = steady_state(wl2, steps, warmup)
+    emit("qwen3_0p6b_layer", wl2, ms, nb)
+    wl3 = WORKLOADS["llama8b_layer"]
+    for fill in (512, 1638, 3000):
+        ms, nb = steady_state(wl3, steps, warmup, fill=fill)
+        emit(f"llama8b_layer fill {fill} (appending)", wl3, ms, nb)
+    ms, nb = steady_state(wl3, steps, warmup)
+    emit("llama8b_layer steady state", wl3, ms, nb)
+    shard = wl3.with_(num_q_heads=4, num_kv_heads=1)
+    ms, nb = steady_state(shard, steps, warmup)
+    emit("llama8b_layer tp8 shard (1 KV head per GPU)", shard, ms, nb)
+    # 32-layer ragged stack at the batch where both caches fit 0.95 x 288 GB
+    wl4 = WORKLOADS["llama8b_stack32_ragged"]
+    cfg_c = make_config(32, 1, 32, 8, 128, wl4.budget)
+    cfg_f = make_config(32, 1, 32, 8, 128, 16384 + 512 + 64, mode="full")
+    per_seq = lf_cache_bytes(cfg_c) + lf_cache_bytes(cfg_f)
+    batch = int(0.95 * 288e9 // per_seq)
+    wl4 = wl4.with_(batch=batch)
+    offsets = TokenStream(wl4).start_offsets()
+    ms, nb = steady_state(wl4, min(steps, 50), 5, layers=32,
+                          ragged=np.minimum(offsets, wl4.budget), seed=4)
+    emit("llama8b_stack32_ragged LongFlow", wl4, ms, nb, 32,
+         {"batch_rule": "largest batch with both caches in 0.95 x 288 GB", "evicting_seqs": int(np.sum(offsets >= wl4.budget))})
+    ms, nb = steady_state(wl4, min(steps, 20), 2, layers=32, mode="full",
+                          capacity=16384 + 512 + 64, ragged=offsets, seed=4)
+    emit("llama8b_stack32_ragged full-KV", wl4, ms, nb, 32)
+    wl5 = WORKLOADS["qwen3_8b_stack36_ties"]
+    for budget in (512, 1024, 2048, 4096):
+        w = wl5.with_(budget=budget)
+        ms, nb = steady_state(w, min(steps, 30), 3, layers=36, seed=5)
+        emit(f"qwen3_8b_stack36 B={budget}", w, ms, nb, 36)
+
+
 def main():
     args = parse_args()
+    if args.suite:
+        import torch
+        torch.cuda.set_device(0)
+        suite(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(each (sequence, KV head) pair is independent: a multi-GPU run would shard "
