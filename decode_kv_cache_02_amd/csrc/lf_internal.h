@@ -32,16 +32,34 @@ struct LayerPtrs {
   int32_t* fill;
 };
 
+// Split-K workspace of one layer launch: per (pair, split) the partial
+// softmax state, per pair the raw logits of a full cache and an arrival
+// counter (zero between launches).
+struct SplitWork {
+  float* part;        // [pairs][max_splits][split_part_floats]
+  float* logit;       // [pairs][slots_pad][group]
+  int32_t* arrive;    // [pairs]
+};
+
+constexpr int kMaxSplits = 16;
+constexpr int kSplitGridTarget = 512;  // split workgroups per layer launch (2 per MI355X CU)
+constexpr int kSplitPairsBelow = 256;  // split only layers with fewer pairs than CUs
+constexpr int kMinSplitSlots = 256;   // fewer slots per split are not worth a split
+
 // Dynamic LDS bytes the decode kernel needs for this geometry, or 0 if the
 // combination (dtype, head_dim, group, slots) is not built.
 size_t decode_lds_bytes(const Geometry& g);
 size_t decode_lds_bytes_for(const Geometry& g, int waves);
+size_t decode_split_lds_bytes(const Geometry& g, int splits);
+size_t split_part_floats(const Geometry& g);
 
 // LDS bytes one workgroup may use on the current device.
 size_t device_lds_limit();
 
-hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const void* q,
-                         const void* k_new, const void* v_new, void* out,
+// splits == 1: one workgroup per pair. splits > 1: split-K over `splits`
+// workgroups per pair (W must then hold room for that many).
+hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
+                         const void* q, const void* k_new, const void* v_new, void* out,
                          int32_t* evicted, hipStream_t stream);
 
 // Copies rows [0, n_b) of each sequence into slots 0..n_b-1 and clears the

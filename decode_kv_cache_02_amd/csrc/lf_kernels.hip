@@ -250,11 +250,77 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t budget;
   int32_t sink;
-  int32_t chunk;        // slots per LDS-resident chunk (EVICT: the whole buffer)
+  int32_t chunk;        // slots per LDS-resident chunk (EVICT: a whole split)
   float scale_log2;     // tau * log2(e)
+  // Split-K across workgroups (SPLIT kernels only).
+  int32_t pairs;        // pairs of the layer
+  int32_t splits;       // workgroups per pair
+  float* ws_part;       // [pairs][splits][2G + G*D]: m, l, unnormalised output
+  float* ws_logit;      // [pairs][slots_pad][G]: raw logits (cache full only)
+  int32_t* arrive;      // [pairs]: arrivals, back to 0 after every launch
 };
 
-template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY>
+// Cross-workgroup data of a split launch goes through relaxed agent-scope
+// atomic accesses: each is coherent across the XCDs on its own, so no
+// whole-cache writeback or invalidate is needed. The writer drains its
+// stores before it takes its ticket, and the last split reads only after
+// its ticket says every other split has arrived.
+__device__ __forceinline__ void ws_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ws_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void drain_stores() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// The G logits of one slot as one buffer access with the device-scope cache
+// policy (the sc1 bit, as the relaxed agent-scope atomics above use).
+constexpr int kDeviceScope = 16;
+template <int G>
+__device__ __forceinline__ void ws_store_g(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[G]) {
+  if constexpr (G == 4) {
+    u32x4_t v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                 __float_as_uint(x[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, kDeviceScope);
+  } else if constexpr (G == 2) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    u32x2_t v = {__float_as_uint(x[0]), __float_as_uint(x[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(off), 0, kDeviceScope);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[0]), r, static_cast<int>(off), 0,
+                                          kDeviceScope);
+  }
+}
+template <int G>
+__device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[G]) {
+  if constexpr (G == 4) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kDeviceScope);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) x[g] = __uint_as_float(v[g]);
+  } else if constexpr (G == 2) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, kDeviceScope);
+    x[0] = __uint_as_float(v[0]);
+    x[1] = __uint_as_float(v[1]);
+  } else {
+    x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, kDeviceScope));
+  }
+}
+
+/*
+ * One decode step.
+ *   SPLIT = false: one workgroup per pair (blockIdx.x = pair).
+ *   SPLIT = true : `splits` workgroups per pair (blockIdx.x = split * pairs +
+ *                  pair), each over a contiguous range of 16-slot tiles. Each
+ *                  publishes its partial softmax state (m, l, output) and,
+ *                  when the cache is full, its raw logits; the last split to
+ *                  arrive combines the partials, scores every slot against
+ *                  the global max and sum, takes the argmin and writes the
+ *                  output and the new token. No workgroup ever waits.
+ */
+template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT>
 __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(DecodeParams P) {
   constexpr int kBytes = Elem<T>::kBytes;
   constexpr int NT = WAVES * kWave;
@@ -264,10 +330,11 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   constexpr int SPI = kWave / LPS;          // V rows per wave-wide load
   constexpr uint32_t kRowBytes = D * kBytes;
   constexpr int kScoreBatch = 16;           // sidecar loads in flight per thread
+  constexpr int kRowLoads = D * kBytes / 16;
   static_assert(G == 1 || G == 2 || G == 4, "group width");
   static_assert(LPS <= kWave && SPI * LPS == kWave, "row split");
 
-  extern __shared__ __attribute__((aligned(16))) float lds[];  // [chunk][G] logits -> p
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [chunk][G] logits (-> p)
   __shared__ float sh_red[WAVES][G][D];     // per-wave output partials
   __shared__ float sh_part[WAVES][G];
   __shared__ float sh_part2[WAVES][G];
@@ -275,11 +342,18 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   __shared__ float sh_vn_new;
   __shared__ float sh_best_score[WAVES];
   __shared__ int sh_best_slot[WAVES];
+  __shared__ float sh_gm[G];                // SPLIT: global max and sum of the pair
+  __shared__ float sh_gl[G];
+  __shared__ int sh_ticket;
+  (void)sh_gm;
+  (void)sh_gl;
+  (void)sh_ticket;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
-  const int pair = blockIdx.x;
+  const int pair = SPLIT ? static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.pairs)) : blockIdx.x;
+  const int split = SPLIT ? static_cast<int>(blockIdx.x / static_cast<uint32_t>(P.pairs)) : 0;
   const int b = pair / P.num_kv_heads;
   const int h = pair - b * P.num_kv_heads;
   const int64_t slots_pad = P.pair_elems / D;
@@ -298,6 +372,17 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       make_rsrc(K, static_cast<uint32_t>((n + 15) >> 4) * kTileBytes);  // whole tiles
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(n) * kRowBytes);
 
+  // This workgroup's slots: [lo, hi), whole 16-slot tiles.
+  int lo = 0, hi = n;
+  if (SPLIT) {
+    const int tiles = (n + 15) >> 4;
+    const int per = (tiles + P.splits - 1) / P.splits;
+    const int tb = min(split * per, tiles);
+    lo = tb * 16;
+    hi = min(min(tb + per, tiles) * 16, n);
+  }
+  float* pbuf = lds;  // p overwrites the logits in place
+
   // Lane roles. K phase: r16 = slot within a 16-slot tile, grp = 16-byte
   // chunk group. V phase: vcol = first element of the lane's 16 bytes of the
   // row, vsub = which of the SPI rows of a wave-wide load.
@@ -307,11 +392,11 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   const int vsub = lane / LPS;
 
   // First K tiles go out before anything else.
-  int cn = min(P.chunk, n);
+  int cn = min(P.chunk, hi - lo);
   int ntiles = (cn + 15) >> 4;
   u32x4_t kr[UA][kChunks];
   {
-    const uint32_t off0 = lane * 16u;
+    const uint32_t off0 = static_cast<uint32_t>(lo >> 4) * kTileBytes + lane * 16u;
 #pragma unroll
     for (int u = 0; u < UA; ++u)
 #pragma unroll
@@ -330,14 +415,15 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   // Sidecar of the slots this thread scores (the first kScoreBatch of them),
   // requested now so the score phase finds it in registers.
   const bool evicting = EVICT && n >= P.budget;
+  const int sc_lo = max(lo, P.sink);
   const __amdgpu_buffer_rsrc_t rN =
-      make_rsrc(P.vnorm1 + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
+      make_rsrc(P.vnorm1 + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(hi) * 4u);
   float vnb[kScoreBatch];
-  if (evicting) {
+  if (!SPLIT && evicting) {
 #pragma unroll
     for (int k = 0; k < kScoreBatch; ++k)
       vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rN, static_cast<int>((P.sink + tid + k * NT) * 4), 0, 0));
+          rN, static_cast<int>((sc_lo + tid + k * NT) * 4), 0, 0));
   }
 
   // Wave 0: the new token's logits and ||v_new||_1 (visible after the first
@@ -358,22 +444,25 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     if (lane == 0) sh_vn_new = l1;
   }
 
-  // Running softmax state, identical in every thread: the new token opens
-  // it with weight exp2(s_new - s_new) = 1.
+  // Running softmax state, identical in every thread. One workgroup per
+  // pair: the new token opens it with weight exp2(s_new - s_new) = 1. Split:
+  // the partial holds the split's own slots only (the new token is added
+  // once, when the partials are combined).
   float m_run[G], l_run[G], w_run[G];
   float acc[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    l_run[g] = 1.0f;
-    w_run[g] = 1.0f;
+    m_run[g] = -INFINITY;
+    l_run[g] = SPLIT ? 0.0f : 1.0f;
+    w_run[g] = SPLIT ? 0.0f : 1.0f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
   }
   float best = INFINITY;
   int best_i = 0x7fffffff;
 
-  for (int c0 = 0; c0 < n; c0 += P.chunk) {
-    cn = min(P.chunk, n - c0);
+  for (int c0 = lo; c0 < hi; c0 += P.chunk) {
+    cn = min(P.chunk, hi - c0);
     ntiles = (cn + 15) >> 4;
 
     // ---------------- Phase A: logits of the chunk ----------------
@@ -381,7 +470,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g) wmax[g] = -INFINITY;
     const uint32_t base_off = static_cast<uint32_t>(c0 >> 4) * kTileBytes + lane * 16u;
-    if (c0 > 0) {  // first tiles of a later chunk (the first chunk's are already in flight)
+    if (c0 > lo) {  // first tiles of a later chunk (the first chunk's are already in flight)
 #pragma unroll
       for (int u = 0; u < UA; ++u)
 #pragma unroll
@@ -450,7 +539,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     float fac[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float m_old = c0 == 0 ? sh_snew[g] : m_run[g];
+      const float m_old = c0 == lo ? sh_snew[g] : m_run[g];
       float m = m_old;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) m = fmaxf(m, sh_part[w][g]);
@@ -462,15 +551,21 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     float lpart[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
+    // Split with a full cache: this pair's raw-logit area (no records otherwise).
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(SPLIT && evicting ? P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G : nullptr,
+                  SPLIT && evicting ? static_cast<uint32_t>(slots_pad) * G * 4u : 0u);
     for (int i = tid; i < ntiles * 16; i += NT) {  // masked slots hold -inf -> p = 0
       float x[G];
       lds_get<G>(lds, i, x);
+      if (SPLIT && evicting && i < cn)  // raw logits for the last split's score
+        ws_store_g<G>(rW, static_cast<uint32_t>(c0 + i) * G * 4u, x);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         x[g] = __builtin_amdgcn_exp2f(x[g] - m_run[g]);  // v_exp_f32; -inf -> 0
         lpart[g] += x[g];
       }
-      lds_put<G>(lds, i, x);
+      lds_put<G>(pbuf, i, x);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -488,9 +583,10 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     }
 
     // ---------------- Phase C: score + argmin (cache full) ----------------
-    // Runs while the first V rows are in flight. Only a full cache evicts,
-    // and then the whole buffer is one chunk, so M and L are final here.
-    if (EVICT && evicting) {
+    // One workgroup per pair: runs while the first V rows are in flight.
+    // Only a full cache evicts, and then the whole buffer is one chunk, so M
+    // and L are final here.
+    if (!SPLIT && EVICT && evicting) {
       float inv_l[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
@@ -535,7 +631,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
           float x[EPL];
           unpack16(vt[u], x, T());
           float p[G];
-          lds_get<G>(lds, r, p);
+          lds_get<G>(pbuf, r, p);
 #pragma unroll
           for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -554,10 +650,10 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       if (q0 + kStepB < nq) pv_rows(vr2, q0 + kStepB);
       if (q0 + 3 * kStepB < nq) load_rows(vr2, q0 + 3 * kStepB);
     }
-    if (c0 + P.chunk < n) __syncthreads();  // the next chunk overwrites the LDS logits
+    if (c0 + P.chunk < hi) __syncthreads();  // the next chunk overwrites the LDS logits
   }
 
-  // ---------------- Phase D: output ----------------
+  // ---------------- Phase D: cross-wave output reduction ----------------
 #pragma unroll
   for (int off = LPS; off < kWave; off <<= 1)
 #pragma unroll
@@ -572,31 +668,140 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   }
   __syncthreads();
   T* out = static_cast<T*>(P.out) + (static_cast<int64_t>(b) * P.num_q_heads + h * G) * D;
-  for (int idx = tid; idx < G * D; idx += NT) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float o = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
-    o = fmaf(w_run[g], to_f32(vn[d]), o);
-    from_f32(o / l_run[g], out + g * D + d);
-  }
 
-  // ---------------- Phase D: in-place write of the new token ----------------
-  constexpr int kRowLoads = D * kBytes / 16;
-  if (tid >= 2 * kRowLoads) return;
   int slot = n;
-  if (evicting) {  // cross-wave argmin, lowest slot on ties
-    float bs = sh_best_score[0];
-    slot = sh_best_slot[0];
+  if constexpr (!SPLIT) {
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int g = idx / D;
+      const int d = idx - g * D;
+      float o = 0.0f;
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) {
-      if (sh_best_score[w] < bs || (sh_best_score[w] == bs && sh_best_slot[w] < slot)) {
-        bs = sh_best_score[w];
-        slot = sh_best_slot[w];
+      for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
+      o = fmaf(w_run[g], to_f32(vn[d]), o);
+      from_f32(o / l_run[g], out + g * D + d);
+    }
+    if (tid >= 2 * kRowLoads) return;
+    if (evicting) {  // cross-wave argmin, lowest slot on ties
+      float bs = sh_best_score[0];
+      slot = sh_best_slot[0];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) {
+        if (sh_best_score[w] < bs || (sh_best_score[w] == bs && sh_best_slot[w] < slot)) {
+          bs = sh_best_score[w];
+          slot = sh_best_slot[w];
+        }
       }
     }
+  } else {
+    // ---------------- Split: publish this split's partial state ----------------
+    constexpr int kPart = 2 * G + G * D;
+    const int S = P.splits;
+    float* mine = P.ws_part + (static_cast<int64_t>(pair) * S + split) * kPart;
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int g = idx / D;
+      const int d = idx - g * D;
+      float o = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
+      ws_store(mine + 2 * G + idx, o);
+    }
+    if (tid < G) {
+      ws_store(mine + tid, m_run[tid]);  // -inf for a split with no slots
+      ws_store(mine + G + tid, l_run[tid]);
+    }
+    drain_stores();
+    __syncthreads();
+    if (tid == 0)
+      sh_ticket = __hip_atomic_fetch_add(P.arrive + pair, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sh_ticket != S - 1) return;  // not the last split of the pair
+
+    // ---------------- Last split: combine, score, choose ----------------
+    const float* part = P.ws_part + static_cast<int64_t>(pair) * S * kPart;
+    if (tid < G) {  // global max and sum, new token included, fixed order
+      const int g = tid;
+      float M = sh_snew[g];
+      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, ws_load(part + s2 * kPart + g));
+      float L = __builtin_amdgcn_exp2f(sh_snew[g] - M);
+      for (int s2 = 0; s2 < S; ++s2)
+        L = fmaf(ws_load(part + s2 * kPart + G + g),
+                 __builtin_amdgcn_exp2f(ws_load(part + s2 * kPart + g) - M), L);
+      sh_gm[g] = M;
+      sh_gl[g] = L;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int g = idx / D;
+      const int d = idx - g * D;
+      const float M = sh_gm[g];
+      float o = 0.0f;
+      for (int s2 = 0; s2 < S; ++s2)
+        o = fmaf(ws_load(part + s2 * kPart + 2 * G + idx),
+                 __builtin_amdgcn_exp2f(ws_load(part + s2 * kPart + g) - M), o);
+      o = fmaf(__builtin_amdgcn_exp2f(sh_snew[g] - M), to_f32(vn[d]), o);
+      from_f32(o / sh_gl[g], out + g * D + d);
+    }
+    if (evicting) {
+      // Score every slot from the published raw logits: the same operations
+      // as one workgroup per pair, so equal tokens get bit-equal scores.
+      float inv_l[G], gm[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        inv_l[g] = 1.0f / sh_gl[g];
+        gm[g] = sh_gm[g];
+      }
+      const __amdgpu_buffer_rsrc_t rL = make_rsrc(
+          P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(n) * G * 4u);
+      const __amdgpu_buffer_rsrc_t rNa =
+          make_rsrc(P.vnorm1 + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
+      constexpr int kLastBatch = 8;  // slots per thread with loads in flight together
+      for (int i0 = P.sink + tid; i0 < n; i0 += NT * kLastBatch) {
+        float vb[kLastBatch];
+        float lg[kLastBatch][G];
+#pragma unroll
+        for (int k = 0; k < kLastBatch; ++k) {
+          vb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rNa, static_cast<int>((i0 + k * NT) * 4), 0, 0));
+          ws_load_g<G>(rL, static_cast<uint32_t>(i0 + k * NT) * G * 4u, lg[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kLastBatch; ++k) {
+          const int i = i0 + k * NT;
+          if (i < n) {
+            float p[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) p[g] = __builtin_amdgcn_exp2f(lg[k][g] - gm[g]);
+            float sc = p[0] * inv_l[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
+            sc = sc * vb[k];
+            if (sc < best) {
+              best = sc;
+              best_i = i;
+            }
+          }
+        }
+      }
+      wave_argmin(best, best_i);
+      if (lane == 0) {
+        sh_best_score[wave] = best;
+        sh_best_slot[wave] = best_i;
+      }
+      __syncthreads();
+      if (tid < 2 * kRowLoads) {  // cross-wave argmin, lowest slot on ties
+        uint32_t bh = __float_as_uint(sh_best_score[0]);
+        uint32_t bl = static_cast<uint32_t>(sh_best_slot[0]);
+        for (int w = 1; w < WAVES; ++w)
+          key_min(bh, bl, __float_as_uint(sh_best_score[w]), static_cast<uint32_t>(sh_best_slot[w]));
+        slot = static_cast<int>(bl);
+      }
+    }
+    if (tid == 0) __hip_atomic_store(P.arrive + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid >= 2 * kRowLoads) return;
   }
+
+  // ---------------- In-place write of the new token ----------------
   if (slot >= P.budget) return;  // FULL cache already at capacity: nothing to store
   char* Kw = reinterpret_cast<char*>(static_cast<T*>(P.kc_w) + pair * P.pair_elems);
   T* Vw = static_cast<T*>(P.vc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
@@ -669,10 +874,10 @@ __global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
   }
 }
 
-template <typename T, int D, int G, bool EVICT, int WAVES = kDecodeWaves, int UA = 1, int UB = 4,
-          int POLICY = kStream>
-hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const void* q,
-                           const void* k_new, const void* v_new, void* out,
+template <typename T, int D, int G, bool EVICT, bool SPLIT, int WAVES = kDecodeWaves, int UA = 1,
+          int UB = 4, int POLICY = kStream>
+hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitWork& W, int splits,
+                           const void* q, const void* k_new, const void* v_new, void* out,
                            int32_t* evicted, hipStream_t stream) {
   DecodeParams P;
   P.q = q;
@@ -692,18 +897,25 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const void* 
   P.budget = geo.budget;
   P.sink = geo.sink_size;
   P.scale_log2 = geo.scale * kLog2e;
-  const size_t lds = decode_lds_bytes_for(geo, WAVES);
-  P.chunk = static_cast<int32_t>(lds / (sizeof(float) * G));
-  if (EVICT) P.chunk = geo.slots_pad;
+  const int pairs = geo.batch * geo.num_kv_heads;
+  P.pairs = pairs;
+  P.splits = SPLIT ? splits : 1;
+  P.ws_part = W.part;
+  P.ws_logit = W.logit;
+  P.arrive = W.arrive;
+  const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits) : decode_lds_bytes(geo);
+  if (lds == 0) return hipErrorInvalidValue;
+  P.chunk = static_cast<int32_t>(lds / (sizeof(float) * G));  // EVICT: a whole split (or pair)
+  auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT>;
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  const int pairs = geo.batch * geo.num_kv_heads;
-  hipLaunchKernelGGL((decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY>), dim3(pairs), dim3(WAVES * kWave), lds,
-                     stream, P);
+  const dim3 grid(SPLIT ? pairs * splits : pairs);
+  const dim3 block(WAVES * kWave);
+  hipLaunchKernelGGL(kern, grid, block, lds, stream, P);
   return hipGetLastError();
 }
 
@@ -755,13 +967,32 @@ size_t decode_lds_bytes_for(const Geometry& g, int waves) {
 
 size_t decode_lds_bytes(const Geometry& g) { return decode_lds_bytes_for(g, kDecodeWaves); }
 
-hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const void* q,
-                         const void* k_new, const void* v_new, void* out, int32_t* evicted,
-                         hipStream_t stream) {
-#define LF_CASE(T, D, G)                                                                    \
-  if (g.head_dim == D && g.group == G) {                                                   \
-    return g.mode == 0 ? launch_decode_t<T, D, G, true>(g, L, q, k_new, v_new, out, evicted, stream) \
-                       : launch_decode_t<T, D, G, false>(g, L, q, k_new, v_new, out, evicted, stream); \
+size_t decode_split_lds_bytes(const Geometry& g, int splits) {
+  if (decode_lds_bytes(g) == 0 || splits < 1) return 0;
+  if (g.mode != 0) return decode_lds_bytes(g);  // FULL: chunked, as without splits
+  const int tiles = g.slots_pad / 16;
+  const int per = (tiles + splits - 1) / splits;
+  return static_cast<size_t>(per) * 16 * g.group * sizeof(float);  // one split's logits
+}
+
+size_t split_part_floats(const Geometry& g) {
+  return 2 * static_cast<size_t>(g.group) + static_cast<size_t>(g.group) * g.head_dim;
+}
+
+hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
+                         const void* q, const void* k_new, const void* v_new, void* out,
+                         int32_t* evicted, hipStream_t stream) {
+#define LF_CASE(T, D, G)                                                                          \
+  if (g.head_dim == D && g.group == G) {                                                         \
+    if (splits > 1)                                                                              \
+      return g.mode == 0 ? launch_decode_t<T, D, G, true, true>(g, L, W, splits, q,   \
+                                                                  k_new, v_new, out, evicted, stream) \
+                         : launch_decode_t<T, D, G, false, true>(g, L, W, splits, q,  \
+                                                                   k_new, v_new, out, evicted, stream); \
+    return g.mode == 0 ? launch_decode_t<T, D, G, true, false>(g, L, W, 1, q, k_new, v_new, \
+                                                                 out, evicted, stream)             \
+                       : launch_decode_t<T, D, G, false, false>(g, L, W, 1, q, k_new, v_new, \
+                                                                  out, evicted, stream);           \
   }
   if (g.dtype == 1) {
     LF_CASE(uint16_t, 128, 1)

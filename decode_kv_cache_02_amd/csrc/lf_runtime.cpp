@@ -7,9 +7,11 @@
 //   V      [slots_pad][head_dim]  cache dtype
 //   ||v||_1 [slots_pad]           float32 sidecar
 //   fill                          int32 tokens held
+//   split-K workspace  partial softmax states and arrival counters
 // and nothing is allocated afterwards. Validation happens on the host before
 // anything is queued; fill levels are mirrored on the host (every decode step
-// adds exactly one token per pair) so no call has to read the device.
+// adds exactly one token per pair) so no call has to read the device, and the
+// split count of each launch is planned from them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -34,6 +36,9 @@ struct lf_cache {
   int64_t layer_pairs;   // batch * num_kv_heads
   size_t elem_bytes;
   std::vector<int32_t> fill_host;  // [num_layers][batch]
+  lf::SplitWork work;              // split-K workspace (shared by the layers)
+  int32_t max_splits;              // 1: no split launches
+  int32_t forced_splits;           // 0: plan automatically
 };
 
 namespace {
@@ -42,7 +47,7 @@ constexpr size_t kAlign = 256;
 constexpr int kSlotAlign = 64;
 
 struct Layout {
-  size_t k_off, v_off, vn_off, fill_off, total;
+  size_t k_off, v_off, vn_off, fill_off, part_off, logit_off, arrive_off, total;
   int32_t slots_pad;
   int64_t pair_elems;
 };
@@ -86,7 +91,7 @@ lf::Geometry geometry(const lf_config* c) {
   return g;
 }
 
-lf_status layout(const lf_config* c, Layout* L) {
+lf_status layout(const lf_config* c, int32_t max_splits, Layout* L) {
   const lf::Geometry g = geometry(c);
   const size_t elem = c->dtype == LF_DTYPE_F32 ? 4 : 2;
   size_t pairs, kv, vn, fl, t;
@@ -108,8 +113,31 @@ lf_status layout(const lf_config* c, Layout* L) {
   if (!add_ok(L->vn_off, align_up(vn), &t)) return LF_ERR_UNSUPPORTED;
   L->fill_off = t;
   if (!add_ok(L->fill_off, align_up(fl), &t)) return LF_ERR_UNSUPPORTED;
+  // Split-K workspace for one layer (the layers run one after another).
+  size_t layer_pairs = static_cast<size_t>(c->batch) * c->num_kv_heads;
+  size_t ws = max_splits > 1 ? layer_pairs * max_splits : 0;
+  const size_t logits = max_splits > 1 && c->mode == LF_MODE_EVICT
+      ? layer_pairs * static_cast<size_t>(g.slots_pad) * g.group * 4 : 0;
+  L->part_off = t;
+  if (!add_ok(L->part_off, align_up(ws * lf::split_part_floats(g) * 4), &t)) return LF_ERR_UNSUPPORTED;
+  L->logit_off = t;
+  if (!add_ok(L->logit_off, align_up(logits), &t)) return LF_ERR_UNSUPPORTED;
+  L->arrive_off = t;
+  if (!add_ok(L->arrive_off, align_up(max_splits > 1 ? layer_pairs * 4 : 0), &t)) return LF_ERR_UNSUPPORTED;
   L->total = t;
   return LF_OK;
+}
+
+// Largest split count a cache can use (sizes its workspace): none once the
+// layer has kSplitPairsBelow pairs (one workgroup per pair already fills the
+// GPU), else a layer grid of about kSplitGridTarget workgroups, capped.
+// Decided from the configuration alone, so that lf_cache_bytes needs no
+// device.
+int32_t max_splits_for(const lf_config* c) {
+  const int64_t pairs = static_cast<int64_t>(c->batch) * c->num_kv_heads;
+  if (pairs <= 0 || pairs >= lf::kSplitPairsBelow) return 1;
+  const int64_t s = lf::kSplitGridTarget / pairs;
+  return static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(s, lf::kMaxSplits)));
 }
 
 lf::LayerPtrs layer_ptrs(const lf_cache* c, int32_t layer) {
@@ -130,6 +158,16 @@ lf_status use_device(const lf_cache* c) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Split count of one launch: up to max_splits workgroups per pair, with at
+// least kMinSplitSlots slots per split of the fullest pair; a forced count
+// (lf_cache_set_splits) wins within max_splits.
+int32_t plan_splits(const lf_cache* c, int32_t n_max) {
+  if (c->max_splits <= 1) return 1;
+  if (c->forced_splits > 0) return std::min(c->forced_splits, c->max_splits);
+  const int32_t by_work = std::max(1, n_max / lf::kMinSplitSlots);
+  return std::max(1, std::min(c->max_splits, by_work));
+}
 
 }  // namespace
 
@@ -152,7 +190,9 @@ lf_status lf_cache_bytes(const lf_config* cfg, size_t* bytes) {
   lf_status s = validate(cfg);
   if (s != LF_OK) return s;
   Layout L;
-  s = layout(cfg, &L);
+  // The split workspace is sized for the most splits that could be planned
+  // (an upper bound that needs no device query).
+  s = layout(cfg, max_splits_for(cfg), &L);
   if (s != LF_OK) return s;
   *bytes = L.total;
   return LF_OK;
@@ -163,9 +203,6 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   *out = nullptr;
   lf_status s = validate(cfg);
   if (s != LF_OK) return s;
-  Layout L;
-  s = layout(cfg, &L);
-  if (s != LF_OK) return s;
   const lf::Geometry geo = geometry(cfg);
   const size_t lds = lf::decode_lds_bytes(geo);
   if (lds == 0) return LF_ERR_UNSUPPORTED;
@@ -175,6 +212,10 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
     return LF_ERR_HIP;
   }
   if (lds > lf::device_lds_limit()) return LF_ERR_UNSUPPORTED;
+  const int32_t max_splits = max_splits_for(cfg);
+  Layout L;
+  s = layout(cfg, max_splits, &L);
+  if (s != LF_OK) return s;
 
   lf_cache* c = new (std::nothrow) lf_cache();
   if (!c) return LF_ERR_OOM;
@@ -209,6 +250,11 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->v = static_cast<char*>(base) + L.v_off;
   c->vnorm1 = reinterpret_cast<float*>(static_cast<char*>(base) + L.vn_off);
   c->fill = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.fill_off);
+  c->work.part = reinterpret_cast<float*>(static_cast<char*>(base) + L.part_off);
+  c->work.logit = reinterpret_cast<float*>(static_cast<char*>(base) + L.logit_off);
+  c->work.arrive = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.arrive_off);
+  c->max_splits = max_splits;
+  c->forced_splits = 0;
   *out = c;
   return LF_OK;
 }
@@ -257,6 +303,18 @@ lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, 
   return LF_OK;
 }
 
+lf_status lf_cache_set_splits(lf_cache* c, int32_t splits) {
+  if (!c || splits < 0) return LF_ERR_INVALID_ARG;
+  c->forced_splits = splits;
+  return LF_OK;
+}
+
+lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits) {
+  if (!c || !max_splits) return LF_ERR_INVALID_ARG;
+  *max_splits = c->max_splits;
+  return LF_OK;
+}
+
 lf_status lf_fill_levels(const lf_cache* c, int32_t layer, int32_t* fill_host) {
   if (!c || !fill_host || layer < 0 || layer >= c->cfg.num_layers) return LF_ERR_INVALID_ARG;
   std::memcpy(fill_host, c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch,
@@ -302,9 +360,14 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
   lf_status s = use_device(c);
   if (s != LF_OK) return s;
   const lf::LayerPtrs p = layer_ptrs(c, layer);
-  if (lf::launch_decode(c->geo, p, q, k_new, v_new, out, evicted_slot,
-                        static_cast<hipStream_t>(stream)) != hipSuccess)
+  int32_t n_max = 0;
+  for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
+  const int32_t splits = plan_splits(c, n_max);
+  if (lf::launch_decode(c->geo, p, c->work, splits, q, k_new, v_new, out, evicted_slot,
+                        static_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
     return LF_ERR_HIP;
+  }
   for (int32_t b = 0; b < c->cfg.batch; ++b)
     if (fh[b] < c->cfg.budget) ++fh[b];
   return LF_OK;

@@ -73,6 +73,8 @@ SIGNATURES = [
     ("lf_cache_snapshot", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p]),
+    ("lf_cache_set_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    ("lf_cache_max_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_fill_levels", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_cache_destroy", None, [ctypes.c_void_p]),
     ("lf_status_str", ctypes.c_char_p, [ctypes.c_int]),
@@ -190,6 +192,18 @@ def lf_cache_snapshot(handle: int, layer: int, k=None, v=None, vnorm1=None, fill
            "lf_cache_snapshot")
 
 
+def lf_cache_set_splits(handle: int, splits: int) -> None:
+    _check(load_library().lf_cache_set_splits(ctypes.c_void_p(handle), int(splits)),
+           "lf_cache_set_splits")
+
+
+def lf_cache_max_splits(handle: int) -> int:
+    v = ctypes.c_int32(0)
+    _check(load_library().lf_cache_max_splits(ctypes.c_void_p(handle), ctypes.byref(v)),
+           "lf_cache_max_splits")
+    return int(v.value)
+
+
 def lf_fill_levels(handle: int, layer: int, batch: int) -> np.ndarray:
     out = np.zeros(batch, dtype=np.int32)
     _check(load_library().lf_fill_levels(ctypes.c_void_p(handle), int(layer),
@@ -264,6 +278,13 @@ class LongFlowCache:
         self._check_tensor(out, (self.batch, self.hq, self.head_dim), "out")
         self._check_tensor(evicted_slot, (self.batch, self.hkv), "evicted_slot", torch.int32)
         lf_decode_step(self.handle, layer, q, k_new, v_new, out, evicted_slot, stream)
+
+    def set_splits(self, splits: int) -> None:
+        lf_cache_set_splits(self.handle, splits)
+
+    @property
+    def max_splits(self) -> int:
+        return lf_cache_max_splits(self.handle)
 
     def view(self, layer) -> lf_view:
         return lf_cache_view(self.handle, layer)

@@ -148,6 +148,15 @@ lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view);
 lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm1,
                             int32_t* fill, void* stream);
 
+/* Split-K tuning. By default each launch picks how many workgroups share a
+ * pair: 1 when the layer has 256 pairs or more (one workgroup per pair
+ * fills the GPU); otherwise up to 512 / pairs and 16, with at least 256
+ * slots per split. A positive `splits` forces that count (clamped to
+ * lf_cache_max_splits); 0 restores the automatic choice. Results do not
+ * depend on the split count except for float32 rounding of the output. */
+lf_status lf_cache_set_splits(lf_cache* c, int32_t splits);
+lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits);
+
 /* Host-side copy of the fill levels of one layer, [batch] int32 into the
  * caller's HOST array. Tracked on the host from the calls made (no device
  * access, no synchronisation). */

@@ -46,13 +46,15 @@ class LockstepReport:
     tie_lowest_index: int = 0
     exact_ties: int = 0
     max_rel_err: float = 0.0
+    max_splits: int = 1
     notes: list = field(default_factory=list)
 
 
 def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
                  prefill_n=None, mode: str = "evict", capacity: Optional[int] = None,
                  sink_size: int = 0, seed_offset: int = 0, layer: int = 0,
-                 num_layers: int = 1, check_cache_every: int = 0) -> LockstepReport:
+                 num_layers: int = 1, check_cache_every: int = 0,
+                 splits: int = 0) -> LockstepReport:
     """Run `steps` decode steps of one layer on the GPU and in the oracle."""
     import torch
     from decode_kv_cache_02_amd.native import LongFlowCache
@@ -60,6 +62,8 @@ def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
     budget = wl.budget if capacity is None else capacity
     cache = LongFlowCache(num_layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                           budget, sink_size=sink_size, dtype=wl.dtype, mode=mode)
+    if splits:
+        cache.set_splits(splits)
     try:
         ts = TokenStream(wl, layer=layer, seed_offset=seed_offset)
         if prefill_n is None:
@@ -118,6 +122,7 @@ def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
                 compare_cache(cache, oracle, layer, wl)
         if check_cache_every:
             compare_cache(cache, oracle, layer, wl)
+        rep.max_splits = cache.max_splits
         return rep
     finally:
         cache.close()

@@ -1,0 +1,90 @@
+"""GPU parity of split-K launches (several workgroups per pair) against the oracle.
+
+Same lockstep protocol and tolerances as test_gpu_parity. Split counts are
+forced through lf_cache_set_splits, including counts that leave some splits
+without any slot, and left to the planner for the TP=8 shard shape.
+"""
+import numpy as np
+import pytest
+
+from decode_kv_cache_02_amd.synth import WORKLOADS
+from lockstep import run_lockstep
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_kv_cache_02_amd import native
+    native.load_library()
+    yield
+
+
+@pytest.mark.parametrize("splits", [2, 4, 8])
+def test_tiny_f32_split(splits):
+    """B = 64 is 4 tiles: 8 splits leave four of them empty."""
+    wl = WORKLOADS["tiny_f32"]
+    _say(f"tiny_f32 256 steps, {splits} splits")
+    rep = run_lockstep(wl, wl.steps, splits=splits, check_cache_every=64)
+    assert rep.evictions == 256
+
+
+@pytest.mark.parametrize("dtype,G,d,budget,prefill,steps,splits", [
+    ("bf16", 4, 128, 100, 90, 30, 3),    # fill -> evict; splits of 48, 48, 4 slots
+    ("bf16", 2, 64, 300, 300, 20, 5),
+    ("f32", 4, 64, 200, 150, 60, 2),
+    ("bf16", 1, 128, 520, 500, 30, 16),
+])
+def test_small_shapes_split(dtype, G, d, budget, prefill, steps, splits):
+    wl = WORKLOADS["tiny_f32"].with_(dtype=dtype, batch=3, num_kv_heads=2, num_q_heads=2 * G,
+                                     head_dim=d, budget=budget, prefill=prefill, steps=steps)
+    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps} splits={splits}")
+    rep = run_lockstep(wl, steps, splits=splits, check_cache_every=10)
+    assert rep.steps == steps
+
+
+def test_split_sinks():
+    wl = WORKLOADS["tiny_f32"].with_(budget=300, prefill=300)
+    _say("tiny_f32 B=300 sink 4, 3 splits")
+    rep = run_lockstep(wl, 64, sink_size=4, splits=3, check_cache_every=32)
+    assert rep.evictions == 64
+
+
+def test_full_mode_split():
+    wl = WORKLOADS["llama8b_layer"].with_(batch=2, prefill=2040)
+    _say("bf16 FULL mode, capacity 2200, prefill 2040, 4 splits")
+    rep = run_lockstep(wl, 20, mode="full", capacity=2200, pairs=[(0, 0), (1, 7), (0, 3)],
+                       splits=4, check_cache_every=10)
+    assert rep.appends == 60
+
+
+@pytest.mark.parametrize("budget,splits", [(1024, 4), (4096, 8)])
+def test_duplicate_ties_across_splits(budget, splits):
+    """Exact score collisions between slots of different splits still go to
+    the lowest slot."""
+    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(batch=8, budget=budget, prefill=budget)
+    pairs = [(b, h) for b in range(0, 8, 2) for h in (1, 6)]
+    _say(f"qwen3_8b ties, B {budget}, batch 8, {splits} splits, 40 steps")
+    rep = run_lockstep(wl, 40, pairs=pairs, splits=splits, check_cache_every=40)
+    print(f"near-ties {rep.near_ties}, exact ties {rep.exact_ties}, "
+          f"lowest index taken {rep.tie_lowest_index}")
+    assert rep.tie_lowest_index == rep.exact_ties
+
+
+def test_tp8_shard_planned_splits():
+    """One GPU's share of the Llama-8B layer under TP = 8: 64 pairs, planned split."""
+    wl = WORKLOADS["llama8b_layer"].with_(num_q_heads=4, num_kv_heads=1)
+    pairs = [(0, 0), (17, 0), (40, 0), (63, 0)]
+    n = np.full(wl.batch, 3270, dtype=np.int32)
+    _say("llama8b tp8 shard (64x4/1x128, B 3277), prefill 3270, 12 steps, planned splits")
+    rep = run_lockstep(wl, 12, pairs=pairs, prefill_n=n, check_cache_every=12)
+    print(f"max splits {rep.max_splits}")
+    assert rep.max_splits == 8
+    assert rep.appends == 7 * len(pairs) and rep.evictions == 5 * len(pairs)
