@@ -140,4 +140,4 @@ def compare_cache(cache, oracle: LayerCache, layer: int, wl: Workload) -> None:
         assert fill[b, h] == n, f"pair {(b, h)}: fill {fill[b, h]} != {n}"
         assert np.array_equal(k[b, h, :n], c.K[:n]), f"pair {(b, h)}: K rows differ"
         assert np.array_equal(v[b, h, :n], c.V[:n]), f"pair {(b, h)}: V rows differ"
-        np.testing.assert_allclose(vn[b, h, :n], c.vnorm1[:n], rtol=2e-6, atol=0)
+        np.testing.assert_allclose(vn[b, h, :n], c.vnorm[:n], rtol=2e-6, atol=0)

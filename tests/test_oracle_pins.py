@@ -43,7 +43,7 @@ def check_stepwise_fixture(fx, mod=lo):
         np.testing.assert_allclose(r.out, _f(st["expected_out"]), rtol=0, atol=1e-13)
         np.testing.assert_allclose(r.scores, _f(st["expected_scores"]), rtol=1e-13, atol=0)
         assert r.evicted == st["expected_evicted"]
-    np.testing.assert_allclose(c.vnorm1, _f(fx["expected_final_vnorm1"]), rtol=0, atol=0)
+    np.testing.assert_allclose(c.vnorm, _f(fx["expected_final_vnorm1"]), rtol=0, atol=0)
 
 
 def test_golden_mha_two_steps():
@@ -79,7 +79,8 @@ def test_golden_fill_no_evict():
 
 def test_golden_fixture_set_is_complete():
     names = sorted(os.path.basename(p) for p in glob.glob(os.path.join(GOLDEN, "*.json")))
-    assert names == ["hand_fill_no_evict.json", "hand_gqa_normalised.json",
+    assert names == ["hand_deferred_order.json", "hand_fill_no_evict.json",
+                     "hand_gqa_normalised.json", "hand_l2_vs_l1.json",
                      "hand_mha_two_steps.json", "hand_tie_and_sinks.json"]
 
 
@@ -350,7 +351,7 @@ def test_p11_overwrite_in_place():
     r = c.step(q, kn, vn)
     e = r.evicted
     assert np.array_equal(c.K[e], kn) and np.array_equal(c.V[e], vn)
-    assert c.vnorm1[e] == np.abs(vn).sum()
+    assert c.vnorm[e] == np.abs(vn).sum()
     others = [i for i in range(64) if i != e]
     assert np.array_equal(c.K[others], K[others]) and np.array_equal(c.V[others], V[others])
     assert c.n == 64
