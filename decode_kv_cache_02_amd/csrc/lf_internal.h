@@ -20,6 +20,9 @@ struct Geometry {
   int32_t slots_pad;    // budget rounded up to 64
   int32_t dtype;        // lf_dtype
   int32_t mode;         // lf_mode
+  int32_t order;        // lf_order
+  int32_t scope;        // lf_scope
+  int32_t norm;         // lf_norm
   int64_t pair_elems;   // slots_pad * head_dim
   float scale;          // tau
 };
@@ -28,8 +31,9 @@ struct Geometry {
 struct LayerPtrs {
   void* k;
   void* v;
-  float* vnorm1;
+  float* vnorm;
   int32_t* fill;
+  int32_t* victim;    // deferred order: next victim per pair, -1 = none
 };
 
 // Split-K workspace of one layer launch: per (pair, split) the partial
@@ -39,6 +43,10 @@ struct SplitWork {
   float* part;        // [pairs][max_splits][split_part_floats]
   float* logit;       // [pairs][slots_pad][group]
   int32_t* arrive;    // [pairs]
+  // One victim per sequence: every pair's score vector and, per sequence, an
+  // arrival counter of its KV heads (zero between launches).
+  float* score;       // [pairs][slots_pad]
+  int32_t* seq_arrive;  // [batch]
 };
 
 constexpr int kMaxSplits = 16;
@@ -68,6 +76,11 @@ hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork&
 hipError_t launch_fill(const Geometry& g, const LayerPtrs& L, const void* k,
                        const void* v, const int32_t* n_host, int32_t seq0,
                        int32_t count, int32_t n_max, hipStream_t stream);
+
+// Drops every layer's pairs of the `count` sequences in seqs_host to 0 tokens
+// with no pending victim.
+hipError_t launch_seq_reset(const Geometry& g, int32_t num_layers, int32_t* fill, int32_t* victim,
+                            const int32_t* seqs_host, int32_t count, hipStream_t stream);
 
 constexpr int kFillSeqPerLaunch = 256;
 

@@ -222,15 +222,20 @@ __device__ __forceinline__ void wave_argmin(float& score, int& slot) {
   slot = static_cast<int>(bl);
 }
 
-// ||row||_1 in float32 in one fixed order, evaluated by a whole wave; the
-// result is lane 0's. The fill and the decode kernels both use this routine,
-// so equal stored rows always get bit-equal sidecar values.
+// ||row||_1 (or ||row||_2 when l2) in float32 in one fixed order, evaluated
+// by a whole wave; the result is lane 0's. The fill and the decode kernels
+// both use this routine, so equal stored rows always get bit-equal sidecar
+// values.
 template <typename T, int D>
-__device__ __forceinline__ float wave_l1(const T* row, int lane) {
+__device__ __forceinline__ float wave_norm(const T* row, int lane, bool l2) {
   float x = 0.0f;
 #pragma unroll
-  for (int k = 0; k < D / kWave; ++k) x += fabsf(to_f32(row[lane + k * kWave]));
-  return wave_sum(x);
+  for (int k = 0; k < D / kWave; ++k) {
+    const float v = to_f32(row[lane + k * kWave]);
+    x = l2 ? fmaf(v, v, x) : x + fabsf(v);
+  }
+  const float s = wave_sum(x);
+  return l2 ? sqrtf(s) : s;
 }
 
 struct DecodeParams {
@@ -243,8 +248,9 @@ struct DecodeParams {
   const void* vc;
   void* kc_w;
   void* vc_w;
-  float* vnorm1;
+  float* vnorm;         // ||v||_1 (or ||v||_2) sidecar
   int32_t* fill;
+  int32_t* victim;      // deferred order: next victim per pair, -1 = none
   int64_t pair_elems;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -252,12 +258,18 @@ struct DecodeParams {
   int32_t sink;
   int32_t chunk;        // slots per LDS-resident chunk (EVICT: a whole split)
   float scale_log2;     // tau * log2(e)
+  int32_t deferred;     // 1: write into the previous victim, then choose the next
+  int32_t shared;       // 1: one victim per sequence (scores summed over KV heads)
+  int32_t norm_l2;      // 1: the sidecar holds ||v||_2
   // Split-K across workgroups (SPLIT kernels only).
   int32_t pairs;        // pairs of the layer
   int32_t splits;       // workgroups per pair
   float* ws_part;       // [pairs][splits][2G + G*D]: m, l, unnormalised output
   float* ws_logit;      // [pairs][slots_pad][G]: raw logits (cache full only)
   int32_t* arrive;      // [pairs]: arrivals, back to 0 after every launch
+  // One victim per sequence.
+  float* ws_score;      // [pairs][slots_pad]: each pair's score vector
+  int32_t* seq_arrive;  // [batch]: KV heads done, back to 0 after every launch
 };
 
 // Cross-workgroup data of a split launch goes through relaxed agent-scope
@@ -319,8 +331,11 @@ __device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off
  *                  arrive combines the partials, scores every slot against
  *                  the global max and sum, takes the argmin and writes the
  *                  output and the new token. No workgroup ever waits.
+ *   VAR = true: the deferred order and one victim per sequence are available
+ *               (runtime flags); false compiles them out of the main path.
  */
-template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT>
+template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT,
+          bool VAR>
 __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(DecodeParams P) {
   constexpr int kBytes = Elem<T>::kBytes;
   constexpr int NT = WAVES * kWave;
@@ -412,14 +427,31 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   for (int c = 0; c < kChunks; ++c)
     qa[c] = load16(qg + (r16 % G) * D + (64 * c + 16 * grp) / kBytes);
 
+  // What this step does with the new token.
+  //   same-step order: below the budget it is appended at slot n; at the
+  //     budget the cached slots are scored and the argmin is overwritten.
+  //   deferred order: below the budget it is appended; at the budget it
+  //     replaces `masked`, the previous step's victim (budget-1 if none),
+  //     whose old token then takes no part in the step. The cached slots are
+  //     scored whenever the buffer is full after the write, and the argmin
+  //     becomes the next victim.
+  const bool deferred = VAR && P.deferred;
+  const bool shared = VAR && P.shared;
+  const bool overwrite = EVICT && n >= P.budget;
+  int masked = -1;
+  if (EVICT && deferred && overwrite) {
+    const int v = P.victim[pair];
+    masked = (v >= 0 && v < P.budget) ? v : P.budget - 1;
+  }
+  const bool scoring = EVICT && (deferred ? n + 1 >= P.budget : overwrite);
+
   // Sidecar of the slots this thread scores (the first kScoreBatch of them),
   // requested now so the score phase finds it in registers.
-  const bool evicting = EVICT && n >= P.budget;
   const int sc_lo = max(lo, P.sink);
   const __amdgpu_buffer_rsrc_t rN =
-      make_rsrc(P.vnorm1 + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(hi) * 4u);
+      make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(hi) * 4u);
   float vnb[kScoreBatch];
-  if (!SPLIT && evicting) {
+  if (!SPLIT && scoring) {
 #pragma unroll
     for (int k = 0; k < kScoreBatch; ++k)
       vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
@@ -440,8 +472,8 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       x = wave_sum(x);
       if (lane == 0) sh_snew[g] = x * P.scale_log2;
     }
-    const float l1 = wave_l1<T, D>(vn, lane);
-    if (lane == 0) sh_vn_new = l1;
+    const float nrm = wave_norm<T, D>(vn, lane, P.norm_l2 != 0);
+    if (lane == 0) sh_vn_new = nrm;
   }
 
   // Running softmax state, identical in every thread. One workgroup per
@@ -489,9 +521,10 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
           for (int c = 0; c < kChunks; ++c) s4 = mfma_chunk(qa[c], kt[u][c], s4, T());
           const int i = (t0 + u) * 16 + r16;
           float s[G];
+          const bool live = i < cn && (!VAR || c0 + i != masked);
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            s[g] = (i < cn) ? s4[g] * P.scale_log2 : -INFINITY;
+            s[g] = live ? s4[g] * P.scale_log2 : -INFINITY;
             wmax[g] = fmaxf(wmax[g], s[g]);
           }
           if (grp == 0) lds_put<G>(lds, i, s);
@@ -553,12 +586,12 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
     // Split with a full cache: this pair's raw-logit area (no records otherwise).
     const __amdgpu_buffer_rsrc_t rW =
-        make_rsrc(SPLIT && evicting ? P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G : nullptr,
-                  SPLIT && evicting ? static_cast<uint32_t>(slots_pad) * G * 4u : 0u);
+        make_rsrc(SPLIT && scoring ? P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G : nullptr,
+                  SPLIT && scoring ? static_cast<uint32_t>(slots_pad) * G * 4u : 0u);
     for (int i = tid; i < ntiles * 16; i += NT) {  // masked slots hold -inf -> p = 0
       float x[G];
       lds_get<G>(lds, i, x);
-      if (SPLIT && evicting && i < cn)  // raw logits for the last split's score
+      if (SPLIT && scoring && i < cn)  // raw logits for the last split's score
         ws_store_g<G>(rW, static_cast<uint32_t>(c0 + i) * G * 4u, x);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -582,11 +615,15 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       w_run[g] *= fac[g];
     }
 
-    // ---------------- Phase C: score + argmin (cache full) ----------------
+    // ---------------- Phase C: score + argmin ----------------
     // One workgroup per pair: runs while the first V rows are in flight.
-    // Only a full cache evicts, and then the whole buffer is one chunk, so M
-    // and L are final here.
-    if (!SPLIT && EVICT && evicting) {
+    // Only an evicting cache scores, and then the whole buffer is one chunk,
+    // so M and L are final here. With one victim per sequence the scores are
+    // also published for the sequence's last KV head to sum.
+    if (!SPLIT && EVICT && scoring) {
+      const __amdgpu_buffer_rsrc_t rSc =
+          make_rsrc(shared ? P.ws_score + static_cast<int64_t>(pair) * slots_pad : nullptr,
+                    shared ? static_cast<uint32_t>(n) * 4u : 0u);
       float inv_l[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
@@ -600,13 +637,17 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
 #pragma unroll
         for (int k = 0; k < kScoreBatch; ++k) {
           const int i = i0 + k * NT;
-          if (i < n) {
+          if (i < n && (!VAR || i != masked)) {
             float p[G];
             lds_get<G>(lds, i, p);
             float sc = p[0] * inv_l[0];
 #pragma unroll
             for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
             sc = sc * vnb[k];
+            if (shared) {
+              const float one[1] = {sc};
+              ws_store_g<1>(rSc, static_cast<uint32_t>(i) * 4u, one);
+            }
             if (sc < best) {  // slots visited in increasing order: first minimum kept
               best = sc;
               best_i = i;
@@ -669,7 +710,6 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   __syncthreads();
   T* out = static_cast<T*>(P.out) + (static_cast<int64_t>(b) * P.num_q_heads + h * G) * D;
 
-  int slot = n;
   if constexpr (!SPLIT) {
     for (int idx = tid; idx < G * D; idx += NT) {
       const int g = idx / D;
@@ -679,18 +719,6 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
       o = fmaf(w_run[g], to_f32(vn[d]), o);
       from_f32(o / l_run[g], out + g * D + d);
-    }
-    if (tid >= 2 * kRowLoads) return;
-    if (evicting) {  // cross-wave argmin, lowest slot on ties
-      float bs = sh_best_score[0];
-      slot = sh_best_slot[0];
-#pragma unroll
-      for (int w = 1; w < WAVES; ++w) {
-        if (sh_best_score[w] < bs || (sh_best_score[w] == bs && sh_best_slot[w] < slot)) {
-          bs = sh_best_score[w];
-          slot = sh_best_slot[w];
-        }
-      }
     }
   } else {
     // ---------------- Split: publish this split's partial state ----------------
@@ -717,7 +745,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     __syncthreads();
     if (sh_ticket != S - 1) return;  // not the last split of the pair
 
-    // ---------------- Last split: combine, score, choose ----------------
+    // ---------------- Last split: combine, score ----------------
     const float* part = P.ws_part + static_cast<int64_t>(pair) * S * kPart;
     if (tid < G) {  // global max and sum, new token included, fixed order
       const int g = tid;
@@ -742,7 +770,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       o = fmaf(__builtin_amdgcn_exp2f(sh_snew[g] - M), to_f32(vn[d]), o);
       from_f32(o / sh_gl[g], out + g * D + d);
     }
-    if (evicting) {
+    if (scoring) {
       // Score every slot from the published raw logits: the same operations
       // as one workgroup per pair, so equal tokens get bit-equal scores.
       float inv_l[G], gm[G];
@@ -751,10 +779,13 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
         inv_l[g] = 1.0f / sh_gl[g];
         gm[g] = sh_gm[g];
       }
+      const __amdgpu_buffer_rsrc_t rSc =
+          make_rsrc(shared ? P.ws_score + static_cast<int64_t>(pair) * slots_pad : nullptr,
+                    shared ? static_cast<uint32_t>(n) * 4u : 0u);
       const __amdgpu_buffer_rsrc_t rL = make_rsrc(
           P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(n) * G * 4u);
       const __amdgpu_buffer_rsrc_t rNa =
-          make_rsrc(P.vnorm1 + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
+          make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
       constexpr int kLastBatch = 8;  // slots per thread with loads in flight together
       for (int i0 = P.sink + tid; i0 < n; i0 += NT * kLastBatch) {
         float vb[kLastBatch];
@@ -768,7 +799,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
 #pragma unroll
         for (int k = 0; k < kLastBatch; ++k) {
           const int i = i0 + k * NT;
-          if (i < n) {
+          if (i < n && (!VAR || i != masked)) {
             float p[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) p[g] = __builtin_amdgcn_exp2f(lg[k][g] - gm[g]);
@@ -776,6 +807,10 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
 #pragma unroll
             for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
             sc = sc * vb[k];
+            if (shared) {
+              const float one[1] = {sc};
+              ws_store_g<1>(rSc, static_cast<uint32_t>(i) * 4u, one);
+            }
             if (sc < best) {
               best = sc;
               best_i = i;
@@ -788,21 +823,136 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
         sh_best_score[wave] = best;
         sh_best_slot[wave] = best_i;
       }
-      __syncthreads();
-      if (tid < 2 * kRowLoads) {  // cross-wave argmin, lowest slot on ties
-        uint32_t bh = __float_as_uint(sh_best_score[0]);
-        uint32_t bl = static_cast<uint32_t>(sh_best_slot[0]);
-        for (int w = 1; w < WAVES; ++w)
-          key_min(bh, bl, __float_as_uint(sh_best_score[w]), static_cast<uint32_t>(sh_best_slot[w]));
-        slot = static_cast<int>(bl);
-      }
     }
     if (tid == 0) __hip_atomic_store(P.arrive + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid >= 2 * kRowLoads) return;
+  }
+
+  // ---------------- Choice of the victim ----------------
+  // One victim per pair: the cross-wave argmin of this workgroup, lowest slot
+  // on ties. One victim per sequence: every KV head has published its score
+  // vector; the last of them to finish sums them in head order and takes the
+  // argmin. choice = -1 when there is no candidate.
+  int choice = -1;
+  bool decider = !shared;
+  if (scoring) {
+    if (!shared) {
+      __syncthreads();  // every wave's best visible
+      uint32_t bh = __float_as_uint(sh_best_score[0]);
+      uint32_t bl = static_cast<uint32_t>(sh_best_slot[0]);
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w)
+        key_min(bh, bl, __float_as_uint(sh_best_score[w]), static_cast<uint32_t>(sh_best_slot[w]));
+      choice = static_cast<int>(bl);
+    } else {
+      drain_stores();
+      __syncthreads();
+      if (tid == 0)
+        sh_ticket = __hip_atomic_fetch_add(P.seq_arrive + b, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      decider = sh_ticket == P.num_kv_heads - 1;
+      if (decider) {
+        const int hk = P.num_kv_heads;
+        const __amdgpu_buffer_rsrc_t rS = make_rsrc(
+            P.ws_score + static_cast<int64_t>(b) * hk * slots_pad,
+            static_cast<uint32_t>(hk) * static_cast<uint32_t>(slots_pad) * 4u);
+        constexpr int kSeqBatch = 8;
+        float sbest = INFINITY;
+        int sbest_i = 0x7fffffff;
+        for (int i0 = P.sink + tid; i0 < n; i0 += NT * kSeqBatch) {
+          float tot[kSeqBatch];
+          for (int hh = 0; hh < hk; ++hh) {
+            float x[kSeqBatch][1];
+#pragma unroll
+            for (int k = 0; k < kSeqBatch; ++k)
+              ws_load_g<1>(rS, (static_cast<uint32_t>(hh) * slots_pad + i0 + k * NT) * 4u, x[k]);
+#pragma unroll
+            for (int k = 0; k < kSeqBatch; ++k) tot[k] = hh == 0 ? x[k][0] : tot[k] + x[k][0];
+          }
+#pragma unroll
+          for (int k = 0; k < kSeqBatch; ++k) {
+            const int i = i0 + k * NT;
+            if (i < n && i != masked && tot[k] < sbest) {
+              sbest = tot[k];
+              sbest_i = i;
+            }
+          }
+        }
+        wave_argmin(sbest, sbest_i);
+        if (lane == 0) {
+          sh_best_score[wave] = sbest;
+          sh_best_slot[wave] = sbest_i;
+        }
+        __syncthreads();
+        uint32_t bh = __float_as_uint(sh_best_score[0]);
+        uint32_t bl = static_cast<uint32_t>(sh_best_slot[0]);
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w)
+          key_min(bh, bl, __float_as_uint(sh_best_score[w]), static_cast<uint32_t>(sh_best_slot[w]));
+        choice = static_cast<int>(bl);
+        if (tid == 0)
+          __hip_atomic_store(P.seq_arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (choice < 0 || choice >= P.budget) choice = -1;
   }
 
   // ---------------- In-place write of the new token ----------------
-  if (slot >= P.budget) return;  // FULL cache already at capacity: nothing to store
+  int slot;
+  if (!deferred) {
+    if (!overwrite) {
+      slot = n;
+    } else if (!shared) {
+      slot = choice;
+    } else {
+      // One victim per sequence: its deciding workgroup stores the new token
+      // of every KV head of the sequence (each head's reads are done: it took
+      // its ticket after them).
+      if (!decider) return;
+      const int hk = P.num_kv_heads;
+      if (choice >= 0) {
+        for (int idx = tid; idx < hk * 2 * kRowLoads; idx += NT) {
+          const int hh = idx / (2 * kRowLoads);
+          const int j = idx - hh * (2 * kRowLoads);
+          const int64_t pr = static_cast<int64_t>(b) * hk + hh;
+          if (j < kRowLoads) {
+            char* Kh = reinterpret_cast<char*>(static_cast<T*>(P.kc_w) + pr * P.pair_elems);
+            store16(Kh + k_chunk_offset<kRowBytes>(choice, j),
+                    load16(static_cast<const T*>(P.k_new) + pr * D + j * EPL));
+          } else {
+            T* Vh = static_cast<T*>(P.vc_w) + pr * P.pair_elems + static_cast<int64_t>(choice) * D;
+            store16(Vh + (j - kRowLoads) * EPL,
+                    load16(static_cast<const T*>(P.v_new) + pr * D + (j - kRowLoads) * EPL));
+          }
+        }
+        for (int hh = wave; hh < hk; hh += WAVES) {
+          const int64_t pr = static_cast<int64_t>(b) * hk + hh;
+          const float nrm = wave_norm<T, D>(static_cast<const T*>(P.v_new) + pr * D, lane,
+                                            P.norm_l2 != 0);
+          if (lane == 0) P.vnorm[pr * slots_pad + choice] = nrm;
+        }
+      }
+      for (int hh = tid; hh < hk; hh += NT) P.evicted[static_cast<int64_t>(b) * hk + hh] = choice;
+      return;
+    }
+  } else {
+    slot = overwrite ? masked : n;
+    if (scoring && decider) {
+      if (!shared) {
+        if (tid == 0) P.victim[pair] = choice;
+      } else {
+        for (int hh = tid; hh < P.num_kv_heads; hh += NT)
+          P.victim[static_cast<int64_t>(b) * P.num_kv_heads + hh] = choice;
+      }
+    }
+  }
+  if (tid >= 2 * kRowLoads) return;
+  if (slot >= P.budget) return;  // FULL cache already at capacity (the host prevents it)
+  if (tid == 0) {
+    P.evicted[pair] = overwrite ? slot : -1;
+    if (!overwrite) P.fill[pair] = n + 1;
+  }
+  if (slot < 0) return;  // no candidate (only with non-finite scores): nothing stored
   char* Kw = reinterpret_cast<char*>(static_cast<T*>(P.kc_w) + pair * P.pair_elems);
   T* Vw = static_cast<T*>(P.vc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
   if (tid < kRowLoads) {
@@ -811,28 +961,27 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     const int j = tid - kRowLoads;
     store16(Vw + j * EPL, load16(vn + j * EPL));
   }
-  if (tid == 0) {
-    P.vnorm1[static_cast<int64_t>(pair) * slots_pad + slot] = sh_vn_new;
-    P.evicted[pair] = evicting ? slot : -1;
-    if (!evicting) P.fill[pair] = n + 1;
-  }
+  if (tid == 0) P.vnorm[static_cast<int64_t>(pair) * slots_pad + slot] = sh_vn_new;
 }
 
 // ---------------------------------------------------------------------------
-// Initial fill: one wave per (pair, slot); copies the row or clears it.
+// Initial fill: one wave per (pair, slot); copies the row or clears it. A
+// sequence whose length is -1 is left untouched.
 // ---------------------------------------------------------------------------
 struct FillParams {
   const void* k;
   const void* v;
   void* kc;
   void* vc;
-  float* vnorm1;
+  float* vnorm;
   int32_t* fill;
+  int32_t* victim;
   int64_t pair_elems;
   int32_t slots_pad;
   int32_t num_kv_heads;
   int32_t n_max;
   int32_t seq0;
+  int32_t norm_l2;
   int32_t n[kFillSeqPerLaunch];
 };
 
@@ -850,10 +999,10 @@ __global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
   const int b = P.seq0 + bl;
   const int64_t pair = static_cast<int64_t>(b) * P.num_kv_heads + h;
   const int nb = P.n[bl];
-  if (slot >= P.slots_pad) return;
+  if (slot >= P.slots_pad || nb < 0) return;
   char* Kd = reinterpret_cast<char*>(static_cast<T*>(P.kc) + pair * P.pair_elems);
   T* Vd = static_cast<T*>(P.vc) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
-  float l1 = 0.0f;
+  float nrm = 0.0f;
   if (slot < nb) {
     const int64_t src = ((static_cast<int64_t>(b) * P.n_max + slot) * P.num_kv_heads + h) * D;
     const T* ks = static_cast<const T*>(P.k) + src;
@@ -862,20 +1011,48 @@ __global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
       store16(Kd + k_chunk_offset<kRowBytes>(slot, lane), load16(ks + lane * EPL));
       store16(Vd + lane * EPL, load16(vs + lane * EPL));
     }
-    l1 = wave_l1<T, D>(vs, lane);
+    nrm = wave_norm<T, D>(vs, lane, P.norm_l2 != 0);
   } else if (lane < kRowChunks) {
     const u32x4_t zero = {0u, 0u, 0u, 0u};
     store16(Kd + k_chunk_offset<kRowBytes>(slot, lane), zero);
     store16(Vd + lane * EPL, zero);
   }
   if (lane == 0) {
-    P.vnorm1[pair * P.slots_pad + slot] = l1;
-    if (slot == 0) P.fill[pair] = nb;
+    P.vnorm[pair * P.slots_pad + slot] = nrm;
+    if (slot == 0) {
+      P.fill[pair] = nb;
+      P.victim[pair] = -1;
+    }
   }
 }
 
-template <typename T, int D, int G, bool EVICT, bool SPLIT, int WAVES = kDecodeWaves, int UA = 1,
-          int UB = 4, int POLICY = kStream>
+// ---------------------------------------------------------------------------
+// Sequence recycling: the listed sequences' pairs, in every layer, drop to 0
+// tokens with no pending victim. One workgroup per (sequence, layer).
+// ---------------------------------------------------------------------------
+struct ResetParams {
+  int32_t* fill;         // [layers][batch][num_kv_heads]
+  int32_t* victim;       // same layout
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t count;
+  int32_t seqs[kFillSeqPerLaunch];
+};
+
+__global__ __launch_bounds__(64) void seq_reset_kernel(ResetParams P) {
+  const int j = blockIdx.x;
+  if (j >= P.count) return;
+  const int b = P.seqs[j];
+  if (b < 0 || b >= P.batch) return;
+  const int64_t base = (static_cast<int64_t>(blockIdx.y) * P.batch + b) * P.num_kv_heads;
+  for (int hh = threadIdx.x; hh < P.num_kv_heads; hh += blockDim.x) {
+    P.fill[base + hh] = 0;
+    P.victim[base + hh] = -1;
+  }
+}
+
+template <typename T, int D, int G, bool EVICT, bool SPLIT, bool VAR = false, int WAVES = kDecodeWaves,
+          int UA = 1, int UB = 4, int POLICY = kStream>
 hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitWork& W, int splits,
                            const void* q, const void* k_new, const void* v_new, void* out,
                            int32_t* evicted, hipStream_t stream) {
@@ -889,14 +1066,20 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   P.vc = L.v;
   P.kc_w = L.k;
   P.vc_w = L.v;
-  P.vnorm1 = L.vnorm1;
+  P.vnorm = L.vnorm;
   P.fill = L.fill;
+  P.victim = L.victim;
   P.pair_elems = geo.pair_elems;
   P.num_q_heads = geo.num_q_heads;
   P.num_kv_heads = geo.num_kv_heads;
   P.budget = geo.budget;
   P.sink = geo.sink_size;
   P.scale_log2 = geo.scale * kLog2e;
+  P.deferred = geo.order == 1;
+  P.shared = geo.scope == 1;
+  P.norm_l2 = geo.norm == 1;
+  P.ws_score = W.score;
+  P.seq_arrive = W.seq_arrive;
   const int pairs = geo.batch * geo.num_kv_heads;
   P.pairs = pairs;
   P.splits = SPLIT ? splits : 1;
@@ -906,7 +1089,7 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits) : decode_lds_bytes(geo);
   if (lds == 0) return hipErrorInvalidValue;
   P.chunk = static_cast<int32_t>(lds / (sizeof(float) * G));  // EVICT: a whole split (or pair)
-  auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT>;
+  auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -928,14 +1111,16 @@ hipError_t launch_fill_t(const Geometry& geo, const LayerPtrs& L, const void* k,
   P.v = v;
   P.kc = L.k;
   P.vc = L.v;
-  P.vnorm1 = L.vnorm1;
+  P.vnorm = L.vnorm;
   P.fill = L.fill;
+  P.victim = L.victim;
   P.pair_elems = geo.pair_elems;
   P.slots_pad = geo.slots_pad;
+  P.norm_l2 = geo.norm == 1;
   P.num_kv_heads = geo.num_kv_heads;
   P.n_max = n_max;
   P.seq0 = seq0;
-  for (int i = 0; i < kFillSeqPerLaunch; ++i) P.n[i] = i < count ? n_host[i] : 0;
+  for (int i = 0; i < kFillSeqPerLaunch; ++i) P.n[i] = i < count ? n_host[i] : -1;
   dim3 grid((geo.slots_pad + 3) / 4, count * geo.num_kv_heads);
   hipLaunchKernelGGL((fill_kernel<T, D>), grid, dim3(256), 0, stream, P);
   return hipGetLastError();
@@ -982,17 +1167,17 @@ size_t split_part_floats(const Geometry& g) {
 hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
                          const void* q, const void* k_new, const void* v_new, void* out,
                          int32_t* evicted, hipStream_t stream) {
-#define LF_CASE(T, D, G)                                                                          \
-  if (g.head_dim == D && g.group == G) {                                                         \
-    if (splits > 1)                                                                              \
-      return g.mode == 0 ? launch_decode_t<T, D, G, true, true>(g, L, W, splits, q,   \
-                                                                  k_new, v_new, out, evicted, stream) \
-                         : launch_decode_t<T, D, G, false, true>(g, L, W, splits, q,  \
-                                                                   k_new, v_new, out, evicted, stream); \
-    return g.mode == 0 ? launch_decode_t<T, D, G, true, false>(g, L, W, 1, q, k_new, v_new, \
-                                                                 out, evicted, stream)             \
-                       : launch_decode_t<T, D, G, false, false>(g, L, W, 1, q, k_new, v_new, \
-                                                                  out, evicted, stream);           \
+  const bool var = g.order != 0 || g.scope != 0;
+#define LF_LAUNCH(T, D, G, EVICT, SPLIT, VAR) \
+  launch_decode_t<T, D, G, EVICT, SPLIT, VAR>(g, L, W, SPLIT ? splits : 1, q, k_new, v_new, out, evicted, stream)
+#define LF_CASE(T, D, G)                                                                      \
+  if (g.head_dim == D && g.group == G) {                                                     \
+    if (g.mode != 0)                                                                         \
+      return splits > 1 ? LF_LAUNCH(T, D, G, false, true, false)                             \
+                        : LF_LAUNCH(T, D, G, false, false, false);                           \
+    if (var)                                                                                 \
+      return splits > 1 ? LF_LAUNCH(T, D, G, true, true, true) : LF_LAUNCH(T, D, G, true, false, true); \
+    return splits > 1 ? LF_LAUNCH(T, D, G, true, true, false) : LF_LAUNCH(T, D, G, true, false, false); \
   }
   if (g.dtype == 1) {
     LF_CASE(uint16_t, 128, 1)
@@ -1010,7 +1195,22 @@ hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork&
     LF_CASE(float, 64, 4)
   }
 #undef LF_CASE
+#undef LF_LAUNCH
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_seq_reset(const Geometry& g, int32_t num_layers, int32_t* fill, int32_t* victim,
+                            const int32_t* seqs_host, int32_t count, hipStream_t stream) {
+  if (count <= 0 || count > kFillSeqPerLaunch || num_layers <= 0) return hipErrorInvalidValue;
+  ResetParams P;
+  P.fill = fill;
+  P.victim = victim;
+  P.batch = g.batch;
+  P.num_kv_heads = g.num_kv_heads;
+  P.count = count;
+  for (int i = 0; i < kFillSeqPerLaunch; ++i) P.seqs[i] = i < count ? seqs_host[i] : -1;
+  hipLaunchKernelGGL(seq_reset_kernel, dim3(count, num_layers), dim3(64), 0, stream, P);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill(const Geometry& g, const LayerPtrs& L, const void* k, const void* v,

@@ -3,11 +3,14 @@
 // Static cache allocator (LongFlow Guide, §Static Memory Pre-Allocation and
 // In-Place Eviction: one fixed buffer of B slots, never compacted): one
 // hipMalloc at create time holds, for every (layer, sequence, KV head) pair,
-//   K      [slots_pad][head_dim]  cache dtype
+//   K      [slots_pad][head_dim]  cache dtype (16-slot tiles, MFMA operand order)
 //   V      [slots_pad][head_dim]  cache dtype
-//   ||v||_1 [slots_pad]           float32 sidecar
+//   ||v||  [slots_pad]            float32 sidecar (l1, or l2)
 //   fill                          int32 tokens held
+//   victim                        int32 pending victim (deferred order)
 //   split-K workspace  partial softmax states and arrival counters
+//   per-sequence workspace  score vectors and arrival counters (one victim
+//                           per sequence)
 // and nothing is allocated afterwards. Validation happens on the host before
 // anything is queued; fill levels are mirrored on the host (every decode step
 // adds exactly one token per pair) so no call has to read the device, and the
@@ -31,8 +34,9 @@ struct lf_cache {
   void* base;
   char* k;
   char* v;
-  float* vnorm1;
+  float* vnorm;
   int32_t* fill;
+  int32_t* victim;
   int64_t layer_pairs;   // batch * num_kv_heads
   size_t elem_bytes;
   std::vector<int32_t> fill_host;  // [num_layers][batch]
@@ -47,7 +51,8 @@ constexpr size_t kAlign = 256;
 constexpr int kSlotAlign = 64;
 
 struct Layout {
-  size_t k_off, v_off, vn_off, fill_off, part_off, logit_off, arrive_off, total;
+  size_t k_off, v_off, vn_off, fill_off, victim_off, part_off, logit_off, arrive_off, score_off,
+      seq_arrive_off, total;
   int32_t slots_pad;
   int64_t pair_elems;
 };
@@ -66,10 +71,21 @@ lf_status validate(const lf_config* c) {
   if (!(c->softmax_scale >= 0.0f) || !std::isfinite(c->softmax_scale)) return LF_ERR_INVALID_ARG;
   if (c->dtype != LF_DTYPE_F32 && c->dtype != LF_DTYPE_BF16) return LF_ERR_INVALID_ARG;
   if (c->mode != LF_MODE_EVICT && c->mode != LF_MODE_FULL) return LF_ERR_INVALID_ARG;
+  if (c->order != LF_ORDER_SAME_STEP && c->order != LF_ORDER_DEFERRED) return LF_ERR_INVALID_ARG;
+  if (c->scope != LF_SCOPE_KV_HEAD && c->scope != LF_SCOPE_SEQUENCE) return LF_ERR_INVALID_ARG;
+  if (c->norm != LF_NORM_L1 && c->norm != LF_NORM_L2) return LF_ERR_INVALID_ARG;
+  if (c->mode == LF_MODE_FULL && (c->order || c->scope || c->norm)) return LF_ERR_INVALID_ARG;
   if (c->head_dim != 64 && c->head_dim != 128) return LF_ERR_UNSUPPORTED;
   const int g = c->num_q_heads / c->num_kv_heads;
   if (g != 1 && g != 2 && g != 4) return LF_ERR_UNSUPPORTED;
   if (c->budget > (1 << 30) - kSlotAlign) return LF_ERR_UNSUPPORTED;
+  if (c->scope == LF_SCOPE_SEQUENCE) {
+    // The deciding workgroup addresses a sequence's score vectors with 32-bit
+    // offsets.
+    const int64_t slots_pad = (static_cast<int64_t>(c->budget) + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
+    if (static_cast<int64_t>(c->num_kv_heads) * slots_pad * 4 >= (int64_t{1} << 31))
+      return LF_ERR_UNSUPPORTED;
+  }
   return LF_OK;
 }
 
@@ -85,6 +101,9 @@ lf::Geometry geometry(const lf_config* c) {
   g.slots_pad = (c->budget + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
   g.dtype = c->dtype;
   g.mode = c->mode;
+  g.order = c->order;
+  g.scope = c->scope;
+  g.norm = c->norm;
   g.pair_elems = static_cast<int64_t>(g.slots_pad) * c->head_dim;
   g.scale = c->softmax_scale > 0.0f ? c->softmax_scale
                                     : static_cast<float>(1.0 / std::sqrt(static_cast<double>(c->head_dim)));
@@ -113,6 +132,8 @@ lf_status layout(const lf_config* c, int32_t max_splits, Layout* L) {
   if (!add_ok(L->vn_off, align_up(vn), &t)) return LF_ERR_UNSUPPORTED;
   L->fill_off = t;
   if (!add_ok(L->fill_off, align_up(fl), &t)) return LF_ERR_UNSUPPORTED;
+  L->victim_off = t;
+  if (!add_ok(L->victim_off, align_up(fl), &t)) return LF_ERR_UNSUPPORTED;
   // Split-K workspace for one layer (the layers run one after another).
   size_t layer_pairs = static_cast<size_t>(c->batch) * c->num_kv_heads;
   size_t ws = max_splits > 1 ? layer_pairs * max_splits : 0;
@@ -124,6 +145,14 @@ lf_status layout(const lf_config* c, int32_t max_splits, Layout* L) {
   if (!add_ok(L->logit_off, align_up(logits), &t)) return LF_ERR_UNSUPPORTED;
   L->arrive_off = t;
   if (!add_ok(L->arrive_off, align_up(max_splits > 1 ? layer_pairs * 4 : 0), &t)) return LF_ERR_UNSUPPORTED;
+  // One victim per sequence: each pair's score vector for one layer launch.
+  const bool shared = c->scope == LF_SCOPE_SEQUENCE;
+  L->score_off = t;
+  if (!add_ok(L->score_off, align_up(shared ? layer_pairs * static_cast<size_t>(g.slots_pad) * 4 : 0), &t))
+    return LF_ERR_UNSUPPORTED;
+  L->seq_arrive_off = t;
+  if (!add_ok(L->seq_arrive_off, align_up(shared ? static_cast<size_t>(c->batch) * 4 : 0), &t))
+    return LF_ERR_UNSUPPORTED;
   L->total = t;
   return LF_OK;
 }
@@ -145,8 +174,9 @@ lf::LayerPtrs layer_ptrs(const lf_cache* c, int32_t layer) {
   const int64_t pair0 = static_cast<int64_t>(layer) * c->layer_pairs;
   p.k = c->k + pair0 * c->geo.pair_elems * static_cast<int64_t>(c->elem_bytes);
   p.v = c->v + pair0 * c->geo.pair_elems * static_cast<int64_t>(c->elem_bytes);
-  p.vnorm1 = c->vnorm1 + pair0 * c->geo.slots_pad;
+  p.vnorm = c->vnorm + pair0 * c->geo.slots_pad;
   p.fill = c->fill + pair0;
+  p.victim = c->victim + pair0;
   return p;
 }
 
@@ -248,11 +278,14 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->base = base;
   c->k = static_cast<char*>(base) + L.k_off;
   c->v = static_cast<char*>(base) + L.v_off;
-  c->vnorm1 = reinterpret_cast<float*>(static_cast<char*>(base) + L.vn_off);
+  c->vnorm = reinterpret_cast<float*>(static_cast<char*>(base) + L.vn_off);
   c->fill = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.fill_off);
+  c->victim = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.victim_off);
   c->work.part = reinterpret_cast<float*>(static_cast<char*>(base) + L.part_off);
   c->work.logit = reinterpret_cast<float*>(static_cast<char*>(base) + L.logit_off);
   c->work.arrive = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.arrive_off);
+  c->work.score = reinterpret_cast<float*>(static_cast<char*>(base) + L.score_off);
+  c->work.seq_arrive = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.seq_arrive_off);
   c->max_splits = max_splits;
   c->forced_splits = 0;
   *out = c;
@@ -275,16 +308,17 @@ lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view) {
   const lf::LayerPtrs p = layer_ptrs(c, layer);
   view->k = p.k;
   view->v = p.v;
-  view->vnorm1 = p.vnorm1;
+  view->vnorm = p.vnorm;
   view->fill = p.fill;
+  view->victim = p.victim;
   view->pair_stride = c->geo.pair_elems;
   view->slots_padded = c->geo.slots_pad;
   view->elem_bytes = static_cast<int32_t>(c->elem_bytes);
   return LF_OK;
 }
 
-lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm1,
-                            int32_t* fill, void* stream) {
+lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm,
+                            int32_t* fill, int32_t* victim, void* stream) {
   if (!c || layer < 0 || layer >= c->cfg.num_layers) return LF_ERR_INVALID_ARG;
   lf_status s = use_device(c);
   if (s != LF_OK) return s;
@@ -294,7 +328,8 @@ lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, 
   const size_t fill_bytes = static_cast<size_t>(c->layer_pairs) * sizeof(int32_t);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const struct { void* dst; const void* src; size_t n; } copies[] = {
-      {k, p.k, kv_bytes}, {v, p.v, kv_bytes}, {vnorm1, p.vnorm1, vn_bytes}, {fill, p.fill, fill_bytes}};
+      {k, p.k, kv_bytes}, {v, p.v, kv_bytes}, {vnorm, p.vnorm, vn_bytes}, {fill, p.fill, fill_bytes},
+      {victim, p.victim, fill_bytes}};
   for (const auto& cp : copies) {
     if (!cp.dst) continue;
     if (hipMemcpyAsync(cp.dst, cp.src, cp.n, hipMemcpyDeviceToDevice, st) != hipSuccess)
@@ -328,20 +363,44 @@ lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void*
     return LF_ERR_INVALID_ARG;
   if (n_max > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return LF_ERR_INVALID_ARG;
   for (int32_t b = 0; b < c->cfg.batch; ++b) {
-    if (n_per_seq[b] < 0 || n_per_seq[b] > n_max) return LF_ERR_INVALID_ARG;
+    if (n_per_seq[b] < -1 || n_per_seq[b] > n_max) return LF_ERR_INVALID_ARG;
     if (n_per_seq[b] > c->cfg.budget) return LF_ERR_CAPACITY;
   }
   lf_status s = use_device(c);
   if (s != LF_OK) return s;
   const lf::LayerPtrs p = layer_ptrs(c, layer);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* fh = c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch;
   for (int32_t b0 = 0; b0 < c->cfg.batch; b0 += lf::kFillSeqPerLaunch) {
     const int32_t count = std::min<int32_t>(lf::kFillSeqPerLaunch, c->cfg.batch - b0);
+    bool any = false;
+    for (int32_t i = 0; i < count; ++i) any = any || n_per_seq[b0 + i] >= 0;
+    if (!any) continue;  // every sequence of this group is left as it is
     if (lf::launch_fill(c->geo, p, k, v, n_per_seq + b0, b0, count, n_max, st) != hipSuccess)
       return LF_ERR_HIP;
   }
-  std::memcpy(c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch, n_per_seq,
-              sizeof(int32_t) * c->cfg.batch);
+  for (int32_t b = 0; b < c->cfg.batch; ++b)
+    if (n_per_seq[b] >= 0) fh[b] = n_per_seq[b];
+  return LF_OK;
+}
+
+lf_status lf_seq_reset(lf_cache* c, const int32_t* seqs, int32_t count, void* stream) {
+  if (!c || count < 0 || (count > 0 && !seqs)) return LF_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < count; ++i)
+    if (seqs[i] < 0 || seqs[i] >= c->cfg.batch) return LF_ERR_INVALID_ARG;
+  if (count == 0) return LF_OK;
+  lf_status s = use_device(c);
+  if (s != LF_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t i0 = 0; i0 < count; i0 += lf::kFillSeqPerLaunch) {
+    const int32_t n = std::min<int32_t>(lf::kFillSeqPerLaunch, count - i0);
+    if (lf::launch_seq_reset(c->geo, c->cfg.num_layers, c->fill, c->victim, seqs + i0, n, st) !=
+        hipSuccess)
+      return LF_ERR_HIP;
+  }
+  for (int32_t l = 0; l < c->cfg.num_layers; ++l)
+    for (int32_t i = 0; i < count; ++i)
+      c->fill_host[static_cast<size_t>(l) * c->cfg.batch + seqs[i]] = 0;
   return LF_OK;
 }
 

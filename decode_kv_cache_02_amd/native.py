@@ -27,9 +27,18 @@ LF_DTYPE_F32 = 0
 LF_DTYPE_BF16 = 1
 LF_MODE_EVICT = 0
 LF_MODE_FULL = 1
+LF_ORDER_SAME_STEP = 0
+LF_ORDER_DEFERRED = 1
+LF_SCOPE_KV_HEAD = 0
+LF_SCOPE_SEQUENCE = 1
+LF_NORM_L1 = 0
+LF_NORM_L2 = 1
 
 DTYPES = {"f32": LF_DTYPE_F32, "bf16": LF_DTYPE_BF16}
 MODES = {"evict": LF_MODE_EVICT, "full": LF_MODE_FULL}
+ORDERS = {"same_step": LF_ORDER_SAME_STEP, "deferred": LF_ORDER_DEFERRED}
+SCOPES = {"kv_head": LF_SCOPE_KV_HEAD, "sequence": LF_SCOPE_SEQUENCE}
+NORMS = {"l1": LF_NORM_L1, "l2": LF_NORM_L2}
 
 
 class lf_config(ctypes.Structure):
@@ -44,6 +53,9 @@ class lf_config(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("mode", ctypes.c_int32),
+        ("order", ctypes.c_int32),
+        ("scope", ctypes.c_int32),
+        ("norm", ctypes.c_int32),
     ]
 
 
@@ -51,8 +63,9 @@ class lf_view(ctypes.Structure):
     _fields_ = [
         ("k", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
-        ("vnorm1", ctypes.c_void_p),
+        ("vnorm", ctypes.c_void_p),
         ("fill", ctypes.c_void_p),
+        ("victim", ctypes.c_void_p),
         ("pair_stride", ctypes.c_int64),
         ("slots_padded", ctypes.c_int32),
         ("elem_bytes", ctypes.c_int32),
@@ -72,7 +85,9 @@ SIGNATURES = [
     ("lf_cache_view", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(lf_view)]),
     ("lf_cache_snapshot", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                          ctypes.c_void_p]),
+                                          ctypes.c_void_p, ctypes.c_void_p]),
+    ("lf_seq_reset", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                     ctypes.c_void_p]),
     ("lf_cache_set_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_max_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_fill_levels", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
@@ -122,11 +137,13 @@ def _check(status: int, where: str) -> None:
 
 
 def make_config(num_layers, batch, num_q_heads, num_kv_heads, head_dim, budget,
-                sink_size=0, softmax_scale=0.0, dtype="bf16", mode="evict") -> lf_config:
+                sink_size=0, softmax_scale=0.0, dtype="bf16", mode="evict",
+                order="same_step", scope="kv_head", norm="l1") -> lf_config:
+    pick = lambda table, x: table[x] if isinstance(x, str) else int(x)
     return lf_config(int(num_layers), int(batch), int(num_q_heads), int(num_kv_heads),
                      int(head_dim), int(budget), int(sink_size), float(softmax_scale),
-                     DTYPES[dtype] if isinstance(dtype, str) else int(dtype),
-                     MODES[mode] if isinstance(mode, str) else int(mode))
+                     pick(DTYPES, dtype), pick(MODES, mode), pick(ORDERS, order),
+                     pick(SCOPES, scope), pick(NORMS, norm))
 
 
 # ----------------------------------------------------------------------------
@@ -183,13 +200,21 @@ def lf_cache_view(handle: int, layer: int) -> lf_view:
     return v
 
 
-def lf_cache_snapshot(handle: int, layer: int, k=None, v=None, vnorm1=None, fill=None,
-                      stream=None) -> None:
+def lf_cache_snapshot(handle: int, layer: int, k=None, v=None, vnorm=None, fill=None,
+                      victim=None, stream=None) -> None:
     ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
     _check(load_library().lf_cache_snapshot(ctypes.c_void_p(handle), int(layer), ptr(k), ptr(v),
-                                            ptr(vnorm1), ptr(fill),
+                                            ptr(vnorm), ptr(fill), ptr(victim),
                                             ctypes.c_void_p(_stream_ptr(stream))),
            "lf_cache_snapshot")
+
+
+def lf_seq_reset(handle: int, seqs, stream=None) -> None:
+    s = np.ascontiguousarray(seqs, dtype=np.int32)
+    _check(load_library().lf_seq_reset(ctypes.c_void_p(handle),
+                                       s.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                       int(s.size), ctypes.c_void_p(_stream_ptr(stream))),
+           "lf_seq_reset")
 
 
 def lf_cache_set_splits(handle: int, splits: int) -> None:
@@ -238,10 +263,11 @@ class LongFlowCache:
     """Owns one lf_cache handle. Tensors are torch device tensors in the cache dtype."""
 
     def __init__(self, num_layers, batch, num_q_heads, num_kv_heads, head_dim, budget,
-                 sink_size=0, softmax_scale=0.0, dtype="bf16", mode="evict"):
+                 sink_size=0, softmax_scale=0.0, dtype="bf16", mode="evict",
+                 order="same_step", scope="kv_head", norm="l1"):
         import torch
         self.cfg = make_config(num_layers, batch, num_q_heads, num_kv_heads, head_dim, budget,
-                               sink_size, softmax_scale, dtype, mode)
+                               sink_size, softmax_scale, dtype, mode, order, scope, norm)
         self.dtype = dtype
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.num_layers, self.batch = int(num_layers), int(batch)
@@ -279,6 +305,9 @@ class LongFlowCache:
         self._check_tensor(evicted_slot, (self.batch, self.hkv), "evicted_slot", torch.int32)
         lf_decode_step(self.handle, layer, q, k_new, v_new, out, evicted_slot, stream)
 
+    def seq_reset(self, seqs, stream=None) -> None:
+        lf_seq_reset(self.handle, seqs, stream)
+
     def set_splits(self, splits: int) -> None:
         lf_cache_set_splits(self.handle, splits)
 
@@ -292,10 +321,11 @@ class LongFlowCache:
     def fill_levels(self, layer) -> np.ndarray:
         return lf_fill_levels(self.handle, layer, self.batch)
 
-    def snapshot(self, layer):
+    def snapshot(self, layer, with_victim: bool = False):
         """Copies of one layer: K, V [batch][hkv][slots_pad][d] (K un-tiled to
-        row-major), ||v||_1 [batch][hkv][slots_pad], fill [batch][hkv]; device
-        tensors, stream-ordered."""
+        row-major), the ||v|| sidecar [batch][hkv][slots_pad], fill [batch][hkv]
+        and, if asked, the pending victims [batch][hkv]; device tensors,
+        stream-ordered."""
         import torch
         slots = self.view(layer).slots_padded
         k = torch.empty((self.batch, self.hkv, slots * self.head_dim), dtype=self.torch_dtype,
@@ -303,9 +333,11 @@ class LongFlowCache:
         v = torch.empty_like(k)
         vn = torch.empty((self.batch, self.hkv, slots), dtype=torch.float32, device="cuda")
         fill = torch.empty((self.batch, self.hkv), dtype=torch.int32, device="cuda")
-        lf_cache_snapshot(self.handle, layer, k, v, vn, fill)
-        return (untile_k(k, self.head_dim), v.view(self.batch, self.hkv, slots, self.head_dim),
-                vn, fill)
+        victim = torch.empty_like(fill) if with_victim else None
+        lf_cache_snapshot(self.handle, layer, k, v, vn, fill, victim)
+        res = (untile_k(k, self.head_dim), v.view(self.batch, self.hkv, slots, self.head_dim),
+               vn, fill)
+        return res + (victim,) if with_victim else res
 
     def close(self):
         if getattr(self, "handle", None):

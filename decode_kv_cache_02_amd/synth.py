@@ -24,7 +24,9 @@ Value recipe (one reading each, stated where the pages are silent):
     (bfloat16 with round-to-nearest-even, or float32).
   * Near-tie stress: with probability `dup_frac` a token copies both the K and
     V rows of a uniformly chosen earlier token of the same (sequence, KV head),
-    so the two tokens' scores collide exactly.
+    so the two tokens' scores collide exactly. With dup_scope="sequence" the
+    draw is made once per sequence and the same earlier token is copied in
+    every KV head, so scores summed over the heads collide as well.
 """
 from __future__ import annotations
 
@@ -85,6 +87,7 @@ class Workload:
     prefill: int             # prompt tokens per sequence (uniform workloads)
     steps: int               # decode steps in the full trajectory
     dup_frac: float = 0.0
+    dup_scope: str = "pair"      # "sequence": one draw per sequence, copied in every KV head
     ragged_max_offset: int = 0   # >0: per-sequence start offset ~ U[0, this)
     sink_size: int = 0
     note: str = ""
@@ -208,8 +211,12 @@ class TokenStream:
             t = self.tokens_emitted + j
             if t == 0:
                 continue
-            pick = rng.random((wl.batch, wl.num_kv_heads)) < wl.dup_frac
-            choice = rng.integers(0, t, size=(wl.batch, wl.num_kv_heads))
+            if wl.dup_scope == "sequence":
+                pick = np.repeat((rng.random(wl.batch) < wl.dup_frac)[:, None], wl.num_kv_heads, 1)
+                choice = np.repeat(rng.integers(0, t, size=wl.batch)[:, None], wl.num_kv_heads, 1)
+            else:
+                pick = rng.random((wl.batch, wl.num_kv_heads)) < wl.dup_frac
+                choice = rng.integers(0, t, size=(wl.batch, wl.num_kv_heads))
             for b, h in zip(*np.nonzero(pick)):
                 s = int(choice[b, h])
                 if s >= self.tokens_emitted:

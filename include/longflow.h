@@ -11,7 +11,12 @@
  *     §2.1 (LongFlowScore);
  *   - the static buffer, initial fill, argmin eviction and in-place overwrite:
  *     LongFlow Guide, §Static Memory Pre-Allocation and In-Place Eviction,
- *     items 1-3; gist.science summary, §2.3 (static KV cache, one fused pass).
+ *     items 1-3; gist.science summary, §2.3 (static KV cache, one fused pass);
+ *   - the variants selected in lf_config (l2 norm, the engine's deferred
+ *     order, one victim per sequence): LongFlow Guide, §Mathematical
+ *     Derivation (l1 or l2 norm of c_{t,i}) and §End-to-End Implementation:
+ *     Building a LongFlow Engine (victim applied at the next call, scores
+ *     summed over all heads).
  *
  * Unit of work: a "pair" is one (layer, sequence b, KV head h). Query head j
  * belongs to KV head j / G, G = num_q_heads / num_kv_heads. Pairs never
@@ -27,6 +32,20 @@
  *         overwritten in place by k_new, v_new, ||v_new||_1.
  * ||v||_1 is kept per slot in a float32 sidecar, computed once when the token
  * is stored, from the stored (dtype-rounded) values.
+ *
+ * Variants (lf_config.order / scope / norm; 0 selects the behaviour above):
+ *   LF_NORM_L2          the sidecar and the score use ||v||_2 instead.
+ *   LF_ORDER_DEFERRED   the engine's order. Below the budget the token is
+ *                       appended. At the budget it first replaces the slot
+ *                       chosen by the PREVIOUS step (budget-1 if none was
+ *                       chosen yet, e.g. right after a full prefill); the
+ *                       replaced token leaves the softmax. When the buffer is
+ *                       full after the write, the step scores the cached
+ *                       slots (sinks and the slot just written excluded) and
+ *                       keeps the argmin as the next victim.
+ *   LF_SCOPE_SEQUENCE   one victim per (layer, sequence): the argmin of the
+ *                       score summed over the sequence's KV heads, in head
+ *                       order; every KV head of the sequence evicts that slot.
  *
  * Conventions for every call:
  *   - The handle owns all cache memory (K, V, ||v||_1, fill counters): one
@@ -71,6 +90,18 @@ typedef enum {
   LF_MODE_FULL = 1   /* full-KV baseline: capacity `budget`, never evicts         */
 } lf_mode;
 
+typedef enum {
+  LF_ORDER_SAME_STEP = 0, /* score -> argmin -> overwrite within one step         */
+  LF_ORDER_DEFERRED = 1   /* overwrite the previous step's victim, then choose    */
+} lf_order;
+
+typedef enum {
+  LF_SCOPE_KV_HEAD = 0,  /* one victim per (sequence, KV head)                    */
+  LF_SCOPE_SEQUENCE = 1  /* one victim per sequence, scores summed over KV heads  */
+} lf_scope;
+
+typedef enum { LF_NORM_L1 = 0, LF_NORM_L2 = 1 } lf_norm;
+
 typedef struct {
   int32_t num_layers;   /* >= 1                                                  */
   int32_t batch;        /* sequences, >= 1                                       */
@@ -82,6 +113,9 @@ typedef struct {
   float softmax_scale;  /* tau; 0 selects 1/sqrt(head_dim)                      */
   int32_t dtype;        /* lf_dtype: of the cache and of q, k_new, v_new, out    */
   int32_t mode;         /* lf_mode                                               */
+  int32_t order;        /* lf_order; must be 0 in FULL mode                      */
+  int32_t scope;        /* lf_scope; must be 0 in FULL mode                      */
+  int32_t norm;         /* lf_norm; must be 0 in FULL mode                       */
 } lf_config;
 
 /* Device addresses and strides of one layer's region (for tests, snapshots).
@@ -95,8 +129,10 @@ typedef struct {
 typedef struct {
   void* k;              /* [batch][num_kv_heads][slots_padded/16 tiles] cfg.dtype, tiled as above */
   void* v;              /* [batch][num_kv_heads][slots_padded][head_dim] cfg.dtype                */
-  float* vnorm1;        /* [batch][num_kv_heads][slots_padded] float32              */
+  float* vnorm;         /* [batch][num_kv_heads][slots_padded] float32: ||v||_1 (or _2) */
   int32_t* fill;        /* [batch][num_kv_heads] int32: tokens held per pair        */
+  int32_t* victim;      /* [batch][num_kv_heads] int32: LF_ORDER_DEFERRED's next
+                           victim, -1 = none chosen (unused in the other order)   */
   int64_t pair_stride;  /* elements between consecutive pairs in k / v             */
   int32_t slots_padded; /* budget rounded up to a multiple of 64                    */
   int32_t elem_bytes;   /* 4 (float32) or 2 (bfloat16)                              */
@@ -114,9 +150,12 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out);
 /* Initial fill of one layer (LongFlow Guide, §Static Memory..., item 1).
  *   k, v          device, [batch][n_max][num_kv_heads][head_dim], cfg.dtype
  *   n_per_seq     HOST array [batch]; sequence b stores its first n_b rows in
- *                 slots 0..n_b-1 of each of its pairs; 0 <= n_b <= n_max
- * Slots n_b..budget-1 are cleared. Errors: LF_ERR_CAPACITY if some
- * n_b > budget, LF_ERR_INVALID_ARG on null pointers, a bad layer or n_b > n_max. */
+ *                 slots 0..n_b-1 of each of its pairs; 0 <= n_b <= n_max.
+ *                 n_b = -1 leaves sequence b exactly as it is (refill only
+ *                 the sequences being recycled, see lf_seq_reset)
+ * Slots n_b..budget-1 are cleared and no victim is pending. k and v may be
+ * NULL when n_max = 0. Errors: LF_ERR_CAPACITY if some n_b > budget,
+ * LF_ERR_INVALID_ARG on null pointers, a bad layer, n_b > n_max or n_b < -1. */
 lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void* v,
                           const int32_t* n_per_seq, int32_t n_max, void* stream);
 
@@ -125,8 +164,9 @@ lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void*
  *   k_new, v_new  device [batch][num_kv_heads][head_dim], cfg.dtype
  *   out           device [batch][num_q_heads][head_dim], cfg.dtype; written
  *                 (bfloat16 outputs are rounded to nearest even from float32)
- *   evicted_slot  device [batch][num_kv_heads] int32; written: the slot that
- *                 was overwritten, or -1 when the token was appended
+ *   evicted_slot  device [batch][num_kv_heads] int32; written: the slot whose
+ *                 token was replaced this step, or -1 when the token was
+ *                 appended
  * Accumulation is float32. Errors: LF_ERR_INVALID_ARG on null pointers or a
  * bad layer; LF_ERR_CAPACITY in FULL mode when a pair already holds
  * `budget` tokens; LF_ERR_HIP if the launch fails. */
@@ -142,11 +182,12 @@ lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view);
  * single contiguous copy):
  *   k, v    [batch][num_kv_heads][slots_padded*head_dim] cfg.dtype, in the
  *           layouts of lf_view (K tiled, V row-major)
- *   vnorm1  [batch][num_kv_heads][slots_padded] float32
+ *   vnorm   [batch][num_kv_heads][slots_padded] float32
  *   fill    [batch][num_kv_heads] int32
- * Any of the four may be NULL to skip it. */
-lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm1,
-                            int32_t* fill, void* stream);
+ *   victim  [batch][num_kv_heads] int32
+ * Any of the five may be NULL to skip it. */
+lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm,
+                            int32_t* fill, int32_t* victim, void* stream);
 
 /* Split-K tuning. By default each launch picks how many workgroups share a
  * pair: 1 when the layer has 256 pairs or more (one workgroup per pair
@@ -161,6 +202,22 @@ lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits);
  * caller's HOST array. Tracked on the host from the calls made (no device
  * access, no synchronisation). */
 lf_status lf_fill_levels(const lf_cache* c, int32_t layer, int32_t* fill_host);
+
+/* Recycle the regions of `count` sequences for new requests (continuous
+ * batching over the static buffer, LongFlow Guide, §Static Memory
+ * Pre-Allocation and In-Place Eviction: slots are reused in place, never
+ * freed or compacted). In every layer, each listed sequence's pairs drop to 0
+ * tokens with no pending victim; its rows are left as they are and are never
+ * read again before being overwritten. Nothing is allocated or freed.
+ *   seqs   HOST array [count] of sequence indices in [0, batch)
+ * A later lf_prefill_fill with n_b = -1 for the other sequences loads the new
+ * prompts; decode steps may also start from 0 tokens. A sequence that stays
+ * idle keeps taking one token per decode step (its q, k_new, v_new rows are
+ * the caller's to fill, its output is to be ignored). Stream-ordered; no
+ * memset is queued (safe under graph capture). Errors: LF_ERR_INVALID_ARG on
+ * a null handle, count < 0, seqs == NULL with count > 0, or an index out of
+ * range. */
+lf_status lf_seq_reset(lf_cache* c, const int32_t* seqs, int32_t count, void* stream);
 
 /* Release the handle and its device memory. NULL is a no-op. The caller must
  * make sure no queued work still uses the cache. */

@@ -62,8 +62,8 @@ def test_cache_bytes_layout(lib):
     pairs = 64 * 8
     slots = 3328                       # 3277 rounded up to 64
     kv = pairs * slots * 128 * 2
-    assert b >= 2 * kv + pairs * slots * 4 + pairs * 4
-    assert b < 2 * kv + pairs * slots * 4 + pairs * 4 + 4 * 256
+    assert b >= 2 * kv + pairs * slots * 4 + 2 * pairs * 4         # + fill and victim
+    assert b < 2 * kv + pairs * slots * 4 + 2 * pairs * 4 + 5 * 256
     b32 = native.lf_cache_bytes(_cfg(num_layers=32, batch=103))
     assert b32 > 32 * 103 * 8 * slots * 128 * 2 * 2
 
@@ -77,6 +77,12 @@ def test_cache_bytes_layout(lib):
     (dict(softmax_scale=-1.0), native.LF_ERR_INVALID_ARG),
     (dict(dtype=7), native.LF_ERR_INVALID_ARG),
     (dict(mode=9), native.LF_ERR_INVALID_ARG),
+    (dict(order=2), native.LF_ERR_INVALID_ARG),
+    (dict(scope=-1), native.LF_ERR_INVALID_ARG),
+    (dict(norm=3), native.LF_ERR_INVALID_ARG),
+    (dict(mode="full", order="deferred"), native.LF_ERR_INVALID_ARG),
+    (dict(mode="full", scope="sequence"), native.LF_ERR_INVALID_ARG),
+    (dict(mode="full", norm="l2"), native.LF_ERR_INVALID_ARG),
     (dict(head_dim=96), native.LF_ERR_UNSUPPORTED),
     (dict(num_q_heads=64), native.LF_ERR_UNSUPPORTED),        # G = 8 not built
 ])
@@ -96,7 +102,8 @@ def test_null_arguments_rejected(lib):
     assert lib.lf_prefill_fill(None, 0, None, None, n, 0, None) == native.LF_ERR_INVALID_ARG
     assert lib.lf_decode_step(None, 0, None, None, None, None, None, None) == native.LF_ERR_INVALID_ARG
     assert lib.lf_cache_view(None, 0, None) == native.LF_ERR_INVALID_ARG
-    assert lib.lf_cache_snapshot(None, 0, None, None, None, None, None) == native.LF_ERR_INVALID_ARG
+    assert lib.lf_cache_snapshot(None, 0, None, None, None, None, None, None) == native.LF_ERR_INVALID_ARG
+    assert lib.lf_seq_reset(None, None, 0, None) == native.LF_ERR_INVALID_ARG
     assert lib.lf_fill_levels(None, 0, None) == native.LF_ERR_INVALID_ARG
     lib.lf_cache_destroy(None)   # no-op
 
@@ -105,3 +112,31 @@ def test_binding_raises_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(native, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         native.load_library(str(tmp_path / "nope.so"))
+
+
+def test_config_struct_matches_header():
+    """The ctypes mirror of lf_config has the header's fields, in order."""
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct {\n  int32_t num_layers;"):]
+    body = body[:body.index("} lf_config;")]
+    fields = re.findall(r"^\s+(?:int32_t|float)\s+(\w+);", body, flags=re.M)
+    assert fields == [f for f, _ in native.lf_config._fields_]
+
+
+def test_view_struct_matches_header():
+    text = open(HEADER).read()
+    body = text[:text.index("} lf_view;")]
+    body = body[body.rindex("typedef struct {"):]
+    fields = re.findall(r"^\s+[\w\*]+\s+\*?(\w+);", body, flags=re.M)
+    assert fields == [f for f, _ in native.lf_view._fields_]
+
+
+def test_variant_workspace_bytes(lib):
+    """One victim per sequence adds each pair's score vector and a counter per
+    sequence; the other variants add nothing beyond the victim array."""
+    base = native.lf_cache_bytes(_cfg())
+    assert native.lf_cache_bytes(_cfg(order="deferred")) == base
+    assert native.lf_cache_bytes(_cfg(norm="l2")) == base
+    shared = native.lf_cache_bytes(_cfg(scope="sequence"))
+    extra = 64 * 8 * 3328 * 4
+    assert extra <= shared - base < extra + 2 * 256 + 64 * 4

@@ -159,7 +159,7 @@ def test_static_memory_and_determinism():
         evs = torch.empty((11,) + tuple(ev.shape), dtype=ev.dtype, device="cuda")
         torch.cuda.synchronize()
         v0 = c.view(0)
-        ptrs0 = (v0.k, v0.v, v0.vnorm1, v0.fill)
+        ptrs0 = (v0.k, v0.v, v0.vnorm, v0.fill)
         free0 = torch.cuda.mem_get_info()[0]
         for t in range(1000):
             q, kn, vn = dev[t % 16]
@@ -169,7 +169,7 @@ def test_static_memory_and_determinism():
                 evs[t // 97].copy_(ev)
         torch.cuda.synchronize()
         v1 = c.view(0)
-        assert (v1.k, v1.v, v1.vnorm1, v1.fill) == ptrs0
+        assert (v1.k, v1.v, v1.vnorm, v1.fill) == ptrs0
         assert torch.cuda.mem_get_info()[0] == free0
         snap = c.snapshot(0)
         results.append((outs.cpu(), evs.cpu(),

@@ -1,0 +1,165 @@
+"""GPU parity of the variants against the oracle: the blog engine's deferred
+order, one victim per sequence (scores summed over KV heads), the l2 score,
+and sequence recycling in the static buffer (lf_seq_reset + partial prefill).
+
+Same lockstep protocol and tolerances as test_gpu_parity; the deferred order's
+victim is observed one step later as the slot it replaces.
+"""
+import numpy as np
+import pytest
+
+from decode_kv_cache_02_amd.synth import WORKLOADS
+from lockstep import run_lockstep
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_kv_cache_02_amd import native
+    native.load_library()
+    yield
+
+
+TINY_MULTI = WORKLOADS["tiny_f32"].with_(batch=3, num_q_heads=4, num_kv_heads=2)
+
+
+# ----------------------------------------------------------------------------
+# Deferred order
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("prefill", [64, 40])
+def test_deferred_tiny_f32(prefill):
+    """prefill 64 = budget: the first step falls back to the last slot;
+    prefill 40: the buffer fills, then the step that fills it picks a victim."""
+    wl = WORKLOADS["tiny_f32"].with_(prefill=prefill)
+    _say(f"tiny_f32 deferred, prefill {prefill}, 200 steps")
+    rep = run_lockstep(wl, 200, order="deferred", check_cache_every=25)
+    assert rep.replaced == 200 - (64 - prefill)
+    # every replacing step scores, and so does the step that fills the buffer
+    assert rep.evictions == 200 - (64 - prefill) + (1 if prefill < 64 else 0)
+
+
+def test_deferred_sinks_and_tiny_budget():
+    wl = WORKLOADS["tiny_f32"].with_(budget=8, prefill=3)
+    _say("f32 deferred, B 8, sink 4, 60 steps")
+    rep = run_lockstep(wl, 60, order="deferred", sink_size=4, check_cache_every=10)
+    assert rep.replaced == 55
+
+
+@pytest.mark.parametrize("dtype,G,d,budget,prefill,steps,splits", [
+    ("bf16", 4, 128, 200, 200, 40, 0),
+    ("bf16", 2, 64, 300, 290, 30, 3),
+    ("f32", 4, 128, 520, 500, 30, 4),
+])
+def test_deferred_small_shapes(dtype, G, d, budget, prefill, steps, splits):
+    wl = WORKLOADS["tiny_f32"].with_(dtype=dtype, batch=3, num_kv_heads=2, num_q_heads=2 * G,
+                                     head_dim=d, budget=budget, prefill=prefill, steps=steps)
+    _say(f"deferred {dtype} G={G} d={d} B={budget} prefill={prefill} splits={splits}")
+    rep = run_lockstep(wl, steps, order="deferred", splits=splits, check_cache_every=10)
+    assert rep.replaced >= steps - (budget - prefill)
+
+
+def test_deferred_llama_layer_sampled_pairs():
+    wl = WORKLOADS["llama8b_layer"].with_(prefill=3277)
+    pairs = [(0, 0), (17, 3), (40, 7), (63, 5)]
+    _say("llama8b layer deferred, steady state, 6 steps, 4 sampled pairs")
+    rep = run_lockstep(wl, 6, pairs=pairs, order="deferred", check_cache_every=6)
+    assert rep.replaced == 24
+
+
+# ----------------------------------------------------------------------------
+# One victim per sequence
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", ["same_step", "deferred"])
+def test_shared_scope_tiny(order):
+    _say(f"f32 shared scope ({order}), batch 3, 2 KV heads, 120 steps")
+    rep = run_lockstep(TINY_MULTI, 120, scope="sequence", order=order, check_cache_every=20)
+    assert rep.evictions >= 120 * 6 - 6
+
+
+@pytest.mark.parametrize("order,splits", [("same_step", 2), ("deferred", 4), ("same_step", 0)])
+def test_shared_scope_bf16(order, splits):
+    wl = WORKLOADS["tiny_f32"].with_(dtype="bf16", batch=4, num_q_heads=32, num_kv_heads=8,
+                                     head_dim=128, budget=400, prefill=380)
+    _say(f"bf16 shared scope ({order}), 8 KV heads, B 400, splits {splits}, 40 steps")
+    rep = run_lockstep(wl, 40, scope="sequence", order=order, splits=splits,
+                       check_cache_every=20)
+    assert rep.steps == 40
+
+
+@pytest.mark.parametrize("order", ["same_step", "deferred"])
+def test_shared_scope_exact_ties(order):
+    """Tokens duplicated in every KV head give exactly equal head sums; the
+    lowest slot must win."""
+    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(batch=4, budget=512, prefill=512,
+                                                  dup_scope="sequence", dup_frac=0.2)
+    _say(f"bf16 shared scope ties ({order}), batch 4, B 512, 40 steps")
+    rep = run_lockstep(wl, 40, pairs=[(0, 0), (2, 0)], scope="sequence", order=order,
+                       check_cache_every=40)
+    print(f"near-ties {rep.near_ties}, exact ties {rep.exact_ties}, "
+          f"lowest index taken {rep.tie_lowest_index}")
+    assert rep.exact_ties > 0
+    assert rep.tie_lowest_index == rep.exact_ties
+
+
+def test_shared_scope_llama_layer_sampled_sequences():
+    wl = WORKLOADS["llama8b_layer"].with_(prefill=3277)
+    _say("llama8b layer, shared scope, steady state, 4 steps, sequences 0 and 63")
+    rep = run_lockstep(wl, 4, pairs=[(0, 0), (63, 0)], scope="sequence", check_cache_every=4)
+    assert rep.evictions == 4 * 16
+
+
+# ----------------------------------------------------------------------------
+# l2 score
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order,scope,splits", [
+    ("same_step", "kv_head", 0), ("same_step", "kv_head", 4),
+    ("deferred", "sequence", 0), ("deferred", "sequence", 2),
+])
+def test_l2_norm(order, scope, splits):
+    _say(f"f32 l2 score ({order}, {scope}, splits {splits}), 80 steps")
+    rep = run_lockstep(TINY_MULTI, 80, norm="l2", order=order, scope=scope, splits=splits,
+                       check_cache_every=20)
+    assert rep.steps == 80
+
+
+def test_l2_bf16_layer_shape():
+    wl = WORKLOADS["qwen3_0p6b_layer"].with_(prefill=1024)
+    _say("qwen3 0.6B layer, l2 score, 5 steps, sampled pairs")
+    rep = run_lockstep(wl, 5, pairs=[(0, 0), (31, 7), (9, 4)], norm="l2", check_cache_every=5)
+    assert rep.evictions == 15
+
+
+# ----------------------------------------------------------------------------
+# Sequence recycling
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order,scope", [("same_step", "kv_head"), ("deferred", "kv_head"),
+                                         ("same_step", "sequence")])
+def test_recycling(order, scope):
+    """Sequences finish and new prompts take their slots mid-run: reset to 0,
+    a partial prefill (the others untouched), and decode continues."""
+    wl = TINY_MULTI.with_(budget=48, prefill=30)
+    plan = {25: ([1], 20), 50: ([0, 2], 48), 70: ([1], 0)}
+    _say(f"f32 recycling ({order}, {scope}), 100 steps, resets at {sorted(plan)}")
+    rep = run_lockstep(wl, 100, order=order, scope=scope, recycle=plan, check_cache_every=5)
+    assert rep.recycled == 4
+
+
+def test_recycling_bf16_with_splits():
+    wl = WORKLOADS["tiny_f32"].with_(dtype="bf16", batch=4, num_q_heads=8, num_kv_heads=2,
+                                     head_dim=128, budget=600, prefill=600)
+    plan = {3: ([2], 100), 8: ([0, 3], 599)}
+    _say("bf16 recycling, B 600, 4 splits, 16 steps")
+    rep = run_lockstep(wl, 16, splits=4, recycle=plan, check_cache_every=4)
+    assert rep.recycled == 3
