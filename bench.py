@@ -174,7 +174,7 @@ def full_kv_baseline(wl, steps, warmup, fills=(8704, 16384)):
 
 
 def steady_state(wl, steps, warmup, fill=None, mode="evict", layers=1, capacity=None,
-                 ragged=None, seed=0):
+                 ragged=None, seed=0, order="same_step", scope="kv_head", norm="l1"):
     """Time `steps` model steps (one lf_decode_step per layer) at the given
     fill levels; returns (ms per model step, algorithmic bytes per model step)."""
     import torch
@@ -184,7 +184,7 @@ def steady_state(wl, steps, warmup, fill=None, mode="evict", layers=1, capacity=
     cap = wl.budget if capacity is None else capacity
     torch.cuda.empty_cache()
     cache = LongFlowCache(layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, cap,
-                          dtype=wl.dtype, mode=mode)
+                          dtype=wl.dtype, mode=mode, order=order, scope=scope, norm=norm)
     try:
         n = np.full(wl.batch, wl.budget if fill is None else fill, dtype=np.int64)
         if ragged is not None:
@@ -228,6 +228,69 @@ def steady_state(wl, steps, warmup, fill=None, mode="evict", layers=1, capacity=
         cache.close()
 
 
+def churn(wl, steps, warmup, every=16, per_event=4, prompt=512):
+    """Serving churn over the static buffer: start with every pair full; every
+    `every` steps, `per_event` sequences (round robin) finish and their slots
+    are recycled for a new request (lf_seq_reset, then lf_prefill_fill of a
+    `prompt`-token prompt with -1 for every other sequence). The reset and
+    prefill calls are inside the timed window. Returns (ms per step, algorithmic
+    bytes per step: decode at the actual fill levels plus the prompts' K and V
+    read and written)."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import device_prefill
+    e = 2 if wl.dtype == "bf16" else 4
+    torch.cuda.empty_cache()
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                          dtype=wl.dtype)
+    try:
+        k, v = device_prefill(wl, wl.budget, seed=11)
+        cache.prefill(0, k, v, np.full(wl.batch, wl.budget, dtype=np.int32))
+        del k, v
+        pk, pv = device_prefill(wl, prompt, seed=12)     # prompts, [batch][prompt][hkv][d]
+        ring = make_ring(wl, wl.dtype)
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=ring[0][0].dtype,
+                          device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        fill = np.full(wl.batch, wl.budget, dtype=np.int64)
+        nbytes = 0
+        nxt = 0
+
+        def one(t, count):
+            nonlocal nxt, nbytes
+            if t % every == every - 1:
+                seqs = [(nxt + i) % wl.batch for i in range(per_event)]
+                nxt = (nxt + per_event) % wl.batch
+                cache.seq_reset(seqs)
+                n = np.full(wl.batch, -1, dtype=np.int32)
+                n[seqs] = prompt
+                cache.prefill(0, pk, pv, n)
+                fill[seqs] = prompt
+                if count:
+                    nbytes += len(seqs) * wl.num_kv_heads * prompt * (4 * wl.head_dim * e + 4)
+            q, kn, vn = ring[t % RING]
+            cache.decode_step(0, q, kn, vn, out, ev)
+            if count:
+                nbytes += wl.num_kv_heads * sum(
+                    algorithmic_bytes_per_pair(int(nb), wl.group, wl.head_dim, e, nb >= wl.budget)
+                    for nb in fill)
+            np.minimum(fill + 1, wl.budget, out=fill)
+
+        for t in range(warmup):
+            one(t, False)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for t in range(warmup, warmup + steps):
+            one(t, True)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps, nbytes / steps
+    finally:
+        cache.close()
+
+
 def suite(args):
     """One JSON line per workload shape (steady state unless stated)."""
     import torch
@@ -253,6 +316,15 @@ def suite(args):
         emit(f"llama8b_layer fill {fill} (appending)", wl3, ms, nb)
     ms, nb = steady_state(wl3, steps, warmup)
     emit("llama8b_layer steady state", wl3, ms, nb)
+    for label, kw in (("deferred order (the blog engine's)", dict(order="deferred")),
+                      ("one victim per sequence", dict(scope="sequence")),
+                      ("one victim per sequence, deferred order", dict(scope="sequence", order="deferred")),
+                      ("l2 score", dict(norm="l2"))):
+        ms, nb = steady_state(wl3, steps, warmup, **kw)
+        emit(f"llama8b_layer steady state, {label}", wl3, ms, nb, extra={"variant": kw})
+    ms, nb = churn(wl3, min(steps, 256), warmup)
+    emit("llama8b_layer churn: 4 sequences recycled every 16 steps (512-token prompts)", wl3, ms, nb,
+         extra={"note": "reset + prefill inside the timed window; bytes include the prompts"})
     shard = wl3.with_(num_q_heads=4, num_kv_heads=1)
     ms, nb = steady_state(shard, steps, warmup)
     emit("llama8b_layer tp8 shard (1 KV head per GPU)", shard, ms, nb)
