@@ -45,7 +45,7 @@ struct SplitWork {
   int32_t* arrive;    // [pairs]
   // One victim per sequence: every pair's score vector and, per sequence, an
   // arrival counter of its KV heads (zero between launches).
-  float* score;       // [pairs][slots_pad]
+  float* score;       // [batch][slots_pad][num_kv_heads]
   int32_t* seq_arrive;  // [batch]
 };
 

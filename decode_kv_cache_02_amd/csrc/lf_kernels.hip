@@ -268,7 +268,8 @@ struct DecodeParams {
   float* ws_logit;      // [pairs][slots_pad][G]: raw logits (cache full only)
   int32_t* arrive;      // [pairs]: arrivals, back to 0 after every launch
   // One victim per sequence.
-  float* ws_score;      // [pairs][slots_pad]: each pair's score vector
+  float* ws_score;      // [batch][slots_pad][num_kv_heads]: every head's score of a slot
+                        // side by side, so one thread gathers a slot's heads at once
   int32_t* seq_arrive;  // [batch]: KV heads done, back to 0 after every launch
 };
 
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   const __amdgpu_buffer_rsrc_t rN =
       make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(hi) * 4u);
   float vnb[kScoreBatch];
-  if (!SPLIT && scoring) {
+  if (!SPLIT && scoring && !shared) {
 #pragma unroll
     for (int k = 0; k < kScoreBatch; ++k)
       vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
@@ -618,12 +619,10 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     // ---------------- Phase C: score + argmin ----------------
     // One workgroup per pair: runs while the first V rows are in flight.
     // Only an evicting cache scores, and then the whole buffer is one chunk,
-    // so M and L are final here. With one victim per sequence the scores are
-    // also published for the sequence's last KV head to sum.
-    if (!SPLIT && EVICT && scoring) {
-      const __amdgpu_buffer_rsrc_t rSc =
-          make_rsrc(shared ? P.ws_score + static_cast<int64_t>(pair) * slots_pad : nullptr,
-                    shared ? static_cast<uint32_t>(n) * 4u : 0u);
+    // so M and L are final here. (With one victim per sequence the scores are
+    // computed after the V pass instead, where publishing them does not slow
+    // the transition.)
+    if (!SPLIT && EVICT && scoring && !shared) {
       float inv_l[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
@@ -644,10 +643,6 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
 #pragma unroll
             for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
             sc = sc * vnb[k];
-            if (shared) {
-              const float one[1] = {sc};
-              ws_store_g<1>(rSc, static_cast<uint32_t>(i) * 4u, one);
-            }
             if (sc < best) {  // slots visited in increasing order: first minimum kept
               best = sc;
               best_i = i;
@@ -720,6 +715,39 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       o = fmaf(w_run[g], to_f32(vn[d]), o);
       from_f32(o / l_run[g], out + g * D + d);
     }
+    if (EVICT && scoring && shared) {
+      // One victim per sequence: this head's score vector, from the p still
+      // in LDS, with the operations of the score phase (bit-equal results),
+      // published for the sequence's deciding workgroup.
+      float inv_l[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
+      const __amdgpu_buffer_rsrc_t rSc = make_rsrc(
+          P.ws_score + static_cast<int64_t>(b) * slots_pad * P.num_kv_heads + h,
+          static_cast<uint32_t>(n) * P.num_kv_heads * 4u);
+      constexpr int kPubBatch = 8;
+      for (int i0 = P.sink + tid; i0 < n; i0 += NT * kPubBatch) {
+        float vb[kPubBatch];
+#pragma unroll
+        for (int k = 0; k < kPubBatch; ++k)
+          vb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rN, static_cast<int>((i0 + k * NT) * 4), 0, 0));
+#pragma unroll
+        for (int k = 0; k < kPubBatch; ++k) {
+          const int i = i0 + k * NT;
+          if (i < n && i != masked) {
+            float p[G];
+            lds_get<G>(lds, i, p);
+            float sc = p[0] * inv_l[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
+            sc = sc * vb[k];
+            const float one[1] = {sc};
+            ws_store_g<1>(rSc, static_cast<uint32_t>(i) * P.num_kv_heads * 4u, one);
+          }
+        }
+      }
+    }
   } else {
     // ---------------- Split: publish this split's partial state ----------------
     constexpr int kPart = 2 * G + G * D;
@@ -779,9 +807,9 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
         inv_l[g] = 1.0f / sh_gl[g];
         gm[g] = sh_gm[g];
       }
-      const __amdgpu_buffer_rsrc_t rSc =
-          make_rsrc(shared ? P.ws_score + static_cast<int64_t>(pair) * slots_pad : nullptr,
-                    shared ? static_cast<uint32_t>(n) * 4u : 0u);
+      const __amdgpu_buffer_rsrc_t rSc = make_rsrc(
+          shared ? P.ws_score + static_cast<int64_t>(b) * slots_pad * P.num_kv_heads + h : nullptr,
+          shared ? static_cast<uint32_t>(n) * P.num_kv_heads * 4u : 0u);
       const __amdgpu_buffer_rsrc_t rL = make_rsrc(
           P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(n) * G * 4u);
       const __amdgpu_buffer_rsrc_t rNa =
@@ -809,7 +837,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
             sc = sc * vb[k];
             if (shared) {
               const float one[1] = {sc};
-              ws_store_g<1>(rSc, static_cast<uint32_t>(i) * 4u, one);
+              ws_store_g<1>(rSc, static_cast<uint32_t>(i) * P.num_kv_heads * 4u, one);
             }
             if (sc < best) {
               best = sc;
@@ -854,20 +882,46 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       if (decider) {
         const int hk = P.num_kv_heads;
         const __amdgpu_buffer_rsrc_t rS = make_rsrc(
-            P.ws_score + static_cast<int64_t>(b) * hk * slots_pad,
+            P.ws_score + static_cast<int64_t>(b) * slots_pad * hk,
             static_cast<uint32_t>(hk) * static_cast<uint32_t>(slots_pad) * 4u);
-        constexpr int kSeqBatch = 8;
+        // Slot i's head scores sit at [i][0..hk): with hk a multiple of 4 a
+        // thread fetches 8 heads of each of its kSeqBatch slots with 16-byte
+        // loads all in flight together, then sums them in head order.
+        constexpr int kSeqBatch = 4;
+        const bool vec4 = (hk & 3) == 0;
         float sbest = INFINITY;
         int sbest_i = 0x7fffffff;
         for (int i0 = P.sink + tid; i0 < n; i0 += NT * kSeqBatch) {
           float tot[kSeqBatch];
-          for (int hh = 0; hh < hk; ++hh) {
-            float x[kSeqBatch][1];
 #pragma unroll
-            for (int k = 0; k < kSeqBatch; ++k)
-              ws_load_g<1>(rS, (static_cast<uint32_t>(hh) * slots_pad + i0 + k * NT) * 4u, x[k]);
+          for (int k = 0; k < kSeqBatch; ++k) tot[k] = 0.0f;
+          if (vec4) {
+            for (int c0 = 0; c0 < hk; c0 += 8) {
+              u32x4_t x[kSeqBatch][2];
 #pragma unroll
-            for (int k = 0; k < kSeqBatch; ++k) tot[k] = hh == 0 ? x[k][0] : tot[k] + x[k][0];
+              for (int k = 0; k < kSeqBatch; ++k)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                  x[k][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                      rS, static_cast<int>((static_cast<uint32_t>(i0 + k * NT) * hk + c0 + 4 * j) * 4u),
+                      0, kDeviceScope);
+#pragma unroll
+              for (int k = 0; k < kSeqBatch; ++k)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                  if (c0 + 4 * j < hk)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) tot[k] += __uint_as_float(x[k][j][r]);
+            }
+          } else {
+            for (int hh = 0; hh < hk; ++hh) {
+              float x[kSeqBatch][1];
+#pragma unroll
+              for (int k = 0; k < kSeqBatch; ++k)
+                ws_load_g<1>(rS, (static_cast<uint32_t>(i0 + k * NT) * hk + hh) * 4u, x[k]);
+#pragma unroll
+              for (int k = 0; k < kSeqBatch; ++k) tot[k] += x[k][0];
+            }
           }
 #pragma unroll
           for (int k = 0; k < kSeqBatch; ++k) {
