@@ -45,7 +45,8 @@ struct SplitWork {
   int32_t* arrive;    // [pairs]
   // One victim per sequence: every pair's score vector and, per sequence, an
   // arrival counter of its KV heads (zero between launches).
-  float* score;       // [batch][slots_pad][num_kv_heads]
+  float* score;       // [batch][num_kv_heads][slots_pad]
+  float* new_norm;    // [batch][num_kv_heads]: ||v_new|| of every head
   int32_t* seq_arrive;  // [batch]
 };
 
@@ -57,6 +58,7 @@ constexpr int kMinSplitSlots = 256;   // fewer slots per split are not worth a s
 // Dynamic LDS bytes the decode kernel needs for this geometry, or 0 if the
 // combination (dtype, head_dim, group, slots) is not built.
 size_t decode_lds_bytes(const Geometry& g);
+size_t decode_score_lds_bytes(const Geometry& g);  // part of decode_lds_bytes
 size_t decode_lds_bytes_for(const Geometry& g, int waves);
 size_t decode_split_lds_bytes(const Geometry& g, int splits);
 size_t split_part_floats(const Geometry& g);

@@ -268,8 +268,8 @@ struct DecodeParams {
   float* ws_logit;      // [pairs][slots_pad][G]: raw logits (cache full only)
   int32_t* arrive;      // [pairs]: arrivals, back to 0 after every launch
   // One victim per sequence.
-  float* ws_score;      // [batch][slots_pad][num_kv_heads]: every head's score of a slot
-                        // side by side, so one thread gathers a slot's heads at once
+  float* ws_score;      // [batch][num_kv_heads][slots_pad]: every head's score vector
+  float* ws_nnorm;      // [batch][num_kv_heads]: every head's ||v_new||
   int32_t* seq_arrive;  // [batch]: KV heads done, back to 0 after every launch
 };
 
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   const __amdgpu_buffer_rsrc_t rN =
       make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(hi) * 4u);
   float vnb[kScoreBatch];
-  if (!SPLIT && scoring && !shared) {
+  if (!SPLIT && scoring) {
 #pragma unroll
     for (int k = 0; k < kScoreBatch; ++k)
       vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
@@ -619,10 +619,10 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
     // ---------------- Phase C: score + argmin ----------------
     // One workgroup per pair: runs while the first V rows are in flight.
     // Only an evicting cache scores, and then the whole buffer is one chunk,
-    // so M and L are final here. (With one victim per sequence the scores are
-    // computed after the V pass instead, where publishing them does not slow
-    // the transition.)
-    if (!SPLIT && EVICT && scoring && !shared) {
+    // so M and L are final here. With one victim per sequence the scores go
+    // to LDS and are published after the V pass (a global store here would
+    // slow the transition).
+    if (!SPLIT && EVICT && scoring) {
       float inv_l[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
@@ -643,6 +643,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
 #pragma unroll
             for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
             sc = sc * vnb[k];
+            if (shared) lds[P.chunk * G + i] = sc;
             if (sc < best) {  // slots visited in increasing order: first minimum kept
               best = sc;
               best_i = i;
@@ -716,37 +717,18 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       from_f32(o / l_run[g], out + g * D + d);
     }
     if (EVICT && scoring && shared) {
-      // One victim per sequence: this head's score vector, from the p still
-      // in LDS, with the operations of the score phase (bit-equal results),
-      // published for the sequence's deciding workgroup.
-      float inv_l[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
+      // One victim per sequence: publish this head's score vector (in LDS
+      // since the score phase) and its new token's norm for the sequence's
+      // deciding workgroup. Whole 16-byte groups; entries the score phase
+      // skipped (sinks, the replaced slot) are never read back.
+      const float* lsc = lds + P.chunk * G;
       const __amdgpu_buffer_rsrc_t rSc = make_rsrc(
-          P.ws_score + static_cast<int64_t>(b) * slots_pad * P.num_kv_heads + h,
-          static_cast<uint32_t>(n) * P.num_kv_heads * 4u);
-      constexpr int kPubBatch = 8;
-      for (int i0 = P.sink + tid; i0 < n; i0 += NT * kPubBatch) {
-        float vb[kPubBatch];
-#pragma unroll
-        for (int k = 0; k < kPubBatch; ++k)
-          vb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              rN, static_cast<int>((i0 + k * NT) * 4), 0, 0));
-#pragma unroll
-        for (int k = 0; k < kPubBatch; ++k) {
-          const int i = i0 + k * NT;
-          if (i < n && i != masked) {
-            float p[G];
-            lds_get<G>(lds, i, p);
-            float sc = p[0] * inv_l[0];
-#pragma unroll
-            for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
-            sc = sc * vb[k];
-            const float one[1] = {sc};
-            ws_store_g<1>(rSc, static_cast<uint32_t>(i) * P.num_kv_heads * 4u, one);
-          }
-        }
+          P.ws_score + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(slots_pad) * 4u);
+      for (int q4 = tid; 4 * q4 < n; q4 += NT) {
+        const u32x4_t v4 = *reinterpret_cast<const u32x4_t*>(lsc + 4 * q4);
+        __builtin_amdgcn_raw_buffer_store_b128(v4, rSc, 16 * q4, 0, kDeviceScope);
       }
+      if (tid == 0) ws_store(P.ws_nnorm + pair, sh_vn_new);
     }
   } else {
     // ---------------- Split: publish this split's partial state ----------------
@@ -807,9 +789,9 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
         inv_l[g] = 1.0f / sh_gl[g];
         gm[g] = sh_gm[g];
       }
-      const __amdgpu_buffer_rsrc_t rSc = make_rsrc(
-          shared ? P.ws_score + static_cast<int64_t>(b) * slots_pad * P.num_kv_heads + h : nullptr,
-          shared ? static_cast<uint32_t>(n) * P.num_kv_heads * 4u : 0u);
+      const __amdgpu_buffer_rsrc_t rSc =
+          make_rsrc(shared ? P.ws_score + static_cast<int64_t>(pair) * slots_pad : nullptr,
+                    shared ? static_cast<uint32_t>(n) * 4u : 0u);
       const __amdgpu_buffer_rsrc_t rL = make_rsrc(
           P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(n) * G * 4u);
       const __amdgpu_buffer_rsrc_t rNa =
@@ -837,7 +819,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
             sc = sc * vb[k];
             if (shared) {
               const float one[1] = {sc};
-              ws_store_g<1>(rSc, static_cast<uint32_t>(i) * P.num_kv_heads * 4u, one);
+              ws_store_g<1>(rSc, static_cast<uint32_t>(i) * 4u, one);
             }
             if (sc < best) {
               best = sc;
@@ -852,6 +834,7 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
         sh_best_slot[wave] = best_i;
       }
     }
+    if (shared && scoring && tid == 0) ws_store(P.ws_nnorm + pair, sh_vn_new);
     if (tid == 0) __hip_atomic_store(P.arrive + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -862,6 +845,8 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
   // argmin. choice = -1 when there is no candidate.
   int choice = -1;
   bool decider = !shared;
+  u32x4_t pre = {0u, 0u, 0u, 0u};  // one victim per sequence: prefetched new-token data
+  float pre_norm = 0.0f;
   if (scoring) {
     if (!shared) {
       __syncthreads();  // every wave's best visible
@@ -881,56 +866,63 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
       decider = sh_ticket == P.num_kv_heads - 1;
       if (decider) {
         const int hk = P.num_kv_heads;
+        // Prefetch what the write of every head needs (same-step order):
+        // this thread's first 16-byte chunk of a new row and, for tid < hk,
+        // head tid's published ||v_new||.
+        if (!deferred) {
+          if (tid < hk * 2 * kRowLoads) {
+            const int hh = tid / (2 * kRowLoads);
+            const int j = tid - hh * (2 * kRowLoads);
+            const int64_t pr = static_cast<int64_t>(b) * hk + hh;
+            pre = j < kRowLoads ? load16(static_cast<const T*>(P.k_new) + pr * D + j * EPL)
+                                : load16(static_cast<const T*>(P.v_new) + pr * D + (j - kRowLoads) * EPL);
+          }
+          if (tid < hk) pre_norm = ws_load(P.ws_nnorm + static_cast<int64_t>(b) * hk + tid);
+        }
+        // Head h's scores of slots 4q..4q+3 are one 16-byte load; a thread
+        // has up to 8 heads x kQuadBatch such loads in flight, then sums the
+        // heads in order.
         const __amdgpu_buffer_rsrc_t rS = make_rsrc(
-            P.ws_score + static_cast<int64_t>(b) * slots_pad * hk,
+            P.ws_score + static_cast<int64_t>(b) * hk * slots_pad,
             static_cast<uint32_t>(hk) * static_cast<uint32_t>(slots_pad) * 4u);
-        // Slot i's head scores sit at [i][0..hk): with hk a multiple of 4 a
-        // thread fetches 8 heads of each of its kSeqBatch slots with 16-byte
-        // loads all in flight together, then sums them in head order.
-        constexpr int kSeqBatch = 4;
-        const bool vec4 = (hk & 3) == 0;
+        constexpr int kQuadBatch = 2;
         float sbest = INFINITY;
         int sbest_i = 0x7fffffff;
-        for (int i0 = P.sink + tid; i0 < n; i0 += NT * kSeqBatch) {
-          float tot[kSeqBatch];
+        for (int q0 = tid; 4 * q0 < n; q0 += NT * kQuadBatch) {
+          float tot[kQuadBatch][4];
 #pragma unroll
-          for (int k = 0; k < kSeqBatch; ++k) tot[k] = 0.0f;
-          if (vec4) {
-            for (int c0 = 0; c0 < hk; c0 += 8) {
-              u32x4_t x[kSeqBatch][2];
+          for (int kb = 0; kb < kQuadBatch; ++kb)
 #pragma unroll
-              for (int k = 0; k < kSeqBatch; ++k)
+            for (int r = 0; r < 4; ++r) tot[kb][r] = 0.0f;
+          for (int h0 = 0; h0 < hk; h0 += 8) {
+            u32x4_t x[8][kQuadBatch];
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                  x[k][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                      rS, static_cast<int>((static_cast<uint32_t>(i0 + k * NT) * hk + c0 + 4 * j) * 4u),
-                      0, kDeviceScope);
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
-              for (int k = 0; k < kSeqBatch; ++k)
+              for (int kb = 0; kb < kQuadBatch; ++kb)
+                x[j][kb] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rS,
+                    static_cast<int>((static_cast<uint32_t>(min(h0 + j, hk - 1)) * slots_pad +
+                                      4u * static_cast<uint32_t>(q0 + kb * NT)) * 4u),
+                    0, kDeviceScope);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                  if (c0 + 4 * j < hk)
+            for (int j = 0; j < 8; ++j)
+              if (h0 + j < hk)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) tot[k] += __uint_as_float(x[k][j][r]);
-            }
-          } else {
-            for (int hh = 0; hh < hk; ++hh) {
-              float x[kSeqBatch][1];
+                for (int kb = 0; kb < kQuadBatch; ++kb)
 #pragma unroll
-              for (int k = 0; k < kSeqBatch; ++k)
-                ws_load_g<1>(rS, (static_cast<uint32_t>(i0 + k * NT) * hk + hh) * 4u, x[k]);
-#pragma unroll
-              for (int k = 0; k < kSeqBatch; ++k) tot[k] += x[k][0];
-            }
+                  for (int r = 0; r < 4; ++r) tot[kb][r] += __uint_as_float(x[j][kb][r]);
           }
 #pragma unroll
-          for (int k = 0; k < kSeqBatch; ++k) {
-            const int i = i0 + k * NT;
-            if (i < n && i != masked && tot[k] < sbest) {
-              sbest = tot[k];
-              sbest_i = i;
+          for (int kb = 0; kb < kQuadBatch; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 4 * (q0 + kb * NT) + r;
+              if (i >= P.sink && i < n && i != masked && tot[kb][r] < sbest) {
+                sbest = tot[kb][r];
+                sbest_i = i;
+              }
             }
-          }
         }
         wave_argmin(sbest, sbest_i);
         if (lane == 0) {
@@ -972,19 +964,15 @@ __global__ __launch_bounds__(WAVES * kWave, (WAVES + 1) / 2) void decode_kernel(
           if (j < kRowLoads) {
             char* Kh = reinterpret_cast<char*>(static_cast<T*>(P.kc_w) + pr * P.pair_elems);
             store16(Kh + k_chunk_offset<kRowBytes>(choice, j),
-                    load16(static_cast<const T*>(P.k_new) + pr * D + j * EPL));
+                    idx == tid ? pre : load16(static_cast<const T*>(P.k_new) + pr * D + j * EPL));
           } else {
             T* Vh = static_cast<T*>(P.vc_w) + pr * P.pair_elems + static_cast<int64_t>(choice) * D;
             store16(Vh + (j - kRowLoads) * EPL,
-                    load16(static_cast<const T*>(P.v_new) + pr * D + (j - kRowLoads) * EPL));
+                    idx == tid ? pre
+                               : load16(static_cast<const T*>(P.v_new) + pr * D + (j - kRowLoads) * EPL));
           }
         }
-        for (int hh = wave; hh < hk; hh += WAVES) {
-          const int64_t pr = static_cast<int64_t>(b) * hk + hh;
-          const float nrm = wave_norm<T, D>(static_cast<const T*>(P.v_new) + pr * D, lane,
-                                            P.norm_l2 != 0);
-          if (lane == 0) P.vnorm[pr * slots_pad + choice] = nrm;
-        }
+        if (tid < hk) P.vnorm[(static_cast<int64_t>(b) * hk + tid) * slots_pad + choice] = pre_norm;
       }
       for (int hh = tid; hh < hk; hh += NT) P.evicted[static_cast<int64_t>(b) * hk + hh] = choice;
       return;
@@ -1133,6 +1121,7 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   P.shared = geo.scope == 1;
   P.norm_l2 = geo.norm == 1;
   P.ws_score = W.score;
+  P.ws_nnorm = W.new_norm;
   P.seq_arrive = W.seq_arrive;
   const int pairs = geo.batch * geo.num_kv_heads;
   P.pairs = pairs;
@@ -1142,7 +1131,10 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   P.arrive = W.arrive;
   const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits) : decode_lds_bytes(geo);
   if (lds == 0) return hipErrorInvalidValue;
-  P.chunk = static_cast<int32_t>(lds / (sizeof(float) * G));  // EVICT: a whole split (or pair)
+  // One workgroup per pair with one victim per sequence: the pair's scores
+  // follow the logits in LDS.
+  const size_t score_lds = !SPLIT ? decode_score_lds_bytes(geo) : 0;
+  P.chunk = static_cast<int32_t>((lds - score_lds) / (sizeof(float) * G));  // EVICT: a whole split (or pair)
   auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1204,7 +1196,16 @@ size_t decode_lds_bytes_for(const Geometry& g, int waves) {
   return slots * g.group * sizeof(float);
 }
 
-size_t decode_lds_bytes(const Geometry& g) { return decode_lds_bytes_for(g, kDecodeWaves); }
+size_t decode_score_lds_bytes(const Geometry& g) {
+  return g.mode == 0 && g.scope == 1 ? static_cast<size_t>(g.slots_pad) * sizeof(float) : 0;
+}
+
+size_t decode_lds_bytes(const Geometry& g) {
+  const size_t logits = decode_lds_bytes_for(g, kDecodeWaves);
+  if (logits == 0) return 0;
+  const size_t total = logits + decode_score_lds_bytes(g);
+  return total > kEvictLdsCap ? 0 : total;
+}
 
 size_t decode_split_lds_bytes(const Geometry& g, int splits) {
   if (decode_lds_bytes(g) == 0 || splits < 1) return 0;

@@ -52,7 +52,7 @@ constexpr int kSlotAlign = 64;
 
 struct Layout {
   size_t k_off, v_off, vn_off, fill_off, victim_off, part_off, logit_off, arrive_off, score_off,
-      seq_arrive_off, total;
+      seq_arrive_off, new_norm_off, total;
   int32_t slots_pad;
   int64_t pair_elems;
 };
@@ -153,6 +153,8 @@ lf_status layout(const lf_config* c, int32_t max_splits, Layout* L) {
   L->seq_arrive_off = t;
   if (!add_ok(L->seq_arrive_off, align_up(shared ? static_cast<size_t>(c->batch) * 4 : 0), &t))
     return LF_ERR_UNSUPPORTED;
+  L->new_norm_off = t;
+  if (!add_ok(L->new_norm_off, align_up(shared ? layer_pairs * 4 : 0), &t)) return LF_ERR_UNSUPPORTED;
   L->total = t;
   return LF_OK;
 }
@@ -286,6 +288,7 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->work.arrive = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.arrive_off);
   c->work.score = reinterpret_cast<float*>(static_cast<char*>(base) + L.score_off);
   c->work.seq_arrive = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.seq_arrive_off);
+  c->work.new_norm = reinterpret_cast<float*>(static_cast<char*>(base) + L.new_norm_off);
   c->max_splits = max_splits;
   c->forced_splits = 0;
   *out = c;
