@@ -30,7 +30,8 @@ if ROOT not in sys.path:
 
 METRIC = "fused decode+evict steps/sec (tokens/s) and achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, AMD public specification
-KERNEL_SOURCE = os.path.join(ROOT, "decode_kv_cache_02_amd", "csrc", "lf_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_kv_cache_02_amd", "csrc", f)
+                  for f in ("lf_decode.h", "lf_decode_w4.hip", "lf_decode_w8.hip", "lf_kernels.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama8b_layer.json")
 RING = 64
 
@@ -51,8 +52,12 @@ def algorithmic_bytes_per_pair(n: int, G: int, d: int, e: int, evict: bool) -> i
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the kernel sources (decode kernel, its instances, fill)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(bytes_alg_per_launch: float):

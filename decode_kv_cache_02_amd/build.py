@@ -11,14 +11,18 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "liblongflow.so")
-SOURCES = ("lf_kernels.hip", "lf_runtime.cpp")
+SOURCES = ("lf_decode_w4.hip", "lf_decode_w8.hip", "lf_kernels.hip", "lf_runtime.cpp")
+HEADERS = ("lf_decode.h", "lf_internal.h")
 ARCH = os.environ.get("LONGFLOW_OFFLOAD_ARCH", "gfx950")
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def hipcc() -> str:
@@ -28,28 +32,44 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the LongFlow HIP library cannot be built")
 
 
-def compile_command(out_path: str) -> list:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-Wall", "-Wno-unused-function",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", INCLUDE,
-        *[os.path.join(CSRC, s) for s in SOURCES],
-        "-o", out_path,
-    ]
+def compile_commands(obj_dir: str) -> list:
+    """One hipcc -c per source (they build in parallel)."""
+    return [[hipcc(), f"--offload-arch={ARCH}", *FLAGS, "-I", INCLUDE, "-c",
+             os.path.join(CSRC, src), "-o", os.path.join(obj_dir, src + ".o")]
+            for src in SOURCES]
+
+
+def link_command(obj_dir: str, out_path: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+            *[os.path.join(obj_dir, src + ".o") for src in SOURCES], "-o", out_path]
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and res.stderr.strip():
-        sys.stderr.write(res.stderr)
+    with tempfile.TemporaryDirectory(prefix="longflow_build_") as obj_dir:
+        procs = []
+        for cmd in compile_commands(obj_dir):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                          text=True))
+        failed = False
+        for p in procs:
+            out, err = p.communicate()
+            if p.returncode != 0:
+                failed = True
+                sys.stderr.write(out + err)
+            elif verbose and err.strip():
+                sys.stderr.write(err)
+        if failed:
+            raise RuntimeError("hipcc failed")
+        tmp = LIB_PATH + ".tmp"
+        cmd = link_command(obj_dir, tmp)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -67,10 +67,22 @@ size_t split_part_floats(const Geometry& g);
 size_t device_lds_limit();
 
 // splits == 1: one workgroup per pair. splits > 1: split-K over `splits`
-// workgroups per pair (W must then hold room for that many).
-hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
+// workgroups per pair (W must then hold room for that many). waves: 4 or 8
+// waves of 64 lanes per workgroup (8 when one workgroup per CU is all the
+// launch has).
+hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits, int waves,
                          const void* q, const void* k_new, const void* v_new, void* out,
                          int32_t* evicted, hipStream_t stream);
+hipError_t launch_decode_w4(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
+                            const void* q, const void* k_new, const void* v_new, void* out,
+                            int32_t* evicted, hipStream_t stream);
+hipError_t launch_decode_w8(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
+                            const void* q, const void* k_new, const void* v_new, void* out,
+                            int32_t* evicted, hipStream_t stream);
+
+// Static LDS of a decode workgroup of `waves` waves (per-wave output
+// partials and reduction scratch), an upper bound.
+size_t decode_static_lds_bytes(const Geometry& g, int waves);
 
 // Copies rows [0, n_b) of each sequence into slots 0..n_b-1 and clears the
 // rest; n_host is a host array of `count` lengths for sequences

@@ -43,6 +43,9 @@ struct lf_cache {
   lf::SplitWork work;              // split-K workspace (shared by the layers)
   int32_t max_splits;              // 1: no split launches
   int32_t forced_splits;           // 0: plan automatically
+  int32_t forced_waves;            // 0: plan automatically
+  int32_t cus;                     // compute units of the device
+  size_t lds_limit;                // LDS bytes one workgroup may use
 };
 
 namespace {
@@ -191,14 +194,40 @@ lf_status use_device(const lf_cache* c) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Split count of one launch: up to max_splits workgroups per pair, with at
-// least kMinSplitSlots slots per split of the fullest pair; a forced count
-// (lf_cache_set_splits) wins within max_splits.
-int32_t plan_splits(const lf_cache* c, int32_t n_max) {
-  if (c->max_splits <= 1) return 1;
-  if (c->forced_splits > 0) return std::min(c->forced_splits, c->max_splits);
-  const int32_t by_work = std::max(1, n_max / lf::kMinSplitSlots);
-  return std::max(1, std::min(c->max_splits, by_work));
+// Launch shape of one decode step: workgroups per pair (split-K) and waves
+// per workgroup.
+//   - A layer with at least as many pairs as compute units runs one
+//     workgroup per pair.
+//   - With fewer pairs, each pair splits over up to cus / pairs workgroups
+//     (at most max_splits, at least kMinSplitSlots slots per split of the
+//     fullest pair), so the launch holds about one workgroup per CU.
+//   - A launch of at most one workgroup per CU uses 8 waves per workgroup,
+//     otherwise 4 (two workgroups per CU). This needs the 8-wave
+//     workgroup's LDS to fit.
+// A forced split count (lf_cache_set_splits) wins within max_splits.
+struct LaunchShape {
+  int32_t splits;
+  int32_t waves;
+};
+
+LaunchShape plan_launch(const lf_cache* c, int32_t n_max) {
+  const int64_t pairs = c->layer_pairs;
+  int32_t s = 1;
+  if (c->max_splits > 1) {
+    if (c->forced_splits > 0) {
+      s = std::min(c->forced_splits, c->max_splits);
+    } else if (pairs < c->cus) {
+      const int64_t by_grid = std::max<int64_t>(1, c->cus / pairs);
+      const int32_t by_work = std::max(1, n_max / lf::kMinSplitSlots);
+      s = static_cast<int32_t>(std::min<int64_t>({c->max_splits, by_grid, by_work}));
+    }
+  }
+  const size_t dyn = s > 1 ? lf::decode_split_lds_bytes(c->geo, s) : lf::decode_lds_bytes(c->geo);
+  const bool fits8 = dyn + lf::decode_static_lds_bytes(c->geo, 8) <= c->lds_limit;
+  int32_t waves = pairs * s <= c->cus ? 8 : 4;
+  if (c->forced_waves > 0) waves = c->forced_waves;
+  if (waves == 8 && !fits8) waves = 4;
+  return {s, waves};
 }
 
 }  // namespace
@@ -291,6 +320,12 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->work.new_norm = reinterpret_cast<float*>(static_cast<char*>(base) + L.new_norm_off);
   c->max_splits = max_splits;
   c->forced_splits = 0;
+  c->forced_waves = 0;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
+    cus = 256;
+  c->cus = cus;
+  c->lds_limit = lf::device_lds_limit();
   *out = c;
   return LF_OK;
 }
@@ -344,6 +379,12 @@ lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, 
 lf_status lf_cache_set_splits(lf_cache* c, int32_t splits) {
   if (!c || splits < 0) return LF_ERR_INVALID_ARG;
   c->forced_splits = splits;
+  return LF_OK;
+}
+
+lf_status lf_cache_set_waves(lf_cache* c, int32_t waves) {
+  if (!c || (waves != 0 && waves != 4 && waves != 8)) return LF_ERR_INVALID_ARG;
+  c->forced_waves = waves;
   return LF_OK;
 }
 
@@ -424,9 +465,9 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
   const lf::LayerPtrs p = layer_ptrs(c, layer);
   int32_t n_max = 0;
   for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
-  const int32_t splits = plan_splits(c, n_max);
-  if (lf::launch_decode(c->geo, p, c->work, splits, q, k_new, v_new, out, evicted_slot,
-                        static_cast<hipStream_t>(stream)) != hipSuccess) {
+  const LaunchShape shape = plan_launch(c, n_max);
+  if (lf::launch_decode(c->geo, p, c->work, shape.splits, shape.waves, q, k_new, v_new, out,
+                        evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {
     (void)hipGetLastError();
     return LF_ERR_HIP;
   }

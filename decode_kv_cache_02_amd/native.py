@@ -89,6 +89,7 @@ SIGNATURES = [
     ("lf_seq_reset", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                      ctypes.c_void_p]),
     ("lf_cache_set_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    ("lf_cache_set_waves", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_max_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_fill_levels", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_cache_destroy", None, [ctypes.c_void_p]),
@@ -222,6 +223,11 @@ def lf_cache_set_splits(handle: int, splits: int) -> None:
            "lf_cache_set_splits")
 
 
+def lf_cache_set_waves(handle: int, waves: int) -> None:
+    _check(load_library().lf_cache_set_waves(ctypes.c_void_p(handle), int(waves)),
+           "lf_cache_set_waves")
+
+
 def lf_cache_max_splits(handle: int) -> int:
     v = ctypes.c_int32(0)
     _check(load_library().lf_cache_max_splits(ctypes.c_void_p(handle), ctypes.byref(v)),
@@ -310,6 +316,9 @@ class LongFlowCache:
 
     def set_splits(self, splits: int) -> None:
         lf_cache_set_splits(self.handle, splits)
+
+    def set_waves(self, waves: int) -> None:
+        lf_cache_set_waves(self.handle, waves)
 
     @property
     def max_splits(self) -> int:

@@ -198,6 +198,15 @@ lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, 
 lf_status lf_cache_set_splits(lf_cache* c, int32_t splits);
 lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits);
 
+/* Workgroup size of the decode launches. By default a launch that holds at
+ * most one workgroup per compute unit uses 8 waves (512 threads) per
+ * workgroup, and any larger launch 4 waves, two workgroups per compute unit.
+ * 4 or 8 forces that size (8 falls back to 4 where its LDS does not fit); 0
+ * restores the automatic choice. Results do not depend on it except for
+ * float32 rounding of the output. Errors: LF_ERR_INVALID_ARG for other
+ * values. */
+lf_status lf_cache_set_waves(lf_cache* c, int32_t waves);
+
 /* Host-side copy of the fill levels of one layer, [batch] int32 into the
  * caller's HOST array. Tracked on the host from the calls made (no device
  * access, no synchronisation). */

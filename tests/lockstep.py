@@ -65,7 +65,8 @@ def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
                  sink_size: int = 0, seed_offset: int = 0, layer: int = 0,
                  num_layers: int = 1, check_cache_every: int = 0,
                  splits: int = 0, order: str = "same_step", scope: str = "kv_head",
-                 norm: str = "l1", recycle: Optional[dict] = None) -> LockstepReport:
+                 norm: str = "l1", recycle: Optional[dict] = None,
+                 waves: int = 0) -> LockstepReport:
     """Run `steps` decode steps of one layer on the GPU and in the oracle."""
     import torch
     from decode_kv_cache_02_amd.native import LongFlowCache
@@ -76,6 +77,8 @@ def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
                           order=order, scope=scope, norm=norm)
     if splits:
         cache.set_splits(splits)
+    if waves:
+        cache.set_waves(waves)
     deferred = order == "deferred" and mode == "evict"
     try:
         ts = TokenStream(wl, layer=layer, seed_offset=seed_offset)

@@ -45,11 +45,12 @@ def test_tiny_f32_full_trajectory():
     ("f32", 1, 128, 130, 129, 10),
     ("f32", 2, 128, 16, 16, 20),
 ])
-def test_small_shapes_every_pair(dtype, G, d, budget, prefill, steps):
+@pytest.mark.parametrize("waves", [4, 8])
+def test_small_shapes_every_pair(dtype, G, d, budget, prefill, steps, waves):
     wl = WORKLOADS["tiny_f32"].with_(dtype=dtype, batch=3, num_kv_heads=2, num_q_heads=2 * G,
                                      head_dim=d, budget=budget, prefill=prefill, steps=steps)
-    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps}")
-    rep = run_lockstep(wl, steps, check_cache_every=10)
+    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps} waves={waves}")
+    rep = run_lockstep(wl, steps, check_cache_every=10, waves=waves)
     assert rep.steps == steps
 
 
@@ -105,13 +106,15 @@ def test_qwen3_0p6b_layer_sampled_pairs():
     assert rep.evictions == 24 * len(pairs)
 
 
-def test_llama8b_layer_fill_then_evict_sampled_pairs():
-    """Full Llama-8B layer shape; prefill 3270 so the run crosses into eviction."""
+@pytest.mark.parametrize("waves", [0, 8])
+def test_llama8b_layer_fill_then_evict_sampled_pairs(waves):
+    """Full Llama-8B layer shape; prefill 3270 so the run crosses into eviction
+    (0: the automatic launch, 4 waves; 8 forced)."""
     wl = WORKLOADS["llama8b_layer"]
     pairs = [(0, 0), (63, 7), (10, 3), (41, 5), (5, 6), (33, 1), (57, 2), (20, 4)]
     n = np.full(wl.batch, 3270, dtype=np.int32)
-    _say("llama8b_layer full shape (64x32/8x128, B 3277), prefill 3270, 16 steps, 8 pairs")
-    rep = run_lockstep(wl, 16, pairs=pairs, prefill_n=n, check_cache_every=16)
+    _say(f"llama8b_layer full shape (64x32/8x128, B 3277), prefill 3270, 16 steps, 8 pairs, waves {waves}")
+    rep = run_lockstep(wl, 16, pairs=pairs, prefill_n=n, check_cache_every=16, waves=waves)
     assert rep.appends == 7 * len(pairs) and rep.evictions == 9 * len(pairs)
 
 

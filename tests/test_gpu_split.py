@@ -27,12 +27,12 @@ def _gpu():
     yield
 
 
-@pytest.mark.parametrize("splits", [2, 4, 8])
-def test_tiny_f32_split(splits):
+@pytest.mark.parametrize("splits,waves", [(2, 0), (4, 0), (8, 0), (4, 4), (8, 4)])
+def test_tiny_f32_split(splits, waves):
     """B = 64 is 4 tiles: 8 splits leave four of them empty."""
     wl = WORKLOADS["tiny_f32"]
-    _say(f"tiny_f32 256 steps, {splits} splits")
-    rep = run_lockstep(wl, wl.steps, splits=splits, check_cache_every=64)
+    _say(f"tiny_f32 256 steps, {splits} splits, waves {waves}")
+    rep = run_lockstep(wl, wl.steps, splits=splits, check_cache_every=64, waves=waves)
     assert rep.evictions == 256
 
 
@@ -42,11 +42,12 @@ def test_tiny_f32_split(splits):
     ("f32", 4, 64, 200, 150, 60, 2),
     ("bf16", 1, 128, 520, 500, 30, 16),
 ])
-def test_small_shapes_split(dtype, G, d, budget, prefill, steps, splits):
+@pytest.mark.parametrize("waves", [4, 8])
+def test_small_shapes_split(dtype, G, d, budget, prefill, steps, splits, waves):
     wl = WORKLOADS["tiny_f32"].with_(dtype=dtype, batch=3, num_kv_heads=2, num_q_heads=2 * G,
                                      head_dim=d, budget=budget, prefill=prefill, steps=steps)
-    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps} splits={splits}")
-    rep = run_lockstep(wl, steps, splits=splits, check_cache_every=10)
+    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps} splits={splits} waves={waves}")
+    rep = run_lockstep(wl, steps, splits=splits, check_cache_every=10, waves=waves)
     assert rep.steps == steps
 
 
