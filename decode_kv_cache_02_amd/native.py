@@ -314,6 +314,26 @@ class LongFlowCache:
     def seq_reset(self, seqs, stream=None) -> None:
         lf_seq_reset(self.handle, seqs, stream)
 
+    def step_args(self, layer, q, k_new, v_new, out, evicted_slot, stream=None):
+        """Check the tensors once and return the ctypes argument tuple of one
+        lf_decode_step call, for callers that issue the same step many times
+        (the tensors must stay alive and unchanged in shape)."""
+        import torch
+        self._check_tensor(q, (self.batch, self.hq, self.head_dim), "q")
+        self._check_tensor(k_new, (self.batch, self.hkv, self.head_dim), "k_new")
+        self._check_tensor(v_new, (self.batch, self.hkv, self.head_dim), "v_new")
+        self._check_tensor(out, (self.batch, self.hq, self.head_dim), "out")
+        self._check_tensor(evicted_slot, (self.batch, self.hkv), "evicted_slot", torch.int32)
+        return (ctypes.c_void_p(self.handle), int(layer), ctypes.c_void_p(q.data_ptr()),
+                ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(evicted_slot.data_ptr()),
+                ctypes.c_void_p(_stream_ptr(stream)))
+
+    @staticmethod
+    def step_prepared(args) -> None:
+        """One lf_decode_step with arguments from step_args."""
+        _check(load_library().lf_decode_step(*args), "lf_decode_step")
+
     def set_splits(self, splits: int) -> None:
         lf_cache_set_splits(self.handle, splits)
 
