@@ -227,19 +227,26 @@ __device__ __forceinline__ void wave_argmin(float& score, int& slot) {
 }
 
 // ||row||_1 (or ||row||_2 when l2) in float32 in one fixed order, evaluated
-// by a whole wave; the result is lane 0's. The fill and the decode kernels
-// both use this routine, so equal stored rows always get bit-equal sidecar
-// values.
+// by a whole wave from the row's elements lane + k * 64 (already loaded); the
+// result is lane 0's. The fill and the decode kernels both use this routine,
+// so equal stored rows always get bit-equal sidecar values.
 template <typename T, int D>
-__device__ __forceinline__ float wave_norm(const T* row, int lane, bool l2) {
+__device__ __forceinline__ float wave_norm_vals(const T (&v)[D / kWave], bool l2) {
   float x = 0.0f;
 #pragma unroll
   for (int k = 0; k < D / kWave; ++k) {
-    const float v = to_f32(row[lane + k * kWave]);
-    x = l2 ? fmaf(v, v, x) : x + fabsf(v);
+    const float f = to_f32(v[k]);
+    x = l2 ? fmaf(f, f, x) : x + fabsf(f);
   }
   const float s = wave_sum(x);
   return l2 ? sqrtf(s) : s;
+}
+template <typename T, int D>
+__device__ __forceinline__ float wave_norm(const T* row, int lane, bool l2) {
+  T v[D / kWave];
+#pragma unroll
+  for (int k = 0; k < D / kWave; ++k) v[k] = row[lane + k * kWave];
+  return wave_norm_vals<T, D>(v, l2);
 }
 
 struct DecodeParams {
@@ -353,6 +360,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   constexpr int kRowLoads = D * kBytes / 16;
   static_assert(G == 1 || G == 2 || G == 4, "group width");
   static_assert(LPS <= kWave && SPI * LPS == kWave, "row split");
+  static_assert(G <= WAVES, "one wave per query head of the group for the new token");
 
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [chunk][G] logits (-> p)
   __shared__ float sh_red[WAVES][G][D];     // per-wave output partials
@@ -463,23 +471,34 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
           rN, static_cast<int>((sc_lo + tid + k * NT) * 4), 0, 0));
   }
 
-  // Wave 0: the new token's logits and ||v_new||_1 (visible after the first
-  // barrier).
-  if (wave == 0) {
+  // The new token's logits (wave g < G takes query head g) and ||v_new||
+  // (wave 0). Their inputs are requested now and used only after the K
+  // stream, so no wave starts its K tiles late; the results are visible
+  // after the first barrier.
+  T nq[D / kWave], nk[D / kWave], nv[D / kWave];
+  {
+    const int hsel = wave < G ? wave : 0;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int k = 0; k < D / kWave; ++k) {
+      const int d = lane + k * kWave;
+      nq[k] = qg[hsel * D + d];
+      nk[k] = kn[d];
+      nv[k] = vn[d];
+    }
+  }
+  auto new_token = [&]() {
+    if (wave < G) {
       float x = 0.0f;
 #pragma unroll
-      for (int k = 0; k < D / kWave; ++k) {
-        const int d = lane + k * kWave;
-        x = fmaf(to_f32(qg[g * D + d]), to_f32(kn[d]), x);
-      }
+      for (int k = 0; k < D / kWave; ++k) x = fmaf(to_f32(nq[k]), to_f32(nk[k]), x);
       x = wave_sum(x);
-      if (lane == 0) sh_snew[g] = x * P.scale_log2;
+      if (lane == 0) sh_snew[wave] = x * P.scale_log2;
     }
-    const float nrm = wave_norm<T, D>(vn, lane, P.norm_l2 != 0);
-    if (lane == 0) sh_vn_new = nrm;
-  }
+    if (wave == 0) {
+      const float nrm = wave_norm_vals<T, D>(nv, P.norm_l2 != 0);
+      if (lane == 0) sh_vn_new = nrm;
+    }
+  };
 
   // Running softmax state, identical in every thread. One workgroup per
   // pair: the new token opens it with weight exp2(s_new - s_new) = 1. Split:
@@ -571,6 +590,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
       const float m = wave_max(wmax[g]);
       if (lane == 0) sh_part[wave][g] = m;
     }
+    if (c0 == lo) new_token();
     __syncthreads();  // logits, wave maxima and (first chunk) the new token visible
 
     // ---------------- A2: running max, p = exp2(s - M), sums ----------------
@@ -693,6 +713,8 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
     }
     if (c0 + P.chunk < hi) __syncthreads();  // the next chunk overwrites the LDS logits
   }
+
+  if (lo >= hi) new_token();  // no slot for this workgroup: nothing streamed
 
   // ---------------- Phase D: cross-wave output reduction ----------------
 #pragma unroll
