@@ -394,11 +394,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   // The host keeps 0 <= n <= budget (and n < budget in FULL mode); clamping
   // keeps every access inside the pair's region even if that were broken.
   const int n = min(max(P.fill[pair], 0), P.budget);
-  // Reads stop at the n valid rows: rows at or beyond n load as zeros.
   constexpr uint32_t kTileBytes = 16 * kRowBytes;
-  const __amdgpu_buffer_rsrc_t rK =
-      make_rsrc(K, static_cast<uint32_t>((n + 15) >> 4) * kTileBytes);  // whole tiles
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(n) * kRowBytes);
 
   // This workgroup's slots: [lo, hi), whole 16-slot tiles.
   int lo = 0, hi = n;
@@ -419,9 +415,17 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   const int vcol = (lane % LPS) * EPL;
   const int vsub = lane / LPS;
 
-  // First K tiles go out before anything else.
+  // K and V reads of the current chunk [c0, c0 + cn) go through descriptors
+  // that end where the chunk ends (whole tiles for K): the loops below always
+  // request the next register set, and requests past the chunk return zeros
+  // without moving data (so the compiler's load counting stays exact and
+  // both register sets stay in flight).
   int cn = min(P.chunk, hi - lo);
   int ntiles = (cn + 15) >> 4;
+  __amdgpu_buffer_rsrc_t rK = make_rsrc(K, static_cast<uint32_t>((lo + cn + 15) >> 4) * kTileBytes);
+  __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(lo + cn) * kRowBytes);
+
+  // First K tiles go out before anything else.
   u32x4_t kr[UA][kChunks];
   {
     const uint32_t off0 = static_cast<uint32_t>(lo >> 4) * kTileBytes + lane * 16u;
@@ -527,6 +531,8 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
     for (int g = 0; g < G; ++g) wmax[g] = -INFINITY;
     const uint32_t base_off = static_cast<uint32_t>(c0 >> 4) * kTileBytes + lane * 16u;
     if (c0 > lo) {  // first tiles of a later chunk (the first chunk's are already in flight)
+      rK = make_rsrc(K, static_cast<uint32_t>((c0 + cn + 15) >> 4) * kTileBytes);
+      rV = make_rsrc(V, static_cast<uint32_t>(c0 + cn) * kRowBytes);
 #pragma unroll
       for (int u = 0; u < UA; ++u)
 #pragma unroll
@@ -566,10 +572,10 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
     constexpr int kStepA = WAVES * UA;
     u32x4_t kr2[UA][kChunks];
     for (int t0 = wave * UA; t0 < ntiles; t0 += 2 * kStepA) {
-      if (t0 + kStepA < ntiles) load_tiles(kr2, t0 + kStepA);
+      load_tiles(kr2, t0 + kStepA);
       qk_tiles(kr, t0);
-      if (t0 + 2 * kStepA < ntiles) load_tiles(kr, t0 + 2 * kStepA);
-      if (t0 + kStepA < ntiles) qk_tiles(kr2, t0 + kStepA);
+      load_tiles(kr, t0 + 2 * kStepA);
+      qk_tiles(kr2, t0 + kStepA);
     }
 
     // First V rows of the chunk go out before the softmax bookkeeping.
@@ -707,9 +713,9 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
     };
     for (int q0 = wave * UB; q0 < nq; q0 += 2 * kStepB) {
       pv_rows(vr, q0);
-      if (q0 + 2 * kStepB < nq) load_rows(vr, q0 + 2 * kStepB);
-      if (q0 + kStepB < nq) pv_rows(vr2, q0 + kStepB);
-      if (q0 + 3 * kStepB < nq) load_rows(vr2, q0 + 3 * kStepB);
+      load_rows(vr, q0 + 2 * kStepB);
+      pv_rows(vr2, q0 + kStepB);
+      load_rows(vr2, q0 + 3 * kStepB);
     }
     if (c0 + P.chunk < hi) __syncthreads();  // the next chunk overwrites the LDS logits
   }
