@@ -190,11 +190,14 @@ lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, 
                             int32_t* fill, int32_t* victim, void* stream);
 
 /* Split-K tuning. By default each launch picks how many workgroups share a
- * pair: 1 when the layer has 256 pairs or more (one workgroup per pair
- * fills the GPU); otherwise up to 512 / pairs and 16, with at least 256
- * slots per split. A positive `splits` forces that count (clamped to
- * lf_cache_max_splits); 0 restores the automatic choice. Results do not
- * depend on the split count except for float32 rounding of the output. */
+ * pair: 1 when the layer has at least as many pairs as the device has
+ * compute units; otherwise about (compute units / pairs), at most
+ * lf_cache_max_splits and 16, with at least 256 slots per split. The
+ * workspace is sized at create for up to min(16, 512 / pairs) splits when
+ * the layer has fewer than 256 pairs (none otherwise). A positive `splits`
+ * forces that count (clamped to lf_cache_max_splits); 0 restores the
+ * automatic choice. Results do not depend on the split count except for
+ * float32 rounding of the output. */
 lf_status lf_cache_set_splits(lf_cache* c, int32_t splits);
 lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits);
 
