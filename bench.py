@@ -304,6 +304,76 @@ def churn(wl, steps, warmup, every=16, per_event=4, prompt=512):
         cache.close()
 
 
+def stream_read_ceiling(total_bytes: int = 860_160_000, workgroups: int = 512, reps: int = 50):
+    """Attainable streaming-read bandwidth: lf_probe_stream_read (the decode
+    kernel's K/V loads) over `total_bytes`, split like the Llama-8B layer
+    launch (512 workgroups, ~1.68 MB each). Returns GB/s (best of 3)."""
+    import torch
+    from decode_kv_cache_02_amd.native import lf_probe_stream_read
+    unit = 16 * workgroups
+    total_bytes -= total_bytes % unit
+    buf = torch.ones(total_bytes // 2, dtype=torch.int16, device="cuda")
+    sink = torch.empty(workgroups * 256 * 4, dtype=torch.int32, device="cuda")
+    for _ in range(5):
+        lf_probe_stream_read(buf, workgroups, sink)
+    best = 0.0
+    for _ in range(3):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            lf_probe_stream_read(buf, workgroups, sink)
+        end.record()
+        torch.cuda.synchronize()
+        best = max(best, total_bytes / (start.elapsed_time(end) / reps) / 1e6)
+    del buf, sink
+    return best
+
+
+def trajectory(wl, steps: int, prompt: int, mode: str):
+    """A whole generation: every sequence starts from a `prompt`-token prompt
+    and decodes `steps` tokens (LongFlow: fill, then evict at the budget;
+    full-KV: the cache grows to prompt + steps). One event pair around the
+    whole run. Returns (ms per step, algorithmic bytes per step)."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import device_prefill
+    e = 2 if wl.dtype == "bf16" else 4
+    cap = wl.budget if mode == "evict" else prompt + steps + 64
+    torch.cuda.empty_cache()
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, cap,
+                          dtype=wl.dtype, mode=mode)
+    try:
+        k, v = device_prefill(wl, prompt, seed=13)
+        cache.prefill(0, k, v, np.full(wl.batch, prompt, dtype=np.int32))
+        del k, v
+        ring = make_ring(wl, wl.dtype)
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=ring[0][0].dtype,
+                          device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        args = prepared_ring(cache, ring, out, ev)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for t in range(steps):
+            cache.step_prepared(args[t % RING][0])
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        nbytes = 0
+        for t in range(steps):
+            n = prompt + t
+            evict = mode == "evict" and n >= wl.budget
+            if mode == "evict":
+                n = min(n, wl.budget)
+            nbytes += algorithmic_bytes_per_pair(n, wl.group, wl.head_dim, e, evict)
+        return ms, nbytes * wl.batch * wl.num_kv_heads / steps
+    finally:
+        cache.close()
+
+
 def suite(args):
     """One JSON line per workload shape (steady state unless stated)."""
     import torch
@@ -329,6 +399,13 @@ def suite(args):
         emit(f"llama8b_layer fill {fill} (appending)", wl3, ms, nb)
     ms, nb = steady_state(wl3, steps, warmup)
     emit("llama8b_layer steady state", wl3, ms, nb)
+    # a whole 16k-token generation from a 512-token prompt, LongFlow vs full-KV
+    ms_lf, nb_lf = trajectory(wl3, 16384, 512, "evict")
+    ms_fk, nb_fk = trajectory(wl3, 16384, 512, "full")
+    emit("llama8b_layer whole generation: prompt 512 + 16384 tokens, LongFlow", wl3, ms_lf, nb_lf,
+         extra={"steps": 16384, "fill_steps": wl3.budget - 512})
+    emit("llama8b_layer whole generation: prompt 512 + 16384 tokens, full-KV", wl3, ms_fk, nb_fk,
+         extra={"steps": 16384, "speedup_of_longflow": ms_fk / ms_lf})
     for label, kw in (("deferred order (the blog engine's)", dict(order="deferred")),
                       ("one victim per sequence", dict(scope="sequence")),
                       ("one victim per sequence, deferred order", dict(scope="sequence", order="deferred")),
@@ -420,6 +497,8 @@ def main():
         del a, b
 
     cache.close()
+    ceiling = stream_read_ceiling(int(bytes_launch))
+    print(f"[bench] streaming-read ceiling: {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
     full = None
     if not args.no_full_kv:
         full = full_kv_baseline(wl, min(args.steps, 200), 10)
@@ -452,6 +531,11 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_launch,
                      "kernel": "decode_kernel (lf_decode_step)", "kernel_sha": kernel_sha()},
         "cpu_baseline": cpu,
+        "stream_read_ceiling": {
+            "GBs": ceiling, "frac_of_peak": ceiling / HBM_PEAK_GBS,
+            "decode_frac_of_ceiling": achieved / ceiling,
+            "kernel": "lf_probe_stream_read: the decode kernel's 16-byte non-temporal buffer loads, "
+                      "512 workgroups over the same bytes as one launch"},
         "full_kv": full,
     }
     print(json.dumps(line), flush=True)

@@ -1,0 +1,50 @@
+// Streaming-read probe (include/longflow_probe.h): every workgroup reads its
+// own contiguous region once with 16-byte non-temporal buffer loads, the same
+// loads the decode kernel uses for K and V, and XORs what it read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/longflow_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;           // loads in flight per thread
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNonTemporal = 3;      // the decode kernel's K/V cache policy
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* buf, uint32_t region,
+                                                               u32x4_t* sink) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(buf) + static_cast<size_t>(blockIdx.x) * region, 0,
+      static_cast<int>(region), kRsrcWord3);
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (uint32_t off = threadIdx.x * 16u; off < region; off += kThreads * 16u * kUnroll) {
+    u32x4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off + u * kThreads * 16u), 0,
+                                                   kNonTemporal);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  }
+  sink[static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" lf_status lf_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups,
+                                          void* sink, void* stream) {
+  if (!buf || !sink || workgroups < 1) return LF_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 15u))
+    return LF_ERR_INVALID_ARG;
+  const size_t unit = 16u * static_cast<size_t>(workgroups);
+  if (bytes == 0 || bytes % unit) return LF_ERR_INVALID_ARG;
+  const size_t region = bytes / static_cast<size_t>(workgroups);
+  if (region >= (size_t{1} << 31)) return LF_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const char*>(buf),
+                     static_cast<uint32_t>(region), static_cast<u32x4_t*>(sink));
+  return hipGetLastError() == hipSuccess ? LF_OK : LF_ERR_HIP;
+}

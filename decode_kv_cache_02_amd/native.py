@@ -94,6 +94,9 @@ SIGNATURES = [
     ("lf_fill_levels", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_cache_destroy", None, [ctypes.c_void_p]),
     ("lf_status_str", ctypes.c_char_p, [ctypes.c_int]),
+    # include/longflow_probe.h
+    ("lf_probe_stream_read", ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p]),
 ]
 
 _lib = None
@@ -245,6 +248,14 @@ def lf_fill_levels(handle: int, layer: int, batch: int) -> np.ndarray:
 
 def lf_status_str(status: int) -> str:
     return status_str(status)
+
+
+def lf_probe_stream_read(buf, workgroups: int, sink, stream=None) -> None:
+    """Read the device tensor `buf` once (include/longflow_probe.h)."""
+    _check(load_library().lf_probe_stream_read(
+        ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel() * buf.element_size()),
+        int(workgroups), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))),
+        "lf_probe_stream_read")
 
 
 def untile_k(k_tiled, head_dim: int):

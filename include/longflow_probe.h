@@ -1,0 +1,37 @@
+/*
+ * longflow_probe.h -- measurement helper shipped in liblongflow.so.
+ *
+ * Not part of the decode step. It reads a device buffer once with the same
+ * loads the decode kernel uses for K and V (16-byte buffer loads,
+ * non-temporal cache policy) and keeps an XOR of what it read, so a
+ * benchmark can report the streaming-read bandwidth this GPU attains next to
+ * the decode kernel's.
+ */
+#ifndef LONGFLOW_PROBE_H
+#define LONGFLOW_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "longflow.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` bytes of `buf` once: `workgroups` workgroups of 256 threads,
+ * each over its own contiguous region of bytes / workgroups bytes.
+ *   buf         device, 16-byte aligned; bytes a multiple of 16 * workgroups
+ *   sink        device, workgroups * 256 * 16 bytes; receives the XORs
+ *   stream      hipStream_t as void* (NULL = default stream); asynchronous
+ * Errors: LF_ERR_INVALID_ARG on null pointers, misalignment, a size that is
+ * not a multiple of 16 * workgroups, or a region of 2 GiB or more;
+ * LF_ERR_HIP if the launch fails. */
+lf_status lf_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups, void* sink,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LONGFLOW_PROBE_H */

@@ -4,6 +4,7 @@ The library loads, exports every function include/longflow.h declares, and
 rejects bad configurations on the host before touching the device.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -13,12 +14,15 @@ from decode_kv_cache_02_amd import native
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "longflow.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lf_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(lf_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -106,6 +110,7 @@ def test_null_arguments_rejected(lib):
     assert lib.lf_seq_reset(None, None, 0, None) == native.LF_ERR_INVALID_ARG
     assert lib.lf_cache_set_waves(None, 4) == native.LF_ERR_INVALID_ARG
     assert lib.lf_cache_set_splits(None, 2) == native.LF_ERR_INVALID_ARG
+    assert lib.lf_probe_stream_read(None, 16, 1, None, None) == native.LF_ERR_INVALID_ARG
     assert lib.lf_fill_levels(None, 0, None) == native.LF_ERR_INVALID_ARG
     lib.lf_cache_destroy(None)   # no-op
 
