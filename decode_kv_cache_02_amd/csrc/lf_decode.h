@@ -14,20 +14,29 @@
 // design below keeps that property for gfx950:
 //
 //   one workgroup = one pair (sequence, KV head), 4 or 8 waves of 64 lanes
-//   (or, split-K, a range of the pair's 16-slot tiles).
-//   Phase A  K stream: 128-bit loads straight into the B operand of
-//            v_mfma_f32_16x16x32_bf16 (16x16x4 f32 for float32 caches),
-//            with the query group replicated over the 16 A rows, so every
-//            lane ends up with all G logits of one slot. Logits go to LDS.
+//   (split-K: a contiguous range of the pair's 16-slot tiles).
+//   Phase A  K stream. K is stored in 16-slot tiles in MFMA operand order,
+//            so 16-byte loads land straight in the B operand of
+//            v_mfma_f32_16x16x32_bf16 (16x16x4 f32 for float32 caches). The
+//            query group is replicated over the 16 A rows, so each lane
+//            holds all G logits of one slot. Logits go to LDS; two register
+//            sets of tiles are in flight per wave.
 //   A2       group max (new token included), p = exp2(s - M) in place in
 //            LDS, row sums L.
-//   Phase B  V stream: 128-bit loads, 16 lanes per 256-byte row, float32
-//            FMAs against p broadcast from LDS.
-//   Phase C  (cache full) score_i = ||v_i||_1 * sum_g p_{g,i}/L_g from LDS
-//            and the float32 sidecar, then (score, slot) argmin through
-//            wave shuffles and LDS; lowest slot wins ties.
+//   Phase C  (when a victim is chosen) score_i = ||v_i|| * sum_g p_{g,i}/L_g
+//            from LDS and the float32 sidecar, while the first V rows are in
+//            flight; (score, slot) argmin through DPP and LDS, lowest slot
+//            on ties.
+//   Phase B  V stream: 16-byte loads, 16 lanes per 256-byte row, float32
+//            FMAs against p broadcast from LDS; two register sets in flight.
 //   Phase D  cross-wave output reduction, the new token's own term, output
-//            write, then the new token's K/V/||v||_1 written in place.
+//            write, then the new token's K, V and ||v|| written in place.
+//   Split-K  every split publishes its (m, l, o) and, when scoring, its raw
+//            logits; the last split to arrive combines, scores and writes.
+//            No workgroup waits for another.
+//   VAR      the engine's deferred order and one victim per sequence, as
+//            run-time flags of separate instances (the main instance carries
+//            neither).
 //
 // Every cached byte is read once; the score needs no second pass because the
 // probabilities of the whole pair stay in LDS until the argmin is known.
@@ -44,7 +53,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kDecodeWaves = 4;                     // waves per decode workgroup
 constexpr int kStream = 3;                          // cache policy: non-temporal (nt) + sc0
 constexpr size_t kEvictLdsCap = 144 * 1024;        // logits of one pair; the rest is static LDS
 constexpr size_t kFullChunkSlots = 2048;            // FULL mode: slots per LDS-resident chunk

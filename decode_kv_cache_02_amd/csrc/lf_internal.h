@@ -51,15 +51,18 @@ struct SplitWork {
 };
 
 constexpr int kMaxSplits = 16;
-constexpr int kSplitGridTarget = 512;  // split workgroups per layer launch (2 per MI355X CU)
-constexpr int kSplitPairsBelow = 256;  // split only layers with fewer pairs than CUs
+// Split-K workspace sizing (no device query, so that lf_cache_bytes works
+// without a GPU): layers with fewer than kSplitPairsBelow pairs get room for
+// kSplitGridTarget / pairs splits (at most kMaxSplits), which covers the
+// launch plan's CUs / pairs on devices of up to kSplitGridTarget CUs.
+constexpr int kSplitGridTarget = 512;
+constexpr int kSplitPairsBelow = 256;
 constexpr int kMinSplitSlots = 256;   // fewer slots per split are not worth a split
 
 // Dynamic LDS bytes the decode kernel needs for this geometry, or 0 if the
 // combination (dtype, head_dim, group, slots) is not built.
 size_t decode_lds_bytes(const Geometry& g);
 size_t decode_score_lds_bytes(const Geometry& g);  // part of decode_lds_bytes
-size_t decode_lds_bytes_for(const Geometry& g, int waves);
 size_t decode_split_lds_bytes(const Geometry& g, int splits);
 size_t split_part_floats(const Geometry& g);
 

@@ -134,8 +134,10 @@ size_t decode_static_lds_bytes(const Geometry& g, int waves) {
   return static_cast<size_t>(waves) * g.group * g.head_dim * sizeof(float) + 1024;
 }
 
-size_t decode_lds_bytes_for(const Geometry& g, int waves) {
-  (void)waves;  // the per-wave output partials are static LDS
+// Logits of one LDS-resident chunk: the whole pair when evicting (the score
+// needs every slot's probabilities), 2048-slot chunks in FULL mode; 0 when
+// the combination is not built or does not fit.
+size_t decode_logit_lds_bytes(const Geometry& g) {
   if (g.head_dim != 64 && g.head_dim != 128) return 0;
   if (g.group != 1 && g.group != 2 && g.group != 4) return 0;
   if (g.dtype != 0 && g.dtype != 1) return 0;
@@ -152,7 +154,7 @@ size_t decode_score_lds_bytes(const Geometry& g) {
 }
 
 size_t decode_lds_bytes(const Geometry& g) {
-  const size_t logits = decode_lds_bytes_for(g, kDecodeWaves);
+  const size_t logits = decode_logit_lds_bytes(g);
   if (logits == 0) return 0;
   const size_t total = logits + decode_score_lds_bytes(g);
   return total > kEvictLdsCap ? 0 : total;

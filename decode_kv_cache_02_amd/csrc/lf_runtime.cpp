@@ -163,10 +163,9 @@ lf_status layout(const lf_config* c, int32_t max_splits, Layout* L) {
 }
 
 // Largest split count a cache can use (sizes its workspace): none once the
-// layer has kSplitPairsBelow pairs (one workgroup per pair already fills the
-// GPU), else a layer grid of about kSplitGridTarget workgroups, capped.
-// Decided from the configuration alone, so that lf_cache_bytes needs no
-// device.
+// layer has kSplitPairsBelow pairs, else kSplitGridTarget / pairs, capped at
+// kMaxSplits. Decided from the configuration alone, so that lf_cache_bytes
+// needs no device.
 int32_t max_splits_for(const lf_config* c) {
   const int64_t pairs = static_cast<int64_t>(c->batch) * c->num_kv_heads;
   if (pairs <= 0 || pairs >= lf::kSplitPairsBelow) return 1;
