@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -52,11 +53,15 @@ def algorithmic_bytes_per_pair(n: int, G: int, d: int, e: int, evict: bool) -> i
 
 
 def kernel_sha() -> str:
-    """sha256[:16] over the kernel sources (decode kernel, its instances, fill)."""
+    """sha256[:16] over the kernel sources (decode kernel, its instances, fill)
+    with comments and whitespace removed, so only code changes alter it."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
