@@ -87,11 +87,11 @@ hipError_t launch_decode_w8(const Geometry& g, const LayerPtrs& L, const SplitWo
 // partials and reduction scratch), an upper bound.
 size_t decode_static_lds_bytes(const Geometry& g, int waves);
 
-// Copies rows [0, n_b) of each sequence into slots 0..n_b-1 and clears the
-// rest; n_host is a host array of `count` lengths for sequences
-// [seq0, seq0 + count).
+// Copies rows [0, n_i) of sequence seq_host[i] into slots 0..n_i-1 of each
+// of its pairs, for `count` listed sequences (host arrays); slots past n_i
+// keep what they held.
 hipError_t launch_fill(const Geometry& g, const LayerPtrs& L, const void* k,
-                       const void* v, const int32_t* n_host, int32_t seq0,
+                       const void* v, const int32_t* seq_host, const int32_t* n_host,
                        int32_t count, int32_t n_max, hipStream_t stream);
 
 // Drops every layer's pairs of the `count` sequences in seqs_host to 0 tokens

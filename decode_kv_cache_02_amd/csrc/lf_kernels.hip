@@ -8,8 +8,10 @@ namespace lf {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Initial fill: one wave per (pair, slot); copies the row or clears it. A
-// sequence whose length is -1 is left untouched.
+// Initial fill: one wave per (pair, slot < n); copies the row (K into its tile
+// position) and writes its norm. Only the listed sequences are touched, and
+// slots at or beyond n keep what they held: no step reads them before they
+// are written (K tiles past n are masked, V reads stop at n).
 // ---------------------------------------------------------------------------
 struct FillParams {
   const void* k;
@@ -23,9 +25,9 @@ struct FillParams {
   int32_t slots_pad;
   int32_t num_kv_heads;
   int32_t n_max;
-  int32_t seq0;
   int32_t norm_l2;
-  int32_t n[kFillSeqPerLaunch];
+  int32_t seq[kFillSeqPerLaunch];  // sequences filled by this launch
+  int32_t n[kFillSeqPerLaunch];    // their lengths (>= 0)
 };
 
 template <typename T, int D>
@@ -39,34 +41,26 @@ __global__ __launch_bounds__(256) void fill_kernel(FillParams P) {
   const int local_pair = blockIdx.y;
   const int bl = local_pair / P.num_kv_heads;
   const int h = local_pair - bl * P.num_kv_heads;
-  const int b = P.seq0 + bl;
+  const int b = P.seq[bl];
   const int64_t pair = static_cast<int64_t>(b) * P.num_kv_heads + h;
   const int nb = P.n[bl];
-  if (slot >= P.slots_pad || nb < 0) return;
+  if (slot >= P.slots_pad) return;
+  if (slot == 0 && lane == 0) {
+    P.fill[pair] = nb;
+    P.victim[pair] = -1;
+  }
+  if (slot >= nb) return;
   char* Kd = reinterpret_cast<char*>(static_cast<T*>(P.kc) + pair * P.pair_elems);
   T* Vd = static_cast<T*>(P.vc) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
-  float nrm = 0.0f;
-  if (slot < nb) {
-    const int64_t src = ((static_cast<int64_t>(b) * P.n_max + slot) * P.num_kv_heads + h) * D;
-    const T* ks = static_cast<const T*>(P.k) + src;
-    const T* vs = static_cast<const T*>(P.v) + src;
-    if (lane < kRowChunks) {
-      store16(Kd + k_chunk_offset<kRowBytes>(slot, lane), load16(ks + lane * EPL));
-      store16(Vd + lane * EPL, load16(vs + lane * EPL));
-    }
-    nrm = wave_norm<T, D>(vs, lane, P.norm_l2 != 0);
-  } else if (lane < kRowChunks) {
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    store16(Kd + k_chunk_offset<kRowBytes>(slot, lane), zero);
-    store16(Vd + lane * EPL, zero);
+  const int64_t src = ((static_cast<int64_t>(b) * P.n_max + slot) * P.num_kv_heads + h) * D;
+  const T* ks = static_cast<const T*>(P.k) + src;
+  const T* vs = static_cast<const T*>(P.v) + src;
+  if (lane < kRowChunks) {
+    store16(Kd + k_chunk_offset<kRowBytes>(slot, lane), load16(ks + lane * EPL));
+    store16(Vd + lane * EPL, load16(vs + lane * EPL));
   }
-  if (lane == 0) {
-    P.vnorm[pair * P.slots_pad + slot] = nrm;
-    if (slot == 0) {
-      P.fill[pair] = nb;
-      P.victim[pair] = -1;
-    }
-  }
+  const float nrm = wave_norm<T, D>(vs, lane, P.norm_l2 != 0);
+  if (lane == 0) P.vnorm[pair * P.slots_pad + slot] = nrm;
 }
 
 // ---------------------------------------------------------------------------
@@ -96,8 +90,8 @@ __global__ __launch_bounds__(64) void seq_reset_kernel(ResetParams P) {
 
 template <typename T, int D>
 hipError_t launch_fill_t(const Geometry& geo, const LayerPtrs& L, const void* k, const void* v,
-                         const int32_t* n_host, int32_t seq0, int32_t count, int32_t n_max,
-                         hipStream_t stream) {
+                         const int32_t* seq_host, const int32_t* n_host, int32_t count,
+                         int32_t n_max, hipStream_t stream) {
   FillParams P;
   P.k = k;
   P.v = v;
@@ -111,9 +105,14 @@ hipError_t launch_fill_t(const Geometry& geo, const LayerPtrs& L, const void* k,
   P.norm_l2 = geo.norm == 1;
   P.num_kv_heads = geo.num_kv_heads;
   P.n_max = n_max;
-  P.seq0 = seq0;
-  for (int i = 0; i < kFillSeqPerLaunch; ++i) P.n[i] = i < count ? n_host[i] : -1;
-  dim3 grid((geo.slots_pad + 3) / 4, count * geo.num_kv_heads);
+  int32_t longest = 0;
+  for (int i = 0; i < kFillSeqPerLaunch; ++i) {
+    P.seq[i] = i < count ? seq_host[i] : 0;
+    P.n[i] = i < count ? n_host[i] : 0;
+    if (i < count && n_host[i] > longest) longest = n_host[i];
+  }
+  // slot 0's wave always runs: it writes the fill level and clears the victim
+  dim3 grid(longest > 0 ? (longest + 3) / 4 : 1, count * geo.num_kv_heads);
   hipLaunchKernelGGL((fill_kernel<T, D>), grid, dim3(256), 0, stream, P);
   return hipGetLastError();
 }
@@ -197,15 +196,19 @@ hipError_t launch_seq_reset(const Geometry& g, int32_t num_layers, int32_t* fill
 }
 
 hipError_t launch_fill(const Geometry& g, const LayerPtrs& L, const void* k, const void* v,
-                       const int32_t* n_host, int32_t seq0, int32_t count, int32_t n_max,
-                       hipStream_t stream) {
+                       const int32_t* seq_host, const int32_t* n_host, int32_t count,
+                       int32_t n_max, hipStream_t stream) {
   if (count <= 0 || count > kFillSeqPerLaunch) return hipErrorInvalidValue;
   if (g.dtype == 1) {
-    if (g.head_dim == 128) return launch_fill_t<uint16_t, 128>(g, L, k, v, n_host, seq0, count, n_max, stream);
-    if (g.head_dim == 64) return launch_fill_t<uint16_t, 64>(g, L, k, v, n_host, seq0, count, n_max, stream);
+    if (g.head_dim == 128)
+      return launch_fill_t<uint16_t, 128>(g, L, k, v, seq_host, n_host, count, n_max, stream);
+    if (g.head_dim == 64)
+      return launch_fill_t<uint16_t, 64>(g, L, k, v, seq_host, n_host, count, n_max, stream);
   } else {
-    if (g.head_dim == 128) return launch_fill_t<float, 128>(g, L, k, v, n_host, seq0, count, n_max, stream);
-    if (g.head_dim == 64) return launch_fill_t<float, 64>(g, L, k, v, n_host, seq0, count, n_max, stream);
+    if (g.head_dim == 128)
+      return launch_fill_t<float, 128>(g, L, k, v, seq_host, n_host, count, n_max, stream);
+    if (g.head_dim == 64)
+      return launch_fill_t<float, 64>(g, L, k, v, seq_host, n_host, count, n_max, stream);
   }
   return hipErrorInvalidValue;
 }

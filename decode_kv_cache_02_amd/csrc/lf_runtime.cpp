@@ -414,13 +414,21 @@ lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void*
   const lf::LayerPtrs p = layer_ptrs(c, layer);
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* fh = c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch;
-  for (int32_t b0 = 0; b0 < c->cfg.batch; b0 += lf::kFillSeqPerLaunch) {
-    const int32_t count = std::min<int32_t>(lf::kFillSeqPerLaunch, c->cfg.batch - b0);
-    bool any = false;
-    for (int32_t i = 0; i < count; ++i) any = any || n_per_seq[b0 + i] >= 0;
-    if (!any) continue;  // every sequence of this group is left as it is
-    if (lf::launch_fill(c->geo, p, k, v, n_per_seq + b0, b0, count, n_max, st) != hipSuccess)
-      return LF_ERR_HIP;
+  // Only the sequences being filled are launched, up to kFillSeqPerLaunch at
+  // a time.
+  int32_t seqs[lf::kFillSeqPerLaunch], lens[lf::kFillSeqPerLaunch];
+  int32_t count = 0;
+  for (int32_t b = 0; b <= c->cfg.batch; ++b) {
+    if (count == lf::kFillSeqPerLaunch || (b == c->cfg.batch && count > 0)) {
+      if (lf::launch_fill(c->geo, p, k, v, seqs, lens, count, n_max, st) != hipSuccess)
+        return LF_ERR_HIP;
+      count = 0;
+    }
+    if (b < c->cfg.batch && n_per_seq[b] >= 0) {
+      seqs[count] = b;
+      lens[count] = n_per_seq[b];
+      ++count;
+    }
   }
   for (int32_t b = 0; b < c->cfg.batch; ++b)
     if (n_per_seq[b] >= 0) fh[b] = n_per_seq[b];

@@ -153,8 +153,9 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out);
  *                 slots 0..n_b-1 of each of its pairs; 0 <= n_b <= n_max.
  *                 n_b = -1 leaves sequence b exactly as it is (refill only
  *                 the sequences being recycled, see lf_seq_reset)
- * Slots n_b..budget-1 are cleared and no victim is pending. k and v may be
- * NULL when n_max = 0. Errors: LF_ERR_CAPACITY if some n_b > budget,
+ * No victim is pending afterwards. Slots n_b..budget-1 keep what they held:
+ * no step reads a slot before it has been written. Only the sequences being
+ * filled are touched (and launched). k and v may be NULL when n_max = 0. Errors: LF_ERR_CAPACITY if some n_b > budget,
  * LF_ERR_INVALID_ARG on null pointers, a bad layer, n_b > n_max or n_b < -1. */
 lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void* v,
                           const int32_t* n_per_seq, int32_t n_max, void* stream);
