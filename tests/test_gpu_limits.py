@@ -67,3 +67,15 @@ def test_llama8b_stack32_ragged_full_shape():
     rep = run_lockstep(wl, 4, pairs=pairs, prefill_n=n, layer=17, num_layers=32,
                        check_cache_every=4)
     assert rep.appends > 0 and rep.evictions > 0
+
+
+@pytest.mark.parametrize("budget", [512, 1024])
+def test_qwen3_8b_stack36_full_shape(budget):
+    """The 36-layer Qwen3-8B stack at batch 256 (the suite's launch), a middle
+    layer, sampled pairs, duplicated tokens included."""
+    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=budget, prefill=budget)
+    pairs = [(0, 0), (77, 3), (128, 5), (255, 7), (200, 1), (31, 6)]
+    _say(f"qwen3_8b stack36, batch 256, B {budget}, layer 20 of 36, 4 steps, pairs {pairs}")
+    rep = run_lockstep(wl, 4, pairs=pairs, layer=20, num_layers=36, check_cache_every=4)
+    assert rep.evictions == 4 * len(pairs)
+    assert rep.tie_lowest_index == rep.exact_ties
