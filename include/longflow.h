@@ -170,7 +170,17 @@ lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void*
  *                 appended
  * Accumulation is float32. Errors: LF_ERR_INVALID_ARG on null pointers or a
  * bad layer; LF_ERR_CAPACITY in FULL mode when a pair already holds
- * `budget` tokens; LF_ERR_HIP if the launch fails. */
+ * `budget` tokens; LF_ERR_HIP if the launch fails.
+ *
+ * The call queues kernel launches only (no memset, no host synchronisation)
+ * and the kernels reset their own cross-workgroup counters, so it can be
+ * captured into a HIP graph, alone or as part of a model step. The kernels
+ * read fill levels and victims from device memory, so replays are exact.
+ * The host-side bookkeeping advances once per call, not per replay: the
+ * launch shape planned at capture time is kept; lf_fill_levels does not see
+ * replays (read fill levels with lf_cache_snapshot); and the FULL-mode
+ * capacity check cannot run inside a replay (a pair at capacity then stores
+ * nothing). */
 lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_new,
                          const void* v_new, void* out, int32_t* evicted_slot,
                          void* stream);

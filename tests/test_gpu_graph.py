@@ -1,0 +1,103 @@
+"""HIP graph capture of decode steps: a captured lf_decode_step (and a captured
+multi-layer model step) replays bit-identically to the same calls made
+eagerly on a twin cache, replay after replay, with eager work (input copies,
+snapshots, synchronisation) between the replays. The step queues only kernel
+launches (no memset, no host synchronisation), and its cross-workgroup
+counters are reset by the kernel itself, so it can be captured.
+"""
+import numpy as np
+import pytest
+
+from decode_kv_cache_02_amd.synth import WORKLOADS, TokenStream
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+@pytest.mark.parametrize("shape", ["llama_batch8", "tp8_split"])
+def test_graph_replay_matches_eager(shape):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    if shape == "llama_batch8":
+        wl = WORKLOADS["llama8b_layer"].with_(batch=8, prefill=3277)
+        layers = 3
+    else:   # 64 pairs of one KV head: split-K launch with counters
+        wl = WORKLOADS["llama8b_layer"].with_(batch=64, num_q_heads=4, num_kv_heads=1,
+                                              prefill=3277)
+        layers = 2
+    _say(f"graph capture, {shape}: {layers} layers, 12 replays")
+    caches = [LongFlowCache(layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                            wl.budget, dtype=wl.dtype) for _ in range(2)]
+    try:
+        for layer in range(layers):
+            pf = TokenStream(wl, layer=layer).prefill()
+            k, v = _dev(pf.k, wl.dtype), _dev(pf.v, wl.dtype)
+            for c in caches:
+                c.prefill(layer, k, v, pf.n_per_seq)
+        ts = TokenStream(wl, seed_offset=3)
+        steps = [ts.step() for _ in range(13)]
+        dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        shp_q = (wl.batch, wl.num_q_heads, wl.head_dim)
+        shp_kv = (wl.batch, wl.num_kv_heads, wl.head_dim)
+        q_s, kn_s, vn_s = (torch.empty(shp_q, dtype=dt, device="cuda"),
+                           torch.empty(shp_kv, dtype=dt, device="cuda"),
+                           torch.empty(shp_kv, dtype=dt, device="cuda"))
+        outs = [torch.empty(shp_q, dtype=dt, device="cuda") for _ in range(layers)]
+        evs = [torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+               for _ in range(layers)]
+        out_e = torch.empty_like(outs[0])
+        ev_e = torch.empty_like(evs[0])
+
+        def load(st):
+            q_s.copy_(_dev(st.q, wl.dtype))
+            kn_s.copy_(_dev(st.k_new, wl.dtype))
+            vn_s.copy_(_dev(st.v_new, wl.dtype))
+
+        # step 0 eagerly on both caches (also warms the graph cache's stream)
+        load(steps[0])
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for layer in range(layers):
+                caches[0].decode_step(layer, q_s, kn_s, vn_s, outs[layer], evs[layer])
+        torch.cuda.current_stream().wait_stream(side)
+        for layer in range(layers):
+            caches[1].decode_step(layer, q_s, kn_s, vn_s, out_e, ev_e)
+        torch.cuda.synchronize()
+
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for layer in range(layers):
+                caches[0].decode_step(layer, q_s, kn_s, vn_s, outs[layer], evs[layer])
+
+        for t in range(1, 13):
+            load(steps[t])
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for layer in range(layers):
+                caches[1].decode_step(layer, q_s, kn_s, vn_s, out_e, ev_e)
+                torch.cuda.synchronize()
+                assert torch.equal(outs[layer], out_e), f"replay {t} layer {layer}: output differs"
+                assert torch.equal(evs[layer], ev_e), f"replay {t} layer {layer}: evicted slots differ"
+                assert int(ev_e.min()) >= 0
+            if t % 4 == 0:
+                for layer in range(layers):
+                    a = caches[0].snapshot(layer, with_victim=True)
+                    b = caches[1].snapshot(layer, with_victim=True)
+                    for x, y in zip(a, b):
+                        assert torch.equal(x, y), f"replay {t} layer {layer}: cache state differs"
+    finally:
+        for c in caches:
+            c.close()
