@@ -379,6 +379,50 @@ def trajectory(wl, steps: int, prompt: int, mode: str):
         cache.close()
 
 
+def tiny_latency(wl, steps: int = 2000, per_graph: int = 64):
+    """The launch-latency-bound tiny workload (one pair, B = 64, fp32): steps/s
+    with one lf_decode_step call per step, and with 64 steps captured in one
+    HIP graph and replayed. Returns (eager ms per step, graph ms per step)."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import device_prefill
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                          dtype=wl.dtype)
+    try:
+        k, v = device_prefill(wl, wl.budget, seed=1)
+        cache.prefill(0, k, v, np.full(wl.batch, wl.budget, dtype=np.int32))
+        ring = make_ring(wl, wl.dtype)
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=ring[0][0].dtype,
+                          device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        eager = time_steps(cache, ring, out, ev, steps, 50)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            args = prepared_ring(cache, ring, out, ev)
+            for t in range(per_graph):
+                cache.step_prepared(args[t % RING][0])
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            args = prepared_ring(cache, ring, out, ev)
+            for t in range(per_graph):
+                cache.step_prepared(args[t % RING][0])
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return eager, start.elapsed_time(end) / (reps * per_graph)
+    finally:
+        cache.close()
+
+
 def suite(args):
     """One JSON line per workload shape (steady state unless stated)."""
     import torch
@@ -395,6 +439,11 @@ def suite(args):
         print(json.dumps(line), flush=True)
 
     steps, warmup = min(args.steps, 300), 20
+    wl1 = WORKLOADS["tiny_f32"]
+    e_ms, g_ms = tiny_latency(wl1)
+    nb1 = wl1.num_kv_heads * algorithmic_bytes_per_pair(wl1.budget, wl1.group, wl1.head_dim, 4, True)
+    emit("tiny_f32 (launch-latency bound), one call per step", wl1, e_ms, nb1)
+    emit("tiny_f32 (launch-latency bound), 64 steps per HIP graph replay", wl1, g_ms, nb1)
     wl2 = WORKLOADS["qwen3_0p6b_layer"]
     ms, nb = steady_state(wl2, steps, warmup)
     emit("qwen3_0p6b_layer", wl2, ms, nb)
