@@ -472,6 +472,11 @@ def suite(args):
     shard = wl3.with_(num_q_heads=4, num_kv_heads=1)
     ms, nb = steady_state(shard, steps, warmup)
     emit("llama8b_layer tp8 shard (1 KV head per GPU)", shard, ms, nb)
+    # small batches: fewer pairs than CUs, so every launch is split-K
+    for b in (1, 4, 16):
+        small = wl3.with_(batch=b)
+        ms, nb = steady_state(small, steps, warmup)
+        emit(f"llama8b_layer batch {b} (split-K)", small, ms, nb)
     # 32-layer ragged stack at the batch where both caches fit 0.95 x 288 GB
     wl4 = WORKLOADS["llama8b_stack32_ragged"]
     cfg_c = make_config(32, 1, 32, 8, 128, wl4.budget)

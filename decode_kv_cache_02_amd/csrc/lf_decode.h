@@ -306,6 +306,11 @@ __device__ __forceinline__ float ws_load(const float* p) {
 __device__ __forceinline__ void drain_stores() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
+// s_waitcnt vmcnt(0) as an instruction the compiler's own wait placement
+// sees (expcnt and lgkmcnt fields at their maxima, so no wait on those):
+// after it, no earlier load counts as outstanding, so later stores of
+// long-loaded values need no wait behind stores issued in between.
+__device__ __forceinline__ void settle_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // The G logits of one slot as one buffer access with the device-scope cache
 // policy (the sc1 bit, as the relaxed agent-scope atomics above use).
@@ -380,9 +385,11 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   __shared__ int sh_best_slot[WAVES];
   __shared__ float sh_gm[G];                // SPLIT: global max and sum of the pair
   __shared__ float sh_gl[G];
+  __shared__ float sh_fac[kMaxSplits][G];  // SPLIT: exp2(m_split - M) per split and head
   __shared__ int sh_ticket;
   (void)sh_gm;
   (void)sh_gl;
+  (void)sh_fac;
   (void)sh_ticket;
 
   const int tid = threadIdx.x;
@@ -498,6 +505,18 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
       nv[k] = vn[d];
     }
   }
+  // What the epilogue reads of the new token, requested now as well: v_new
+  // at this thread's output elements (the new token's own term) and, for
+  // the threads that store the new row, one 16-byte chunk of k_new or v_new.
+  constexpr int kOutPer = (G * D + NT - 1) / NT;  // output elements per thread
+  T ov[kOutPer];
+#pragma unroll
+  for (int j = 0; j < kOutPer; ++j) ov[j] = vn[(tid + j * NT) % D];
+  u32x4_t wrow = {0u, 0u, 0u, 0u};
+  if (tid < kRowLoads)
+    wrow = load16(kn + tid * EPL);
+  else if (tid < 2 * kRowLoads)
+    wrow = load16(vn + (tid - kRowLoads) * EPL);
   auto new_token = [&]() {
     if (wave < G) {
       float x = 0.0f;
@@ -747,14 +766,19 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   T* out = static_cast<T*>(P.out) + (static_cast<int64_t>(b) * P.num_q_heads + h * G) * D;
 
   if constexpr (!SPLIT) {
-    for (int idx = tid; idx < G * D; idx += NT) {
-      const int g = idx / D;
-      const int d = idx - g * D;
-      float o = 0.0f;
+    settle_loads();  // only finished prologue loads and zero-fill tail loads are pending
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
-      o = fmaf(w_run[g], to_f32(vn[d]), o);
-      from_f32(o / l_run[g], out + g * D + d);
+    for (int j = 0; j < kOutPer; ++j) {
+      const int idx = tid + j * NT;
+      if (idx < G * D) {
+        const int g = idx / D;
+        const int d = idx - g * D;
+        float o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
+        o = fmaf(w_run[g], to_f32(ov[j]), o);
+        from_f32(o / l_run[g], out + g * D + d);
+      }
     }
     if (EVICT && scoring && shared) {
       // One victim per sequence: publish this head's score vector (in LDS
@@ -796,29 +820,77 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
     if (sh_ticket != S - 1) return;  // not the last split of the pair
 
     // ---------------- Last split: combine, score ----------------
+    // Everything the combine and the first score batch read is requested
+    // before any of it is used, in the order it is needed: every split's
+    // (m, l) for this thread's query head, its partial outputs, then raw
+    // logits and norms. The tail costs one memory round trip, not four.
     const float* part = P.ws_part + static_cast<int64_t>(pair) * S * kPart;
+    float ml[kMaxSplits][2];
+    {
+      const int g = tid & (G - 1);
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+        ml[s2][0] = s2 < S ? ws_load(part + s2 * kPart + g) : 0.0f;
+        ml[s2][1] = s2 < S ? ws_load(part + s2 * kPart + G + g) : 0.0f;
+      }
+    }
+    float op[kOutPer][kMaxSplits];
+#pragma unroll
+    for (int j = 0; j < kOutPer; ++j) {
+      const int idx = min(tid + j * NT, G * D - 1);  // threads past G*D store nothing
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplits; ++s2)
+        op[j][s2] = s2 < S ? ws_load(part + s2 * kPart + 2 * G + idx) : 0.0f;
+    }
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(
+        P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(n) * G * 4u);
+    const __amdgpu_buffer_rsrc_t rNa =
+        make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
+    constexpr int kLastBatch = 8;  // slots per thread with loads in flight together
+    float vb[kLastBatch];
+    float lg[kLastBatch][G];
+    auto load_batch = [&](int i0) {
+#pragma unroll
+      for (int k = 0; k < kLastBatch; ++k) {
+        vb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rNa, static_cast<int>((i0 + k * NT) * 4), 0, 0));
+        ws_load_g<G>(rL, static_cast<uint32_t>(i0 + k * NT) * G * 4u, lg[k]);
+      }
+    };
+    if (scoring) load_batch(P.sink + tid);
+
     if (tid < G) {  // global max and sum, new token included, fixed order
       const int g = tid;
       float M = sh_snew[g];
-      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, ws_load(part + s2 * kPart + g));
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplits; ++s2)
+        if (s2 < S) M = fmaxf(M, ml[s2][0]);
       float L = __builtin_amdgcn_exp2f(sh_snew[g] - M);
-      for (int s2 = 0; s2 < S; ++s2)
-        L = fmaf(ws_load(part + s2 * kPart + G + g),
-                 __builtin_amdgcn_exp2f(ws_load(part + s2 * kPart + g) - M), L);
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+        if (s2 < S) {
+          const float f = __builtin_amdgcn_exp2f(ml[s2][0] - M);
+          sh_fac[s2][g] = f;
+          L = fmaf(ml[s2][1], f, L);
+        }
+      }
       sh_gm[g] = M;
       sh_gl[g] = L;
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += NT) {
-      const int g = idx / D;
-      const int d = idx - g * D;
-      const float M = sh_gm[g];
+    // Output values now, stores after the score: stores count in the same
+    // counter as loads, so a store issued before the score's last loads
+    // would have to be acknowledged before the score could finish.
+    float ofin[kOutPer];
+#pragma unroll
+    for (int j = 0; j < kOutPer; ++j) {
+      const int g = min((tid + j * NT) / D, G - 1);
       float o = 0.0f;
-      for (int s2 = 0; s2 < S; ++s2)
-        o = fmaf(ws_load(part + s2 * kPart + 2 * G + idx),
-                 __builtin_amdgcn_exp2f(ws_load(part + s2 * kPart + g) - M), o);
-      o = fmaf(__builtin_amdgcn_exp2f(sh_snew[g] - M), to_f32(vn[d]), o);
-      from_f32(o / sh_gl[g], out + g * D + d);
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplits; ++s2)
+        if (s2 < S) o = fmaf(op[j][s2], sh_fac[s2][g], o);
+      o = fmaf(__builtin_amdgcn_exp2f(sh_snew[g] - sh_gm[g]), to_f32(ov[j]), o);
+      ofin[j] = o / sh_gl[g];
     }
     if (scoring) {
       // Score every slot from the published raw logits: the same operations
@@ -832,20 +904,8 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
       const __amdgpu_buffer_rsrc_t rSc =
           make_rsrc(shared ? P.ws_score + static_cast<int64_t>(pair) * slots_pad : nullptr,
                     shared ? static_cast<uint32_t>(n) * 4u : 0u);
-      const __amdgpu_buffer_rsrc_t rL = make_rsrc(
-          P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(n) * G * 4u);
-      const __amdgpu_buffer_rsrc_t rNa =
-          make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
-      constexpr int kLastBatch = 8;  // slots per thread with loads in flight together
       for (int i0 = P.sink + tid; i0 < n; i0 += NT * kLastBatch) {
-        float vb[kLastBatch];
-        float lg[kLastBatch][G];
-#pragma unroll
-        for (int k = 0; k < kLastBatch; ++k) {
-          vb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              rNa, static_cast<int>((i0 + k * NT) * 4), 0, 0));
-          ws_load_g<G>(rL, static_cast<uint32_t>(i0 + k * NT) * G * 4u, lg[k]);
-        }
+        if (i0 != P.sink + tid) load_batch(i0);  // the first batch is in flight already
 #pragma unroll
         for (int k = 0; k < kLastBatch; ++k) {
           const int i = i0 + k * NT;
@@ -873,6 +933,11 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
         sh_best_score[wave] = best;
         sh_best_slot[wave] = best_i;
       }
+    }
+#pragma unroll
+    for (int j = 0; j < kOutPer; ++j) {
+      const int idx = tid + j * NT;  // = g * D + d
+      if (idx < G * D) from_f32(ofin[j], out + idx);
     }
     if (shared && scoring && tid == 0) ws_store(P.ws_nnorm + pair, sh_vn_new);
     if (tid == 0) __hip_atomic_store(P.arrive + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1037,12 +1102,10 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   if (slot < 0) return;  // no candidate (only with non-finite scores): nothing stored
   char* Kw = reinterpret_cast<char*>(static_cast<T*>(P.kc_w) + pair * P.pair_elems);
   T* Vw = static_cast<T*>(P.vc_w) + pair * P.pair_elems + static_cast<int64_t>(slot) * D;
-  if (tid < kRowLoads) {
-    store16(Kw + k_chunk_offset<kRowBytes>(slot, tid), load16(kn + tid * EPL));
-  } else {
-    const int j = tid - kRowLoads;
-    store16(Vw + j * EPL, load16(vn + j * EPL));
-  }
+  if (tid < kRowLoads)
+    store16(Kw + k_chunk_offset<kRowBytes>(slot, tid), wrow);
+  else
+    store16(Vw + (tid - kRowLoads) * EPL, wrow);
   if (tid == 0) P.vnorm[static_cast<int64_t>(pair) * slots_pad + slot] = sh_vn_new;
 }
 
