@@ -423,6 +423,28 @@ def tiny_latency(wl, steps: int = 2000, per_graph: int = 64):
         cache.close()
 
 
+def batch_gain(wl):
+    """Each method on the 32-layer ragged stack at the largest batch its own
+    cache allows in 0.95 x 288 GB, with the same start-offset distribution:
+    the comparison of tokens/s at each method's own batch. Yields (workload,
+    ms per model step, algorithmic bytes per model step, extra fields)."""
+    from decode_kv_cache_02_amd.native import lf_cache_bytes, make_config
+    from decode_kv_cache_02_amd.synth import TokenStream
+    rate = {}
+    for method, mode, cap in (("LongFlow", "evict", wl.budget), ("full-KV", "full", 16384 + 512 + 64)):
+        b = int(0.95 * 288e9 // lf_cache_bytes(make_config(32, 1, 32, 8, 128, cap, mode=mode)))
+        w = wl.with_(batch=b)
+        offs = TokenStream(w).start_offsets()
+        ms, nb = steady_state(w, 10, 2, layers=32, mode=mode, capacity=cap,
+                              ragged=np.minimum(offs, cap) if mode == "evict" else offs, seed=6)
+        rate[method] = b / ms
+        extra = {"method": method,
+                 "batch_rule": "largest batch with this method's cache alone in 0.95 x 288 GB"}
+        if method == "full-KV":
+            extra["longflow_tokens_per_s_over_full_kv"] = rate["LongFlow"] / rate["full-KV"]
+        yield w, ms, nb, extra
+
+
 def suite(args):
     """One JSON line per workload shape (steady state unless stated)."""
     import torch
@@ -492,6 +514,8 @@ def suite(args):
     ms, nb = steady_state(wl4, min(steps, 20), 2, layers=32, mode="full",
                           capacity=16384 + 512 + 64, ragged=offsets, seed=4)
     emit("llama8b_stack32_ragged full-KV", wl4, ms, nb, 32)
+    for w, ms, nb, extra in batch_gain(wl4):
+        emit(f"llama8b_stack32_ragged {extra.pop('method')} at its own largest batch", w, ms, nb, 32, extra)
     wl5 = WORKLOADS["qwen3_8b_stack36_ties"]
     for budget in (512, 1024, 2048, 4096):
         w = wl5.with_(budget=budget)

@@ -291,9 +291,19 @@ def device_prefill(wl: Workload, n: int, seed: int, device: str = "cuda"):
     g.manual_seed(int(seed))
     shape = (wl.batch, n, wl.num_kv_heads, wl.head_dim)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    k = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dt)
-    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    scale = torch.empty(shape[:3] + (1,), device=device, dtype=torch.float32)
-    scale.log_normal_(0.0, V_LOGNORMAL_SIGMA, generator=g)
-    v = (v * scale).to(dt)
+    k = torch.empty(shape, device=device, dtype=dt)
+    v = torch.empty(shape, device=device, dtype=dt)
+    # Drawn a few sequences at a time, so the float32 temporaries stay near
+    # 1 GB even when the caches being filled take most of the device.
+    per_seq = max(1, n * wl.num_kv_heads * wl.head_dim)
+    step = max(1, (1 << 27) // per_seq)
+    for b0 in range(0, wl.batch, step):
+        b1 = min(wl.batch, b0 + step)
+        sub = (b1 - b0,) + shape[1:]
+        k[b0:b1] = torch.randn(sub, generator=g, device=device, dtype=torch.float32).to(dt)
+        vv = torch.randn(sub, generator=g, device=device, dtype=torch.float32)
+        scale = torch.empty(sub[:3] + (1,), device=device, dtype=torch.float32)
+        scale.log_normal_(0.0, V_LOGNORMAL_SIGMA, generator=g)
+        v[b0:b1] = (vv * scale).to(dt)
+        del vv, scale
     return k, v
