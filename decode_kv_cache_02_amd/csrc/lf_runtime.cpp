@@ -82,6 +82,12 @@ lf_status validate(const lf_config* c) {
   const int g = c->num_q_heads / c->num_kv_heads;
   if (g != 1 && g != 2 && g != 4) return LF_ERR_UNSUPPORTED;
   if (c->budget > (1 << 30) - kSlotAlign) return LF_ERR_UNSUPPORTED;
+  {
+    // The kernels address one pair's K and V rows with 32-bit byte offsets.
+    const int64_t slots_pad = (static_cast<int64_t>(c->budget) + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
+    const int64_t row_bytes = static_cast<int64_t>(c->head_dim) * (c->dtype == LF_DTYPE_F32 ? 4 : 2);
+    if (slots_pad * row_bytes > int64_t{0xffffffff}) return LF_ERR_UNSUPPORTED;
+  }
   if (c->scope == LF_SCOPE_SEQUENCE) {
     // The deciding workgroup addresses a sequence's score vectors with 32-bit
     // offsets.
@@ -184,12 +190,29 @@ lf::LayerPtrs layer_ptrs(const lf_cache* c, int32_t layer) {
   return p;
 }
 
-lf_status use_device(const lf_cache* c) {
-  int cur = -1;
-  if (hipGetDevice(&cur) != hipSuccess) return LF_ERR_HIP;
-  if (cur != c->device && hipSetDevice(c->device) != hipSuccess) return LF_ERR_HIP;
-  return LF_OK;
-}
+// Makes the cache's device current for the length of one call and gives the
+// caller's current device back afterwards.
+class DeviceScope {
+ public:
+  explicit DeviceScope(int device) {
+    if (hipGetDevice(&prev_) != hipSuccess) {
+      ok_ = false;
+      return;
+    }
+    if (prev_ != device) ok_ = switched_ = hipSetDevice(device) == hipSuccess;
+  }
+  ~DeviceScope() {
+    if (switched_) (void)hipSetDevice(prev_);
+  }
+  DeviceScope(const DeviceScope&) = delete;
+  DeviceScope& operator=(const DeviceScope&) = delete;
+  bool ok() const { return ok_; }
+
+ private:
+  int prev_ = -1;
+  bool ok_ = true;
+  bool switched_ = false;
+};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -332,10 +355,8 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
 void lf_cache_destroy(lf_cache* c) {
   if (!c) return;
   if (c->base) {
-    int cur = -1;
-    if (hipGetDevice(&cur) == hipSuccess && cur != c->device) (void)hipSetDevice(c->device);
+    DeviceScope dev(c->device);
     (void)hipFree(c->base);
-    if (cur >= 0 && cur != c->device) (void)hipSetDevice(cur);
   }
   delete c;
 }
@@ -357,8 +378,8 @@ lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view) {
 lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm,
                             int32_t* fill, int32_t* victim, void* stream) {
   if (!c || layer < 0 || layer >= c->cfg.num_layers) return LF_ERR_INVALID_ARG;
-  lf_status s = use_device(c);
-  if (s != LF_OK) return s;
+  DeviceScope dev(c->device);
+  if (!dev.ok()) return LF_ERR_HIP;
   const lf::LayerPtrs p = layer_ptrs(c, layer);
   const size_t kv_bytes = static_cast<size_t>(c->layer_pairs) * c->geo.pair_elems * c->elem_bytes;
   const size_t vn_bytes = static_cast<size_t>(c->layer_pairs) * c->geo.slots_pad * sizeof(float);
@@ -409,8 +430,8 @@ lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void*
     if (n_per_seq[b] < -1 || n_per_seq[b] > n_max) return LF_ERR_INVALID_ARG;
     if (n_per_seq[b] > c->cfg.budget) return LF_ERR_CAPACITY;
   }
-  lf_status s = use_device(c);
-  if (s != LF_OK) return s;
+  DeviceScope dev(c->device);
+  if (!dev.ok()) return LF_ERR_HIP;
   const lf::LayerPtrs p = layer_ptrs(c, layer);
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* fh = c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch;
@@ -440,8 +461,8 @@ lf_status lf_seq_reset(lf_cache* c, const int32_t* seqs, int32_t count, void* st
   for (int32_t i = 0; i < count; ++i)
     if (seqs[i] < 0 || seqs[i] >= c->cfg.batch) return LF_ERR_INVALID_ARG;
   if (count == 0) return LF_OK;
-  lf_status s = use_device(c);
-  if (s != LF_OK) return s;
+  DeviceScope dev(c->device);
+  if (!dev.ok()) return LF_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (int32_t i0 = 0; i0 < count; i0 += lf::kFillSeqPerLaunch) {
     const int32_t n = std::min<int32_t>(lf::kFillSeqPerLaunch, count - i0);
@@ -467,8 +488,8 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
     for (int32_t b = 0; b < c->cfg.batch; ++b)
       if (fh[b] >= c->cfg.budget) return LF_ERR_CAPACITY;
   }
-  lf_status s = use_device(c);
-  if (s != LF_OK) return s;
+  DeviceScope dev(c->device);
+  if (!dev.ok()) return LF_ERR_HIP;
   const lf::LayerPtrs p = layer_ptrs(c, layer);
   int32_t n_max = 0;
   for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);

@@ -178,6 +178,7 @@ def _stream_ptr(stream) -> int:
 
 
 def lf_prefill_fill(handle: int, layer: int, k, v, n_per_seq, n_max: int, stream=None) -> None:
+    """`n_per_seq` must hold the cache's batch of entries: the library reads that many."""
     n = np.ascontiguousarray(n_per_seq, dtype=np.int32)
     kp = k.data_ptr() if k is not None else 0
     vp = v.data_ptr() if v is not None else 0
@@ -239,6 +240,7 @@ def lf_cache_max_splits(handle: int) -> int:
 
 
 def lf_fill_levels(handle: int, layer: int, batch: int) -> np.ndarray:
+    """`batch` must be the cache's batch: the library writes that many entries."""
     out = np.zeros(batch, dtype=np.int32)
     _check(load_library().lf_fill_levels(ctypes.c_void_p(handle), int(layer),
                                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
@@ -307,6 +309,8 @@ class LongFlowCache:
 
     def prefill(self, layer, k, v, n_per_seq, stream=None):
         n_per_seq = np.asarray(n_per_seq, dtype=np.int32)
+        if n_per_seq.shape != (self.batch,):
+            raise ValueError(f"n_per_seq: expected shape ({self.batch},), got {n_per_seq.shape}")
         n_max = int(k.shape[1]) if k is not None else 0
         if k is not None:
             self._check_tensor(k, (self.batch, n_max, self.hkv, self.head_dim), "k")

@@ -54,6 +54,9 @@
  *   - The caller owns every I/O pointer. They are contiguous DEVICE buffers in
  *     cfg.dtype (float32 or bfloat16) unless stated, and must stay valid until
  *     the work queued on `stream` has completed.
+ *   - The cache lives on the device that was current at lf_cache_create.
+ *     Every later call on the handle runs there and leaves the caller's
+ *     current device as it found it.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls are stream-ordered and asynchronous; the library never
  *     synchronises the device and never copies device -> host.
@@ -108,7 +111,10 @@ typedef struct {
   int32_t num_q_heads;  /* multiple of num_kv_heads; G = num_q_heads/num_kv_heads */
   int32_t num_kv_heads; /* >= 1                                                  */
   int32_t head_dim;     /* 64 or 128                                             */
-  int32_t budget;       /* slots per pair (EVICT) or capacity (FULL), >= 1       */
+  int32_t budget;       /* slots per pair (EVICT) or capacity (FULL), >= 1; one
+                           pair's K region (budget rounded up to 64, times
+                           head_dim, times the element size) must stay under
+                           4 GiB, else LF_ERR_UNSUPPORTED                         */
   int32_t sink_size;    /* slots [0, sink_size) are never evicted; < budget      */
   float softmax_scale;  /* tau; 0 selects 1/sqrt(head_dim)                      */
   int32_t dtype;        /* lf_dtype: of the cache and of q, k_new, v_new, out    */
@@ -155,8 +161,9 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out);
  *                 the sequences being recycled, see lf_seq_reset)
  * No victim is pending afterwards. Slots n_b..budget-1 keep what they held:
  * no step reads a slot before it has been written. Only the sequences being
- * filled are touched (and launched). k and v may be NULL when n_max = 0. Errors: LF_ERR_CAPACITY if some n_b > budget,
- * LF_ERR_INVALID_ARG on null pointers, a bad layer, n_b > n_max or n_b < -1. */
+ * filled are touched (and launched). k and v may be NULL when n_max = 0.
+ * Errors: LF_ERR_CAPACITY if some n_b > budget; LF_ERR_INVALID_ARG on null
+ * pointers, a bad layer, n_b > n_max or n_b < -1. */
 lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void* v,
                           const int32_t* n_per_seq, int32_t n_max, void* stream);
 

@@ -72,6 +72,22 @@ def test_cache_bytes_layout(lib):
     assert b32 > 32 * 103 * 8 * slots * 128 * 2 * 2
 
 
+def test_pair_region_must_fit_32bit_offsets(lib):
+    """The kernels address one pair's K or V rows with 32-bit byte offsets:
+    float32, head_dim 128 (512-byte rows) allows at most 2^23 - 64 padded
+    slots per pair; one more padded block is refused before any allocation."""
+    one = dict(batch=1, num_q_heads=1, num_kv_heads=1, dtype="f32", mode="full")
+    last = (1 << 23) - 64                     # already a multiple of 64
+    assert native.lf_cache_bytes(_cfg(budget=last, **one)) > 2 * last * 128 * 4
+    for budget in (last + 1, 1 << 23, (1 << 30) - 64):
+        with pytest.raises(native.LongFlowError) as ei:
+            native.lf_cache_bytes(_cfg(budget=budget, **one))
+        assert ei.value.status == native.LF_ERR_UNSUPPORTED
+        with pytest.raises(native.LongFlowError) as ei:
+            native.lf_cache_create(_cfg(budget=budget, **one))
+        assert ei.value.status == native.LF_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=30), native.LF_ERR_INVALID_ARG),        # not a multiple of 8
     (dict(batch=0), native.LF_ERR_INVALID_ARG),

@@ -90,6 +90,9 @@ def test_prefill_errors_change_nothing(cache):
     assert ei.value.status == native.LF_ERR_INVALID_ARG
     with pytest.raises(ValueError):                        # the binding refuses non-contiguous views
         cache.prefill(0, k[:, :10], k[:, :10], [5, 0, 0])
+    for short in ([5, 0], [5, 0, 0, 0]):                   # one length per sequence, no more, no less
+        with pytest.raises(ValueError):
+            cache.prefill(0, k10, k10, short)
     torch.cuda.synchronize()
     _same(before, _state(cache))
 
