@@ -32,7 +32,8 @@ if ROOT not in sys.path:
 METRIC = "fused decode+evict steps/sec (tokens/s) and achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, AMD public specification
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_kv_cache_02_amd", "csrc", f)
-                  for f in ("lf_decode.h", "lf_decode_w4.hip", "lf_decode_w8.hip", "lf_kernels.hip")]
+                  for f in ("lf_decode.h", "lf_decode_w4.hip", "lf_decode_w8.hip", "lf_decode_w4i.hip",
+                            "lf_decode_w8i.hip", "lf_kernels.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama8b_layer.json")
 RING = 64
 

@@ -15,22 +15,23 @@
 //
 //   one workgroup = one pair (sequence, KV head), 4 or 8 waves of 64 lanes
 //   (split-K: a contiguous range of the pair's 16-slot tiles).
-//   Phase A  K stream. K is stored in 16-slot tiles in MFMA operand order,
-//            so 16-byte loads land straight in the B operand of
-//            v_mfma_f32_16x16x32_bf16 (16x16x4 f32 for float32 caches). The
-//            query group is replicated over the 16 A rows, so each lane
-//            holds all G logits of one slot. Logits go to LDS; two register
-//            sets of tiles are in flight per wave.
-//   A2       group max (new token included), p = exp2(s - M) in place in
-//            LDS, row sums L.
-//   Phase C  (when a victim is chosen) score_i = ||v_i|| * sum_g p_{g,i}/L_g
-//            from LDS and the float32 sidecar, while the first V rows are in
-//            flight; (score, slot) argmin through DPP and LDS, lowest slot
-//            on ties.
-//   Phase B  V stream: 16-byte loads, 16 lanes per 256-byte row, float32
-//            FMAs against p broadcast from LDS; two register sets in flight.
-//   Phase D  cross-wave output reduction, the new token's own term, output
-//            write, then the new token's K, V and ||v|| written in place.
+//   Stream   each wave takes every WAVES-th 16-slot tile and streams its K
+//            and the V rows of the same slots together, two tiles in
+//            flight. K is stored in MFMA operand order, so 16-byte loads
+//            land straight in the B operand of v_mfma_f32_16x16x32_bf16
+//            (16x16x4 f32 for float32 caches); the query group is
+//            replicated over the 16 A rows, so each lane holds all G logits
+//            of one slot. The raw logits go to LDS (kept for the score);
+//            p = exp2(s - m) against the wave's own running maximum is
+//            staged in a small per-wave strip of LDS and the V rows are
+//            accumulated against it (online softmax, one per wave).
+//   Combine  after one barrier: the workgroup's max M and sum L (the new
+//            token included) and each wave's rescaling factor, in a fixed
+//            order; output written.
+//   Score    score_i = ||v_i|| * sum_g exp2(s_{g,i} - M_g)/L_g from the raw
+//            logits in LDS and the float32 sidecar; (score, slot) argmin
+//            through DPP and LDS, lowest slot on ties; the new token's K, V
+//            and ||v|| are written in place.
 //   Split-K  every split publishes its (m, l, o) and, when scoring, its raw
 //            logits; the last split to arrive combines, scores and writes.
 //            No workgroup waits for another.
@@ -38,8 +39,9 @@
 //            run-time flags of separate instances (the main instance carries
 //            neither).
 //
-// Every cached byte is read once; the score needs no second pass because the
-// probabilities of the whole pair stay in LDS until the argmin is known.
+// Every cached byte is read once and no barrier interrupts the stream: the
+// score needs no second pass over HBM because the raw logits of the whole
+// pair stay in LDS until M and L are known.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,7 +57,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kStream = 3;                          // cache policy: non-temporal (nt) + sc0
 constexpr size_t kEvictLdsCap = 144 * 1024;        // logits of one pair; the rest is static LDS
-constexpr size_t kFullChunkSlots = 2048;            // FULL mode: slots per LDS-resident chunk
+constexpr size_t kFullChunkSlots = 2048;            // FULL mode, phased loop: slots per LDS chunk
+constexpr float kSlack = 32.0f;                     // online softmax: rescale when a logit exceeds
+                                                    // the reference maximum by more (log2 units)
+constexpr float kNoMax = -1.0e30f;                  // reference maximum before any live slot
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Storage types: float32 is `float`, bfloat16 is its 16-bit pattern.
@@ -185,6 +190,18 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
 }
+// Ordering point for lanes of one wave that exchange values through LDS
+// without a workgroup barrier. The hardware runs one wave's LDS operations in
+// issue order, but the compiler reasons per lane: a lane that does not take
+// part in a guarded write could otherwise have its read of the same strip
+// moved ahead of the write. Wavefront-scope release and acquire fences
+// around a wave barrier keep every lane's accesses on their side of it.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float lane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
@@ -195,6 +212,15 @@ __device__ __forceinline__ float wave_sum(float x) {
   x += dpp_f<kDppRor4>(x);
   x += dpp_f<kDppRor8>(x);
   return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
+}
+// Sum over each row of 16 lanes (the same DPP butterflies as wave_sum); every
+// lane of a row ends with its row's sum.
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppRor4>(x);
+  x += dpp_f<kDppRor8>(x);
+  return x;
 }
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp_f<kDppXor1>(x));
@@ -275,7 +301,7 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t budget;
   int32_t sink;
-  int32_t chunk;        // slots per LDS-resident chunk (EVICT: a whole split)
+  int32_t chunk;        // phased loop: slots per LDS-resident chunk (EVICT: the whole split)
   float scale_log2;     // tau * log2(e)
   int32_t deferred;     // 1: write into the previous victim, then choose the next
   int32_t shared;       // 1: one victim per sequence (scores summed over KV heads)
@@ -358,9 +384,13 @@ __device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off
  *                  output and the new token. No workgroup ever waits.
  *   VAR = true: the deferred order and one victim per sequence are available
  *               (runtime flags); false compiles them out of the main path.
+ *   ILV = true: the interleaved loop (each wave streams the K and the V of
+ *               the same tiles together, UA tiles per set, two sets in
+ *               flight); false: the phased loop (all K, then all V, UA K
+ *               tiles or UB V row loads per set).
  */
 template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT,
-          bool VAR>
+          bool VAR, bool ILV>
 __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel(DecodeParams P) {
   constexpr int kBytes = Elem<T>::kBytes;
   constexpr int NT = WAVES * kWave;
@@ -371,21 +401,23 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   constexpr uint32_t kRowBytes = D * kBytes;
   constexpr int kScoreBatch = 16;           // sidecar loads in flight per thread
   constexpr int kRowLoads = D * kBytes / 16;
+  constexpr int kVLoads = 16 / SPI;         // wave-wide V loads per 16-slot tile (= kChunks)
   static_assert(G == 1 || G == 2 || G == 4, "group width");
   static_assert(LPS <= kWave && SPI * LPS == kWave, "row split");
   static_assert(G <= WAVES, "one wave per query head of the group for the new token");
 
-  extern __shared__ __attribute__((aligned(16))) float lds[];  // [chunk][G] logits (-> p)
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // EVICT: [hi - lo][G] raw logits
   __shared__ float sh_red[WAVES][G][D];     // per-wave output partials
-  __shared__ float sh_part[WAVES][G];
-  __shared__ float sh_part2[WAVES][G];
+  __shared__ __attribute__((aligned(16))) float sh_pst[WAVES][16 * G];  // per-wave p of one tile
+  __shared__ float sh_part[WAVES][G];       // per-wave reference maximum
+  __shared__ float sh_part2[WAVES][G];      // per-wave sum of p
   __shared__ float sh_snew[G];
   __shared__ float sh_vn_new;
   __shared__ float sh_best_score[WAVES];
   __shared__ int sh_best_slot[WAVES];
-  __shared__ float sh_gm[G];                // SPLIT: global max and sum of the pair
+  __shared__ float sh_gm[G];                // last split: the pair's max and sum
   __shared__ float sh_gl[G];
-  __shared__ float sh_fac[kMaxSplits][G];  // SPLIT: exp2(m_split - M) per split and head
+  __shared__ float sh_fac[kMaxSplits][G];  // last split: exp2(m_split - M) per split
   __shared__ int sh_ticket;
   (void)sh_gm;
   (void)sh_gl;
@@ -420,44 +452,14 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
     lo = tb * 16;
     hi = min(min(tb + per, tiles) * 16, n);
   }
-  float* pbuf = lds;  // p overwrites the logits in place
 
-  // Lane roles. K phase: r16 = slot within a 16-slot tile, grp = 16-byte
-  // chunk group. V phase: vcol = first element of the lane's 16 bytes of the
-  // row, vsub = which of the SPI rows of a wave-wide load.
+  // Lane roles. K: r16 = slot within a 16-slot tile, grp = 16-byte chunk
+  // group. V: vcol = first element of the lane's 16 bytes of the row, vsub =
+  // which of the SPI rows of a wave-wide load.
   const int r16 = lane & 15;
   const int grp = lane >> 4;
   const int vcol = (lane % LPS) * EPL;
   const int vsub = lane / LPS;
-
-  // K and V reads of the current chunk [c0, c0 + cn) go through descriptors
-  // that end where the chunk ends (whole tiles for K): the loops below always
-  // request the next register set, and requests past the chunk return zeros
-  // without moving data (so the compiler's load counting stays exact and
-  // both register sets stay in flight).
-  int cn = min(P.chunk, hi - lo);
-  int ntiles = (cn + 15) >> 4;
-  __amdgpu_buffer_rsrc_t rK = make_rsrc(K, static_cast<uint32_t>((lo + cn + 15) >> 4) * kTileBytes);
-  __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(lo + cn) * kRowBytes);
-
-  // First K tiles go out before anything else.
-  u32x4_t kr[UA][kChunks];
-  {
-    const uint32_t off0 = static_cast<uint32_t>(lo >> 4) * kTileBytes + lane * 16u;
-#pragma unroll
-    for (int u = 0; u < UA; ++u)
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c)
-        kr[u][c] = bload16<POLICY>(
-            rK, off0 + static_cast<uint32_t>(wave * UA + u) * kTileBytes + 1024u * c);
-  }
-
-  // Query operand in the MFMA A layout: lane = row (query head row % G) +
-  // 16 * (16-byte chunk group); the same byte offsets as the key loads.
-  u32x4_t qa[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c)
-    qa[c] = load16(qg + (r16 % G) * D + (64 * c + 16 * grp) / kBytes);
 
   // What this step does with the new token.
   //   same-step order: below the budget it is appended at slot n; at the
@@ -477,23 +479,10 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   }
   const bool scoring = EVICT && (deferred ? n + 1 >= P.budget : overwrite);
 
-  // Sidecar of the slots this thread scores (the first kScoreBatch of them),
-  // requested now so the score phase finds it in registers.
-  const int sc_lo = max(lo, P.sink);
-  const __amdgpu_buffer_rsrc_t rN =
-      make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(hi) * 4u);
-  float vnb[kScoreBatch];
-  if (!SPLIT && scoring) {
-#pragma unroll
-    for (int k = 0; k < kScoreBatch; ++k)
-      vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rN, static_cast<int>((sc_lo + tid + k * NT) * 4), 0, 0));
-  }
-
   // The new token's logits (wave g < G takes query head g) and ||v_new||
-  // (wave 0). Their inputs are requested now and used only after the K
-  // stream, so no wave starts its K tiles late; the results are visible
-  // after the first barrier.
+  // (wave 0). Their inputs are requested now and used after the stream, so
+  // no wave starts its tiles late; the results are visible after the
+  // workgroup's first barrier.
   T nq[D / kWave], nk[D / kWave], nv[D / kWave];
   {
     const int hsel = wave < G ? wave : 0;
@@ -531,292 +520,653 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
     }
   };
 
-  // Running softmax state, identical in every thread. One workgroup per
-  // pair: the new token opens it with weight exp2(s_new - s_new) = 1. Split:
-  // the partial holds the split's own slots only (the new token is added
-  // once, when the partials are combined).
-  float m_run[G], l_run[G], w_run[G];
-  float acc[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = SPLIT ? 0.0f : 1.0f;
-    w_run[g] = SPLIT ? 0.0f : 1.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
-  }
-  float best = INFINITY;
+  // This pair's output rows [G][D].
+  auto out_rows = [&]() {
+    return static_cast<T*>(P.out) + (static_cast<int64_t>(b) * P.num_q_heads + h * G) * D;
+  };
+  float best = INFINITY;  // this thread's (score, slot) minimum
   int best_i = 0x7fffffff;
+  constexpr int kPart = 2 * G + G * D;  // split partial: m[G], l[G], o[G][D]
+  const int S = SPLIT ? P.splits : 1;
+  (void)S;
 
-  for (int c0 = lo; c0 < hi; c0 += P.chunk) {
-    cn = min(P.chunk, hi - c0);
-    ntiles = (cn + 15) >> 4;
-
-    // ---------------- Phase A: logits of the chunk ----------------
-    float wmax[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) wmax[g] = -INFINITY;
-    const uint32_t base_off = static_cast<uint32_t>(c0 >> 4) * kTileBytes + lane * 16u;
-    if (c0 > lo) {  // first tiles of a later chunk (the first chunk's are already in flight)
-      rK = make_rsrc(K, static_cast<uint32_t>((c0 + cn + 15) >> 4) * kTileBytes);
-      rV = make_rsrc(V, static_cast<uint32_t>(c0 + cn) * kRowBytes);
-#pragma unroll
-      for (int u = 0; u < UA; ++u)
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c)
-          kr[u][c] = bload16<POLICY>(
-              rK, base_off + static_cast<uint32_t>(wave * UA + u) * kTileBytes + 1024u * c);
-    }
-    // Two register sets of UA tiles: the next set is requested before the
-    // current one is multiplied, so every wave keeps K loads in flight.
-    auto qk_tiles = [&](const u32x4_t (&kt)[UA][kChunks], int t0) {
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        if (t0 + u < ntiles) {
-          f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int c = 0; c < kChunks; ++c) s4 = mfma_chunk(qa[c], kt[u][c], s4, T());
-          const int i = (t0 + u) * 16 + r16;
-          float s[G];
-          const bool live = i < cn && (!VAR || c0 + i != masked);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            s[g] = live ? s4[g] * P.scale_log2 : -INFINITY;
-            wmax[g] = fmaxf(wmax[g], s[g]);
-          }
-          if (grp == 0) lds_put<G>(lds, i, s);
-        }
-      }
-    };
-    auto load_tiles = [&](u32x4_t (&kt)[UA][kChunks], int t0) {
+  if constexpr (ILV) {
+    // ======== Interleaved loop: K and V of each tile together ========
+    // For short streams (small batches, split-K, small budgets): both
+    // streams in flight from the first tile and no barrier until the end.
+    // The K tiles and V rows of [lo, hi) are read through descriptors that end
+    // at hi (whole tiles for K): the loop always requests the next set, and
+    // requests past the end return zeros without moving data, so the
+    // compiler's load counting stays exact and both sets stay in flight.
+    const int ntiles = (hi - lo + 15) >> 4;
+    const __amdgpu_buffer_rsrc_t rK =
+        make_rsrc(K, static_cast<uint32_t>((hi + 15) >> 4) * kTileBytes);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(hi) * kRowBytes);
+    const uint32_t kbase = static_cast<uint32_t>(lo >> 4) * kTileBytes + lane * 16u;
+    const uint32_t vbase = static_cast<uint32_t>(lo + vsub) * kRowBytes + vcol * kBytes;
+    // One set = UA tiles: their K (kChunks loads each) and the V rows of the
+    // same slots (kVLoads loads each).
+    auto load_set = [&](u32x4_t (&kt)[UA][kChunks], u32x4_t (&vt)[UA][kVLoads], int t0) {
 #pragma unroll
       for (int u = 0; u < UA; ++u)
 #pragma unroll
         for (int c = 0; c < kChunks; ++c)
           kt[u][c] = bload16<POLICY>(
-              rK, base_off + static_cast<uint32_t>(t0 + u) * kTileBytes + 1024u * c);
+              rK, kbase + static_cast<uint32_t>(t0 + u) * kTileBytes + 1024u * c);
+#pragma unroll
+      for (int u = 0; u < UA; ++u)
+#pragma unroll
+        for (int j = 0; j < kVLoads; ++j)
+          vt[u][j] = bload16<POLICY>(
+              rV, vbase + static_cast<uint32_t>((t0 + u) * 16 + j * SPI) * kRowBytes);
     };
-    constexpr int kStepA = WAVES * UA;
-    u32x4_t kr2[UA][kChunks];
-    for (int t0 = wave * UA; t0 < ntiles; t0 += 2 * kStepA) {
-      load_tiles(kr2, t0 + kStepA);
-      qk_tiles(kr, t0);
-      load_tiles(kr, t0 + 2 * kStepA);
-      qk_tiles(kr2, t0 + kStepA);
+
+    // The first set goes out before anything else.
+    u32x4_t kr[UA][kChunks], vr[UA][kVLoads];
+    load_set(kr, vr, wave * UA);
+
+    // Query operand in the MFMA A layout: lane = row (query head row % G) +
+    // 16 * (16-byte chunk group); the same byte offsets as the key loads.
+    u32x4_t qa[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      qa[c] = load16(qg + (r16 % G) * D + (64 * c + 16 * grp) / kBytes);
+
+    // Sidecar of the slots this thread scores (the first kScoreBatch of them),
+    // requested now so the score pass finds it in registers.
+    const __amdgpu_buffer_rsrc_t rN =
+        make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(hi) * 4u);
+    float vnb[kScoreBatch];
+    if (!SPLIT && scoring) {
+#pragma unroll
+      for (int k = 0; k < kScoreBatch; ++k)
+        vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rN, static_cast<int>((P.sink + tid + k * NT) * 4), 0, 0));
     }
 
-    // First V rows of the chunk go out before the softmax bookkeeping.
-    const int nq = (cn + SPI - 1) / SPI;
-    const uint32_t vbase = static_cast<uint32_t>(c0 + vsub) * kRowBytes + vcol * kBytes;
-    constexpr int kStepB = WAVES * UB;
-    u32x4_t vr[UB], vr2[UB];
-#pragma unroll
-    for (int u = 0; u < UB; ++u)
-      vr[u] = bload16<POLICY>(rV, vbase + static_cast<uint32_t>((wave * UB + u) * SPI) * kRowBytes);
-#pragma unroll
-    for (int u = 0; u < UB; ++u)
-      vr2[u] = bload16<POLICY>(
-          rV, vbase + static_cast<uint32_t>((wave * UB + kStepB + u) * SPI) * kRowBytes);
-
+    // ---------------- Stream: K and V of each tile together ----------------
+    // Every wave runs its own online softmax over its tiles (t = wave, wave +
+    // WAVES, ...). m_w is a reference maximum, raised (with acc and lsum
+    // rescaled) only when a logit exceeds it by more than kSlack, so
+    // p = exp2(s - m_w) stays below 2^kSlack and float32 sums cannot overflow.
+    // Per tile: the MFMA logits (raw values kept in LDS for the score pass
+    // when evicting), p for the 16 slots x G heads staged in this wave's strip
+    // of LDS, then the V rows of the same slots accumulated against p. Every
+    // lane holds all G logits of its slot (the four chunk groups hold copies),
+    // so p is split over the lanes: lane (grp, r16) evaluates head grp of slot
+    // r16 when grp < G, and keeps the running sum of its head's p.
+    const int hg = grp & (G - 1);  // this lane's head in the p and sum work
+    float m_w[G], lsum = 0.0f;
+    float acc[G][EPL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float m = wave_max(wmax[g]);
-      if (lane == 0) sh_part[wave][g] = m;
+      m_w[g] = kNoMax;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
     }
-    if (c0 == lo) new_token();
-    __syncthreads();  // logits, wave maxima and (first chunk) the new token visible
-
-    // ---------------- A2: running max, p = exp2(s - M), sums ----------------
-    float fac[G];
+    float* pst = &sh_pst[wave][0];
+    auto process = [&](const u32x4_t (&kt)[UA][kChunks], const u32x4_t (&vt)[UA][kVLoads], int t0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m_old = c0 == lo ? sh_snew[g] : m_run[g];
-      float m = m_old;
+      for (int u = 0; u < UA; ++u) {
+        const int t = t0 + u;
+        if (t < ntiles) {
+          f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) m = fmaxf(m, sh_part[w][g]);
-      m_run[g] = m;
-      fac[g] = exp2f(m_old - m);
+          for (int c = 0; c < kChunks; ++c) s4 = mfma_chunk(qa[c], kt[u][c], s4, T());
+          const int i = t * 16 + r16;  // slot - lo
+          const bool live = lo + i < hi && (!VAR || lo + i != masked);
+          float s[G];
+          bool bump = false;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= fac[g];
-    }
-    float lpart[G];
+          for (int g = 0; g < G; ++g) {
+            s[g] = live ? s4[g] * P.scale_log2 : -INFINITY;
+            bump = bump || s[g] > m_w[g] + kSlack;
+          }
+          if (EVICT && grp == 0) lds_put<G>(lds, i, s);
+          if (__builtin_amdgcn_ballot_w64(bump) != 0) {  // wave-uniform
 #pragma unroll
-    for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
-    // Split with a full cache: this pair's raw-logit area (no records otherwise).
-    const __amdgpu_buffer_rsrc_t rW =
-        make_rsrc(SPLIT && scoring ? P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G : nullptr,
-                  SPLIT && scoring ? static_cast<uint32_t>(slots_pad) * G * 4u : 0u);
-    for (int i = tid; i < ntiles * 16; i += NT) {  // masked slots hold -inf -> p = 0
-      float x[G];
-      lds_get<G>(lds, i, x);
-      if (SPLIT && scoring && i < cn)  // raw logits for the last split's score
-        ws_store_g<G>(rW, static_cast<uint32_t>(c0 + i) * G * 4u, x);
+            for (int g = 0; g < G; ++g) {
+              const float m_new = fmaxf(m_w[g], wave_max(s[g]));
+              const float f = __builtin_amdgcn_exp2f(m_w[g] - m_new);
+              m_w[g] = m_new;
+              if (hg == g) lsum *= f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        x[g] = __builtin_amdgcn_exp2f(x[g] - m_run[g]);  // v_exp_f32; -inf -> 0
-        lpart[g] += x[g];
+              for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
+            }
+          }
+          float sg = s[0], mg = m_w[0];
+#pragma unroll
+          for (int g = 1; g < G; ++g) {
+            sg = hg == g ? s[g] : sg;
+            mg = hg == g ? m_w[g] : mg;
+          }
+          const float pv = __builtin_amdgcn_exp2f(sg - mg);  // v_exp_f32; -inf -> 0
+          if (grp < G) {
+            pst[r16 * G + hg] = pv;
+            lsum += pv;
+          }
+          wave_lds_sync();  // every lane reads the strip after the lanes above wrote it
+#pragma unroll
+          for (int j = 0; j < kVLoads; ++j) {
+            float x[EPL];
+            unpack16(vt[u][j], x, T());
+            float pp[G];
+            lds_get<G>(pst, j * SPI + vsub, pp);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pp[g], x[e], acc[g][e]);
+          }
+          wave_lds_sync();  // and before the next tile overwrites it
+        }
       }
-      lds_put<G>(pbuf, i, x);
+    };
+    constexpr int kStep = WAVES * UA;
+    u32x4_t kr2[UA][kChunks], vr2[UA][kVLoads];
+    // The new token's terms are computed once the first tile is done (their
+    // inputs, requested before it, have arrived by then), or after the loop by
+    // a wave with no tile.
+    bool new_pending = true;
+    for (int t0 = wave * UA; t0 < ntiles; t0 += 2 * kStep) {
+      load_set(kr2, vr2, t0 + kStep);
+      process(kr, vr, t0);
+      if (new_pending) {
+        new_token();
+        new_pending = false;
+      }
+      load_set(kr, vr, t0 + 2 * kStep);
+      process(kr2, vr2, t0 + kStep);
     }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float sum = wave_sum(lpart[g]);
-      if (lane == 0) sh_part2[wave][g] = sum;
-    }
-    __syncthreads();  // p and the partial sums visible
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) sum += sh_part2[w][g];
-      l_run[g] = fmaf(l_run[g], fac[g], sum);
-      w_run[g] *= fac[g];
-    }
+    if (new_pending) new_token();
 
-    // ---------------- Phase C: score + argmin ----------------
-    // One workgroup per pair: runs while the first V rows are in flight.
-    // Only an evicting cache scores, and then the whole buffer is one chunk,
-    // so M and L are final here. With one victim per sequence the scores go
-    // to LDS and are published after the V pass (a global store here would
-    // slow the transition).
-    if (!SPLIT && EVICT && scoring) {
-      float inv_l[G];
+    // ---------------- Combine the waves ----------------
+    // Each wave's (m_w, sum, acc) goes to LDS; after one barrier every thread
+    // forms the workgroup's max and sum per query head and each wave's factor
+    // exp2(m_w - M), in one fixed order (so every thread holds the same bits;
+    // one workgroup per pair: the new token included with weight
+    // exp2(s_new - M)). Head g's sum is the sum over row g of the wave (lanes
+    // 16g .. 16g + 15).
+    const float lrow = row_sum(lsum);
 #pragma unroll
-      for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
-      for (int i0 = P.sink + tid; i0 < n; i0 += NT * kScoreBatch) {
-        if (i0 != P.sink + tid) {  // later batches (the first one was prefetched)
+    for (int off = LPS; off < kWave; off <<= 1)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off, kWave);
+    if (lane < LPS) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sh_red[wave][g][vcol + e] = acc[g][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) sh_part[wave][g] = m_w[g];
+    }
+    if (r16 == 0 && grp < G) sh_part2[wave][grp] = lrow;
+    __syncthreads();  // partials, raw logits and the new token visible
+    float gm[G], gl[G], fw[WAVES][G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float M = SPLIT ? kNoMax : sh_snew[g];
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh_part[w][g]);
+      float L = SPLIT ? 0.0f : __builtin_amdgcn_exp2f(sh_snew[g] - M);
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        fw[w][g] = __builtin_amdgcn_exp2f(sh_part[w][g] - M);
+        L = fmaf(sh_part2[w][g], fw[w][g], L);
+      }
+      gm[g] = M;
+      gl[g] = L;
+    }
+    if constexpr (!SPLIT) {
+      settle_loads();  // only finished prologue loads and zero-fill tail loads are pending
+#pragma unroll
+      for (int j = 0; j < kOutPer; ++j) {
+        const int idx = tid + j * NT;
+        if (idx < G * D) {
+          const int g = idx / D;
+          const int d = idx - g * D;
+          float o = 0.0f, fg[WAVES], mg = gm[0], lg = gl[0];
+#pragma unroll
+          for (int w = 0; w < WAVES; ++w) fg[w] = fw[w][0];
+#pragma unroll
+          for (int g2 = 1; g2 < G; ++g2) {
+            if (g == g2) {
+              mg = gm[g2];
+              lg = gl[g2];
+#pragma unroll
+              for (int w = 0; w < WAVES; ++w) fg[w] = fw[w][g2];
+            }
+          }
+#pragma unroll
+          for (int w = 0; w < WAVES; ++w) o = fmaf(sh_red[w][g][d], fg[w], o);
+          o = fmaf(__builtin_amdgcn_exp2f(sh_snew[g] - mg), to_f32(ov[j]), o);
+          from_f32(o / lg, out_rows() + g * D + d);
+        }
+      }
+
+      // ---------------- Score + argmin ----------------
+      // score_i = ||v_i|| * sum_g exp2(s_{g,i} - M_g) / L_g from the raw logits
+      // in LDS and the prefetched sidecar; (score, slot) argmin through DPP
+      // and LDS, lowest slot on ties. With one victim per sequence every score
+      // also goes to this pair's score vector for the sequence's deciding
+      // workgroup.
+      if (EVICT && scoring) {
+        float inv_l[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / gl[g];
+        const __amdgpu_buffer_rsrc_t rSc =
+            make_rsrc(shared ? P.ws_score + static_cast<int64_t>(pair) * slots_pad : nullptr,
+                      shared ? static_cast<uint32_t>(n) * 4u : 0u);
+        auto score_batch = [&](int i0) {
+#pragma unroll
+          for (int k = 0; k < kScoreBatch; ++k) {
+            const int i = i0 + k * NT;
+            if (i < n && (!VAR || i != masked)) {
+              float s[G];
+              lds_get<G>(lds, i, s);
+              float sc = __builtin_amdgcn_exp2f(s[0] - gm[0]) * inv_l[0];
+#pragma unroll
+              for (int g = 1; g < G; ++g) sc = fmaf(__builtin_amdgcn_exp2f(s[g] - gm[g]), inv_l[g], sc);
+              sc = sc * vnb[k];
+              if (shared) {
+                const float one[1] = {sc};
+                ws_store_g<1>(rSc, static_cast<uint32_t>(i) * 4u, one);
+              }
+              if (sc < best) {  // slots visited in increasing order: first minimum kept
+                best = sc;
+                best_i = i;
+              }
+            }
+          }
+        };
+        // The first batch's sidecar was requested in the prologue; later
+        // batches (budgets beyond NT * kScoreBatch slots) load their own.
+        score_batch(P.sink + tid);
+        for (int i0 = P.sink + tid + NT * kScoreBatch; i0 < n; i0 += NT * kScoreBatch) {
 #pragma unroll
           for (int k = 0; k < kScoreBatch; ++k)
             vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                 rN, static_cast<int>((i0 + k * NT) * 4), 0, 0));
+          score_batch(i0);
         }
+        wave_argmin(best, best_i);
+        if (lane == 0) {
+          sh_best_score[wave] = best;
+          sh_best_slot[wave] = best_i;
+        }
+        if (shared && tid == 0) ws_store(P.ws_nnorm + pair, sh_vn_new);
+      }
+    } else {
+      // ---------------- Split: publish this split's partial state ----------------
+      float* mine = P.ws_part + (static_cast<int64_t>(pair) * S + split) * kPart;
+      if (scoring) {
+        // Raw logits of this split's slots for the last split's score.
+        const __amdgpu_buffer_rsrc_t rW = make_rsrc(
+            P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(hi) * G * 4u);
+        for (int i = tid; i < hi - lo; i += NT) {
+          float x[G];
+          lds_get<G>(lds, i, x);
+          ws_store_g<G>(rW, static_cast<uint32_t>(lo + i) * G * 4u, x);
+        }
+      }
 #pragma unroll
-        for (int k = 0; k < kScoreBatch; ++k) {
-          const int i = i0 + k * NT;
-          if (i < n && (!VAR || i != masked)) {
-            float p[G];
-            lds_get<G>(lds, i, p);
-            float sc = p[0] * inv_l[0];
+      for (int g = 0; g < G; ++g) {
+        for (int d = tid; d < D; d += NT) {
+          float o = 0.0f;
 #pragma unroll
-            for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
-            sc = sc * vnb[k];
-            if (shared) lds[P.chunk * G + i] = sc;
-            if (sc < best) {  // slots visited in increasing order: first minimum kept
-              best = sc;
-              best_i = i;
+          for (int w = 0; w < WAVES; ++w) o = fmaf(sh_red[w][g][d], fw[w][g], o);
+          ws_store(mine + 2 * G + g * D + d, o);
+        }
+      }
+      if (tid == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          ws_store(mine + g, gm[g]);  // kNoMax for a split with no slots
+          ws_store(mine + G + g, gl[g]);
+        }
+      }
+      drain_stores();
+      __syncthreads();
+      if (tid == 0)
+        sh_ticket = __hip_atomic_fetch_add(P.arrive + pair, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+    }
+  } else {
+    // ======== Phased loop: K stream, softmax and score, then V stream ========
+    // For long streams: each wave keeps one stream in flight at a time, and
+    // the score is taken mid-stream while the first V rows are in flight.
+    float* pbuf = lds;  // p overwrites the logits in place
+    // K and V reads of the current chunk [c0, c0 + cn) go through descriptors
+    // that end where the chunk ends (whole tiles for K): the loops below always
+    // request the next register set, and requests past the chunk return zeros
+    // without moving data (so the compiler's load counting stays exact and
+    // both register sets stay in flight).
+    int cn = min(P.chunk, hi - lo);
+    int ntiles = (cn + 15) >> 4;
+    __amdgpu_buffer_rsrc_t rK = make_rsrc(K, static_cast<uint32_t>((lo + cn + 15) >> 4) * kTileBytes);
+    __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(lo + cn) * kRowBytes);
+
+    // First K tiles go out before anything else.
+    u32x4_t kr[UA][kChunks];
+    {
+      const uint32_t off0 = static_cast<uint32_t>(lo >> 4) * kTileBytes + lane * 16u;
+#pragma unroll
+      for (int u = 0; u < UA; ++u)
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c)
+          kr[u][c] = bload16<POLICY>(
+              rK, off0 + static_cast<uint32_t>(wave * UA + u) * kTileBytes + 1024u * c);
+    }
+
+    // Query operand in the MFMA A layout: lane = row (query head row % G) +
+    // 16 * (16-byte chunk group); the same byte offsets as the key loads.
+    u32x4_t qa[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      qa[c] = load16(qg + (r16 % G) * D + (64 * c + 16 * grp) / kBytes);
+
+    // Sidecar of the slots this thread scores (the first kScoreBatch of them),
+    // requested now so the score phase finds it in registers.
+    const int sc_lo = max(lo, P.sink);
+    const __amdgpu_buffer_rsrc_t rN =
+        make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(hi) * 4u);
+    float vnb[kScoreBatch];
+    if (!SPLIT && scoring) {
+#pragma unroll
+      for (int k = 0; k < kScoreBatch; ++k)
+        vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rN, static_cast<int>((sc_lo + tid + k * NT) * 4), 0, 0));
+    }
+
+    // Running softmax state, identical in every thread. One workgroup per
+    // pair: the new token opens it with weight exp2(s_new - s_new) = 1. Split:
+    // the partial holds the split's own slots only (the new token is added
+    // once, when the partials are combined).
+    float m_run[G], l_run[G], w_run[G];
+    float acc[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m_run[g] = -INFINITY;
+      l_run[g] = SPLIT ? 0.0f : 1.0f;
+      w_run[g] = SPLIT ? 0.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+    }
+
+    for (int c0 = lo; c0 < hi; c0 += P.chunk) {
+      cn = min(P.chunk, hi - c0);
+      ntiles = (cn + 15) >> 4;
+
+      // ---------------- Phase A: logits of the chunk ----------------
+      float wmax[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) wmax[g] = -INFINITY;
+      const uint32_t base_off = static_cast<uint32_t>(c0 >> 4) * kTileBytes + lane * 16u;
+      if (c0 > lo) {  // first tiles of a later chunk (the first chunk's are already in flight)
+        rK = make_rsrc(K, static_cast<uint32_t>((c0 + cn + 15) >> 4) * kTileBytes);
+        rV = make_rsrc(V, static_cast<uint32_t>(c0 + cn) * kRowBytes);
+#pragma unroll
+        for (int u = 0; u < UA; ++u)
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c)
+            kr[u][c] = bload16<POLICY>(
+                rK, base_off + static_cast<uint32_t>(wave * UA + u) * kTileBytes + 1024u * c);
+      }
+      // Two register sets of UA tiles: the next set is requested before the
+      // current one is multiplied, so every wave keeps K loads in flight.
+      auto qk_tiles = [&](const u32x4_t (&kt)[UA][kChunks], int t0) {
+#pragma unroll
+        for (int u = 0; u < UA; ++u) {
+          if (t0 + u < ntiles) {
+            f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c) s4 = mfma_chunk(qa[c], kt[u][c], s4, T());
+            const int i = (t0 + u) * 16 + r16;
+            float s[G];
+            const bool live = i < cn && (!VAR || c0 + i != masked);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              s[g] = live ? s4[g] * P.scale_log2 : -INFINITY;
+              wmax[g] = fmaxf(wmax[g], s[g]);
+            }
+            if (grp == 0) lds_put<G>(lds, i, s);
+          }
+        }
+      };
+      auto load_tiles = [&](u32x4_t (&kt)[UA][kChunks], int t0) {
+#pragma unroll
+        for (int u = 0; u < UA; ++u)
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c)
+            kt[u][c] = bload16<POLICY>(
+                rK, base_off + static_cast<uint32_t>(t0 + u) * kTileBytes + 1024u * c);
+      };
+      constexpr int kStepA = WAVES * UA;
+      u32x4_t kr2[UA][kChunks];
+      for (int t0 = wave * UA; t0 < ntiles; t0 += 2 * kStepA) {
+        load_tiles(kr2, t0 + kStepA);
+        qk_tiles(kr, t0);
+        load_tiles(kr, t0 + 2 * kStepA);
+        qk_tiles(kr2, t0 + kStepA);
+      }
+
+      // First V rows of the chunk go out before the softmax bookkeeping.
+      const int nq = (cn + SPI - 1) / SPI;
+      const uint32_t vbase = static_cast<uint32_t>(c0 + vsub) * kRowBytes + vcol * kBytes;
+      constexpr int kStepB = WAVES * UB;
+      u32x4_t vr[UB], vr2[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        vr[u] = bload16<POLICY>(rV, vbase + static_cast<uint32_t>((wave * UB + u) * SPI) * kRowBytes);
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        vr2[u] = bload16<POLICY>(
+            rV, vbase + static_cast<uint32_t>((wave * UB + kStepB + u) * SPI) * kRowBytes);
+
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float m = wave_max(wmax[g]);
+        if (lane == 0) sh_part[wave][g] = m;
+      }
+      if (c0 == lo) new_token();
+      __syncthreads();  // logits, wave maxima and (first chunk) the new token visible
+
+      // ---------------- A2: running max, p = exp2(s - M), sums ----------------
+      float fac[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float m_old = c0 == lo ? sh_snew[g] : m_run[g];
+        float m = m_old;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) m = fmaxf(m, sh_part[w][g]);
+        m_run[g] = m;
+        fac[g] = exp2f(m_old - m);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= fac[g];
+      }
+      float lpart[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
+      // Split with a full cache: this pair's raw-logit area (no records otherwise).
+      const __amdgpu_buffer_rsrc_t rW =
+          make_rsrc(SPLIT && scoring ? P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G : nullptr,
+                    SPLIT && scoring ? static_cast<uint32_t>(slots_pad) * G * 4u : 0u);
+      for (int i = tid; i < ntiles * 16; i += NT) {  // masked slots hold -inf -> p = 0
+        float x[G];
+        lds_get<G>(lds, i, x);
+        if (SPLIT && scoring && i < cn)  // raw logits for the last split's score
+          ws_store_g<G>(rW, static_cast<uint32_t>(c0 + i) * G * 4u, x);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          x[g] = __builtin_amdgcn_exp2f(x[g] - m_run[g]);  // v_exp_f32; -inf -> 0
+          lpart[g] += x[g];
+        }
+        lds_put<G>(pbuf, i, x);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float sum = wave_sum(lpart[g]);
+        if (lane == 0) sh_part2[wave][g] = sum;
+      }
+      __syncthreads();  // p and the partial sums visible
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) sum += sh_part2[w][g];
+        l_run[g] = fmaf(l_run[g], fac[g], sum);
+        w_run[g] *= fac[g];
+      }
+
+      // ---------------- Phase C: score + argmin ----------------
+      // One workgroup per pair: runs while the first V rows are in flight.
+      // Only an evicting cache scores, and then the whole buffer is one chunk,
+      // so M and L are final here. With one victim per sequence the scores go
+      // to LDS and are published after the V pass (a global store here would
+      // slow the transition).
+      if (!SPLIT && EVICT && scoring) {
+        float inv_l[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) inv_l[g] = 1.0f / l_run[g];
+        for (int i0 = P.sink + tid; i0 < n; i0 += NT * kScoreBatch) {
+          if (i0 != P.sink + tid) {  // later batches (the first one was prefetched)
+#pragma unroll
+            for (int k = 0; k < kScoreBatch; ++k)
+              vnb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                  rN, static_cast<int>((i0 + k * NT) * 4), 0, 0));
+          }
+#pragma unroll
+          for (int k = 0; k < kScoreBatch; ++k) {
+            const int i = i0 + k * NT;
+            if (i < n && (!VAR || i != masked)) {
+              float p[G];
+              lds_get<G>(lds, i, p);
+              float sc = p[0] * inv_l[0];
+#pragma unroll
+              for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
+              sc = sc * vnb[k];
+              if (shared) lds[P.chunk * G + i] = sc;
+              if (sc < best) {  // slots visited in increasing order: first minimum kept
+                best = sc;
+                best_i = i;
+              }
             }
           }
         }
-      }
-      wave_argmin(best, best_i);
-      if (lane == 0) {
-        sh_best_score[wave] = best;
-        sh_best_slot[wave] = best_i;
-      }
-    }
-
-    // ---------------- Phase B: o += p * v over the chunk ----------------
-    // Two register sets of UB rows, as for K.
-    auto pv_rows = [&](const u32x4_t (&vt)[UB], int q0) {
-#pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        if (q0 + u < nq) {  // rows past the chunk have p = 0 (and load as 0 past n)
-          const int r = (q0 + u) * SPI + vsub;
-          float x[EPL];
-          unpack16(vt[u], x, T());
-          float p[G];
-          lds_get<G>(pbuf, r, p);
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g], x[e], acc[g][e]);
+        wave_argmin(best, best_i);
+        if (lane == 0) {
+          sh_best_score[wave] = best;
+          sh_best_slot[wave] = best_i;
         }
       }
-    };
-    auto load_rows = [&](u32x4_t (&vt)[UB], int q0) {
+
+      // ---------------- Phase B: o += p * v over the chunk ----------------
+      // Two register sets of UB rows, as for K.
+      auto pv_rows = [&](const u32x4_t (&vt)[UB], int q0) {
 #pragma unroll
-      for (int u = 0; u < UB; ++u)
-        vt[u] = bload16<POLICY>(rV, vbase + static_cast<uint32_t>((q0 + u) * SPI) * kRowBytes);
-    };
-    for (int q0 = wave * UB; q0 < nq; q0 += 2 * kStepB) {
-      pv_rows(vr, q0);
-      load_rows(vr, q0 + 2 * kStepB);
-      pv_rows(vr2, q0 + kStepB);
-      load_rows(vr2, q0 + 3 * kStepB);
+        for (int u = 0; u < UB; ++u) {
+          if (q0 + u < nq) {  // rows past the chunk have p = 0 (and load as 0 past n)
+            const int r = (q0 + u) * SPI + vsub;
+            float x[EPL];
+            unpack16(vt[u], x, T());
+            float p[G];
+            lds_get<G>(pbuf, r, p);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g], x[e], acc[g][e]);
+          }
+        }
+      };
+      auto load_rows = [&](u32x4_t (&vt)[UB], int q0) {
+#pragma unroll
+        for (int u = 0; u < UB; ++u)
+          vt[u] = bload16<POLICY>(rV, vbase + static_cast<uint32_t>((q0 + u) * SPI) * kRowBytes);
+      };
+      for (int q0 = wave * UB; q0 < nq; q0 += 2 * kStepB) {
+        pv_rows(vr, q0);
+        load_rows(vr, q0 + 2 * kStepB);
+        pv_rows(vr2, q0 + kStepB);
+        load_rows(vr2, q0 + 3 * kStepB);
+      }
+      if (c0 + P.chunk < hi) __syncthreads();  // the next chunk overwrites the LDS logits
     }
-    if (c0 + P.chunk < hi) __syncthreads();  // the next chunk overwrites the LDS logits
-  }
 
-  if (lo >= hi) new_token();  // no slot for this workgroup: nothing streamed
+    if (lo >= hi) new_token();  // no slot for this workgroup: nothing streamed
 
-  // ---------------- Phase D: cross-wave output reduction ----------------
+    // ---------------- Phase D: cross-wave output reduction ----------------
 #pragma unroll
-  for (int off = LPS; off < kWave; off <<= 1)
+    for (int off = LPS; off < kWave; off <<= 1)
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off, kWave);
-  if (lane < LPS) {
+        for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off, kWave);
+    if (lane < LPS) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sh_red[wave][g][vcol + e] = acc[g][e];
-  }
-  __syncthreads();
-  T* out = static_cast<T*>(P.out) + (static_cast<int64_t>(b) * P.num_q_heads + h * G) * D;
+        for (int e = 0; e < EPL; ++e) sh_red[wave][g][vcol + e] = acc[g][e];
+    }
+    __syncthreads();
 
-  if constexpr (!SPLIT) {
-    settle_loads();  // only finished prologue loads and zero-fill tail loads are pending
+    if constexpr (!SPLIT) {
+      settle_loads();  // only finished prologue loads and zero-fill tail loads are pending
 #pragma unroll
-    for (int j = 0; j < kOutPer; ++j) {
-      const int idx = tid + j * NT;
-      if (idx < G * D) {
+      for (int j = 0; j < kOutPer; ++j) {
+        const int idx = tid + j * NT;
+        if (idx < G * D) {
+          const int g = idx / D;
+          const int d = idx - g * D;
+          float o = 0.0f;
+#pragma unroll
+          for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
+          o = fmaf(w_run[g], to_f32(ov[j]), o);
+          from_f32(o / l_run[g], out_rows() + g * D + d);
+        }
+      }
+      if (EVICT && scoring && shared) {
+        // One victim per sequence: publish this head's score vector (in LDS
+        // since the score phase) and its new token's norm for the sequence's
+        // deciding workgroup. Whole 16-byte groups; entries the score phase
+        // skipped (sinks, the replaced slot) are never read back.
+        const float* lsc = lds + P.chunk * G;
+        const __amdgpu_buffer_rsrc_t rSc = make_rsrc(
+            P.ws_score + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(slots_pad) * 4u);
+        for (int q4 = tid; 4 * q4 < n; q4 += NT) {
+          const u32x4_t v4 = *reinterpret_cast<const u32x4_t*>(lsc + 4 * q4);
+          __builtin_amdgcn_raw_buffer_store_b128(v4, rSc, 16 * q4, 0, kDeviceScope);
+        }
+        if (tid == 0) ws_store(P.ws_nnorm + pair, sh_vn_new);
+      }
+    } else {
+      // ---------------- Split: publish this split's partial state ----------------
+      float* mine = P.ws_part + (static_cast<int64_t>(pair) * S + split) * kPart;
+      for (int idx = tid; idx < G * D; idx += NT) {
         const int g = idx / D;
         const int d = idx - g * D;
         float o = 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
-        o = fmaf(w_run[g], to_f32(ov[j]), o);
-        from_f32(o / l_run[g], out + g * D + d);
+        ws_store(mine + 2 * G + idx, o);
       }
-    }
-    if (EVICT && scoring && shared) {
-      // One victim per sequence: publish this head's score vector (in LDS
-      // since the score phase) and its new token's norm for the sequence's
-      // deciding workgroup. Whole 16-byte groups; entries the score phase
-      // skipped (sinks, the replaced slot) are never read back.
-      const float* lsc = lds + P.chunk * G;
-      const __amdgpu_buffer_rsrc_t rSc = make_rsrc(
-          P.ws_score + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(slots_pad) * 4u);
-      for (int q4 = tid; 4 * q4 < n; q4 += NT) {
-        const u32x4_t v4 = *reinterpret_cast<const u32x4_t*>(lsc + 4 * q4);
-        __builtin_amdgcn_raw_buffer_store_b128(v4, rSc, 16 * q4, 0, kDeviceScope);
+      if (tid < G) {
+        ws_store(mine + tid, m_run[tid]);  // -inf for a split with no slots
+        ws_store(mine + G + tid, l_run[tid]);
       }
-      if (tid == 0) ws_store(P.ws_nnorm + pair, sh_vn_new);
+      drain_stores();
+      __syncthreads();
+      if (tid == 0)
+        sh_ticket = __hip_atomic_fetch_add(P.arrive + pair, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
     }
-  } else {
-    // ---------------- Split: publish this split's partial state ----------------
-    constexpr int kPart = 2 * G + G * D;
-    const int S = P.splits;
-    float* mine = P.ws_part + (static_cast<int64_t>(pair) * S + split) * kPart;
-    for (int idx = tid; idx < G * D; idx += NT) {
-      const int g = idx / D;
-      const int d = idx - g * D;
-      float o = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) o += sh_red[w][g][d];
-      ws_store(mine + 2 * G + idx, o);
-    }
-    if (tid < G) {
-      ws_store(mine + tid, m_run[tid]);  // -inf for a split with no slots
-      ws_store(mine + G + tid, l_run[tid]);
-    }
-    drain_stores();
-    __syncthreads();
-    if (tid == 0)
-      sh_ticket = __hip_atomic_fetch_add(P.arrive + pair, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
+  }
+
+  if constexpr (SPLIT) {
     if (sh_ticket != S - 1) return;  // not the last split of the pair
 
     // ---------------- Last split: combine, score ----------------
@@ -895,11 +1245,11 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
     if (scoring) {
       // Score every slot from the published raw logits: the same operations
       // as one workgroup per pair, so equal tokens get bit-equal scores.
-      float inv_l[G], gm[G];
+      float inv_l[G], pm[G];  // the pair's sums and maxima
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         inv_l[g] = 1.0f / sh_gl[g];
-        gm[g] = sh_gm[g];
+        pm[g] = sh_gm[g];
       }
       const __amdgpu_buffer_rsrc_t rSc =
           make_rsrc(shared ? P.ws_score + static_cast<int64_t>(pair) * slots_pad : nullptr,
@@ -912,7 +1262,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
           if (i < n && (!VAR || i != masked)) {
             float p[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) p[g] = __builtin_amdgcn_exp2f(lg[k][g] - gm[g]);
+            for (int g = 0; g < G; ++g) p[g] = __builtin_amdgcn_exp2f(lg[k][g] - pm[g]);
             float sc = p[0] * inv_l[0];
 #pragma unroll
             for (int g = 1; g < G; ++g) sc = fmaf(p[g], inv_l[g], sc);
@@ -937,12 +1287,11 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
 #pragma unroll
     for (int j = 0; j < kOutPer; ++j) {
       const int idx = tid + j * NT;  // = g * D + d
-      if (idx < G * D) from_f32(ofin[j], out + idx);
+      if (idx < G * D) from_f32(ofin[j], out_rows() + idx);
     }
     if (shared && scoring && tid == 0) ws_store(P.ws_nnorm + pair, sh_vn_new);
     if (tid == 0) __hip_atomic_store(P.arrive + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-
   // ---------------- Choice of the victim ----------------
   // One victim per pair: the cross-wave argmin of this workgroup, lowest slot
   // on ties. One victim per sequence: every KV head has published its score
@@ -1109,7 +1458,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   if (tid == 0) P.vnorm[static_cast<int64_t>(pair) * slots_pad + slot] = sh_vn_new;
 }
 
-template <typename T, int D, int G, bool EVICT, bool SPLIT, bool VAR, int WAVES,
+template <typename T, int D, int G, bool EVICT, bool SPLIT, bool VAR, int WAVES, bool ILV,
           int UA = 1, int UB = 4, int POLICY = kStream>
 hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitWork& W, int splits,
                            const void* q, const void* k_new, const void* v_new, void* out,
@@ -1145,13 +1494,13 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   P.ws_part = W.part;
   P.ws_logit = W.logit;
   P.arrive = W.arrive;
-  const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits) : decode_lds_bytes(geo);
+  const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits, ILV) : decode_lds_bytes(geo, ILV);
   if (lds == 0) return hipErrorInvalidValue;
-  // One workgroup per pair with one victim per sequence: the pair's scores
-  // follow the logits in LDS.
-  const size_t score_lds = !SPLIT ? decode_score_lds_bytes(geo) : 0;
-  P.chunk = static_cast<int32_t>((lds - score_lds) / (sizeof(float) * G));  // EVICT: a whole split (or pair)
-  auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR>;
+  // Phased loop, one workgroup per pair with one victim per sequence: the
+  // pair's scores follow the logits in LDS.
+  const size_t score_lds = !ILV && !SPLIT ? decode_score_lds_bytes(geo) : 0;
+  P.chunk = static_cast<int32_t>((lds - score_lds) / (sizeof(float) * G));
+  auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR, ILV>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1165,14 +1514,14 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
 }
 
 // Dispatch over dtype, head_dim, group width, mode, split and variants for
-// one workgroup size.
-template <int WAVES>
+// one workgroup size and loop kind.
+template <int WAVES, bool ILV>
 hipError_t launch_decode_waves(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
                                const void* q, const void* k_new, const void* v_new, void* out,
                                int32_t* evicted, hipStream_t stream) {
   const bool var = g.order != 0 || g.scope != 0;
 #define LF_LAUNCH(T, D, G, EVICT, SPLIT, VAR) \
-  launch_decode_t<T, D, G, EVICT, SPLIT, VAR, WAVES>(g, L, W, SPLIT ? splits : 1, q, k_new, v_new, out, evicted, stream)
+  launch_decode_t<T, D, G, EVICT, SPLIT, VAR, WAVES, ILV>(g, L, W, SPLIT ? splits : 1, q, k_new, v_new, out, evicted, stream)
 #define LF_CASE(T, D, G)                                                                      \
   if (g.head_dim == D && g.group == G) {                                                     \
     if (g.mode != 0)                                                                         \

@@ -1,4 +1,4 @@
-// Decode kernel instances with 8 waves per workgroup (see lf_decode.h).
+// Decode kernel instances with 8 waves per workgroup, phased loop (long streams) (see lf_decode.h).
 #include "lf_decode.h"
 
 namespace lf {
@@ -6,7 +6,7 @@ namespace lf {
 hipError_t launch_decode_w8(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
                              const void* q, const void* k_new, const void* v_new, void* out,
                              int32_t* evicted, hipStream_t stream) {
-  return launch_decode_waves<8>(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
+  return launch_decode_waves<8, false>(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
 }
 
 }  // namespace lf

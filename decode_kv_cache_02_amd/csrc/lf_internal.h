@@ -58,12 +58,18 @@ constexpr int kMaxSplits = 16;
 constexpr int kSplitGridTarget = 512;
 constexpr int kSplitPairsBelow = 256;
 constexpr int kMinSplitSlots = 256;   // fewer slots per split are not worth a split
+// Launches whose workgroups stream at most this many slots use the
+// interleaved loop (K and V of each tile together, both streams in flight
+// from the start); longer streams use the phased loop (K, then V).
+constexpr int kInterleaveSlots = 1024;
 
-// Dynamic LDS bytes the decode kernel needs for this geometry, or 0 if the
-// combination (dtype, head_dim, group, slots) is not built.
-size_t decode_lds_bytes(const Geometry& g);
-size_t decode_score_lds_bytes(const Geometry& g);  // part of decode_lds_bytes
-size_t decode_split_lds_bytes(const Geometry& g, int splits);
+// Dynamic LDS bytes the decode kernel needs for this geometry and loop kind
+// (ilv: interleaved), or 0 if the combination (dtype, head_dim, group,
+// slots) is not built. decode_score_lds_bytes is the part the phased loop
+// keeps for the scores of one victim per sequence.
+size_t decode_lds_bytes(const Geometry& g, bool ilv);
+size_t decode_split_lds_bytes(const Geometry& g, int splits, bool ilv);
+size_t decode_score_lds_bytes(const Geometry& g);
 size_t split_part_floats(const Geometry& g);
 
 // LDS bytes one workgroup may use on the current device.
@@ -72,16 +78,19 @@ size_t device_lds_limit();
 // splits == 1: one workgroup per pair. splits > 1: split-K over `splits`
 // workgroups per pair (W must then hold room for that many). waves: 4 or 8
 // waves of 64 lanes per workgroup (8 when one workgroup per CU is all the
-// launch has).
+// launch has). ilv: the interleaved loop instead of the phased one.
 hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits, int waves,
-                         const void* q, const void* k_new, const void* v_new, void* out,
+                         bool ilv, const void* q, const void* k_new, const void* v_new, void* out,
                          int32_t* evicted, hipStream_t stream);
-hipError_t launch_decode_w4(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
-                            const void* q, const void* k_new, const void* v_new, void* out,
-                            int32_t* evicted, hipStream_t stream);
-hipError_t launch_decode_w8(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
-                            const void* q, const void* k_new, const void* v_new, void* out,
-                            int32_t* evicted, hipStream_t stream);
+#define LF_DECLARE_DECODE_UNIT(NAME)                                                          \
+  hipError_t NAME(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,    \
+                  const void* q, const void* k_new, const void* v_new, void* out,           \
+                  int32_t* evicted, hipStream_t stream);
+LF_DECLARE_DECODE_UNIT(launch_decode_w4)   // lf_decode_w4.hip: 4 waves, phased
+LF_DECLARE_DECODE_UNIT(launch_decode_w8)   // lf_decode_w8.hip: 8 waves, phased
+LF_DECLARE_DECODE_UNIT(launch_decode_w4i)  // lf_decode_w4i.hip: 4 waves, interleaved
+LF_DECLARE_DECODE_UNIT(launch_decode_w8i)  // lf_decode_w8i.hip: 8 waves, interleaved
+#undef LF_DECLARE_DECODE_UNIT
 
 // Static LDS of a decode workgroup of `waves` waves (per-wave output
 // partials and reduction scratch), an upper bound.

@@ -1,7 +1,8 @@
 // gfx950 (MI355X) kernels around the decode step: the initial fill, sequence
 // recycling, LDS sizing, and the choice of workgroup size for a decode launch.
-// The decode kernel itself is in lf_decode.h, instantiated by lf_decode_w4.hip
-// and lf_decode_w8.hip.
+// The decode kernel itself is in lf_decode.h, instantiated by lf_decode_w4.hip,
+// lf_decode_w8.hip (phased loop) and lf_decode_w4i.hip, lf_decode_w8i.hip
+// (interleaved loop).
 #include "lf_decode.h"
 
 namespace lf {
@@ -129,39 +130,44 @@ size_t device_lds_limit() {
 }
 
 size_t decode_static_lds_bytes(const Geometry& g, int waves) {
-  // sh_red[waves][group][head_dim] floats plus the small per-wave arrays
-  return static_cast<size_t>(waves) * g.group * g.head_dim * sizeof(float) + 1024;
+  // sh_red[waves][group][head_dim] and sh_pst[waves][16 * group] floats, plus
+  // the small per-wave arrays
+  return static_cast<size_t>(waves) * g.group * (g.head_dim + 16) * sizeof(float) + 1024;
 }
 
-// Logits of one LDS-resident chunk: the whole pair when evicting (the score
-// needs every slot's probabilities), 2048-slot chunks in FULL mode; 0 when
-// the combination is not built or does not fit.
-size_t decode_logit_lds_bytes(const Geometry& g) {
-  if (g.head_dim != 64 && g.head_dim != 128) return 0;
-  if (g.group != 1 && g.group != 2 && g.group != 4) return 0;
-  if (g.dtype != 0 && g.dtype != 1) return 0;
-  if (g.mode == 0) {
-    const size_t logits = static_cast<size_t>(g.slots_pad) * g.group * sizeof(float);
-    return logits > kEvictLdsCap ? 0 : logits;
-  }
-  const size_t slots = g.slots_pad < static_cast<int>(kFullChunkSlots) ? g.slots_pad : kFullChunkSlots;
-  return slots * g.group * sizeof(float);
+namespace {
+bool decode_built(const Geometry& g) {
+  return (g.head_dim == 64 || g.head_dim == 128) && (g.group == 1 || g.group == 2 || g.group == 4) &&
+         (g.dtype == 0 || g.dtype == 1);
 }
+}  // namespace
 
 size_t decode_score_lds_bytes(const Geometry& g) {
   return g.mode == 0 && g.scope == 1 ? static_cast<size_t>(g.slots_pad) * sizeof(float) : 0;
 }
 
-size_t decode_lds_bytes(const Geometry& g) {
-  const size_t logits = decode_logit_lds_bytes(g);
-  if (logits == 0) return 0;
-  const size_t total = logits + decode_score_lds_bytes(g);
+// Dynamic LDS of one workgroup per pair.
+//   Evicting: the raw logits of the whole pair (the score needs every
+//   slot's); the phased loop with one victim per sequence also keeps the
+//   pair's scores.
+//   FULL: the phased loop keeps the logits of one 2048-slot chunk at a time;
+//   the interleaved loop keeps none (a nominal 16 bytes).
+// 0 when the combination is not built or does not fit.
+size_t decode_lds_bytes(const Geometry& g, bool ilv) {
+  if (!decode_built(g)) return 0;
+  if (g.mode != 0) {
+    if (ilv) return 16;
+    const size_t slots = g.slots_pad < static_cast<int>(kFullChunkSlots) ? g.slots_pad : kFullChunkSlots;
+    return slots * g.group * sizeof(float);
+  }
+  const size_t logits = static_cast<size_t>(g.slots_pad) * g.group * sizeof(float);
+  const size_t total = logits + (ilv ? 0 : decode_score_lds_bytes(g));
   return total > kEvictLdsCap ? 0 : total;
 }
 
-size_t decode_split_lds_bytes(const Geometry& g, int splits) {
-  if (decode_lds_bytes(g) == 0 || splits < 1) return 0;
-  if (g.mode != 0) return decode_lds_bytes(g);  // FULL: chunked, as without splits
+size_t decode_split_lds_bytes(const Geometry& g, int splits, bool ilv) {
+  if (decode_lds_bytes(g, ilv) == 0 || splits < 1) return 0;
+  if (g.mode != 0) return decode_lds_bytes(g, ilv);  // FULL: as without splits
   const int tiles = g.slots_pad / 16;
   const int per = (tiles + splits - 1) / splits;
   return static_cast<size_t>(per) * 16 * g.group * sizeof(float);  // one split's logits
@@ -172,12 +178,14 @@ size_t split_part_floats(const Geometry& g) {
 }
 
 hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits, int waves,
-                         const void* q, const void* k_new, const void* v_new, void* out,
+                         bool ilv, const void* q, const void* k_new, const void* v_new, void* out,
                          int32_t* evicted, hipStream_t stream) {
   if (waves == 8)
-    return launch_decode_w8(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
+    return ilv ? launch_decode_w8i(g, L, W, splits, q, k_new, v_new, out, evicted, stream)
+               : launch_decode_w8(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
   if (waves == 4)
-    return launch_decode_w4(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
+    return ilv ? launch_decode_w4i(g, L, W, splits, q, k_new, v_new, out, evicted, stream)
+               : launch_decode_w4(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
   return hipErrorInvalidValue;
 }
 

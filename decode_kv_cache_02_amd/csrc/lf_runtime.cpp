@@ -44,6 +44,7 @@ struct lf_cache {
   int32_t max_splits;              // 1: no split launches
   int32_t forced_splits;           // 0: plan automatically
   int32_t forced_waves;            // 0: plan automatically
+  int32_t forced_loop;             // 0: plan automatically, 1: phased, 2: interleaved
   int32_t cus;                     // compute units of the device
   size_t lds_limit;                // LDS bytes one workgroup may use
 };
@@ -223,6 +224,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 //   - With fewer pairs, each pair splits over up to cus / pairs workgroups
 //     (at most max_splits, at least kMinSplitSlots slots per split of the
 //     fullest pair), so the launch holds about one workgroup per CU.
+//   - Workgroups that stream at most kInterleaveSlots slots run the
+//     interleaved loop (K and V of each tile together); longer streams run
+//     the phased loop (K, then V).
 //   - A launch of at most one workgroup per CU uses 8 waves per workgroup,
 //     otherwise 4 (two workgroups per CU). This needs the 8-wave
 //     workgroup's LDS to fit.
@@ -230,6 +234,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct LaunchShape {
   int32_t splits;
   int32_t waves;
+  bool ilv;  // interleaved loop (short streams) instead of the phased one
 };
 
 LaunchShape plan_launch(const lf_cache* c, int32_t n_max) {
@@ -244,12 +249,16 @@ LaunchShape plan_launch(const lf_cache* c, int32_t n_max) {
       s = static_cast<int32_t>(std::min<int64_t>({c->max_splits, by_grid, by_work}));
     }
   }
-  const size_t dyn = s > 1 ? lf::decode_split_lds_bytes(c->geo, s) : lf::decode_lds_bytes(c->geo);
+  // Slots one workgroup streams: short streams take the interleaved loop.
+  const int32_t per_wg = (n_max + s - 1) / s;
+  bool ilv = per_wg <= lf::kInterleaveSlots;
+  if (c->forced_loop > 0) ilv = c->forced_loop == 2;
+  const size_t dyn = s > 1 ? lf::decode_split_lds_bytes(c->geo, s, ilv) : lf::decode_lds_bytes(c->geo, ilv);
   const bool fits8 = dyn + lf::decode_static_lds_bytes(c->geo, 8) <= c->lds_limit;
   int32_t waves = pairs * s <= c->cus ? 8 : 4;
   if (c->forced_waves > 0) waves = c->forced_waves;
   if (waves == 8 && !fits8) waves = 4;
-  return {s, waves};
+  return {s, waves, ilv};
 }
 
 }  // namespace
@@ -287,7 +296,9 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   lf_status s = validate(cfg);
   if (s != LF_OK) return s;
   const lf::Geometry geo = geometry(cfg);
-  const size_t lds = lf::decode_lds_bytes(geo);
+  // The phased loop needs the most LDS (it also keeps the scores of one
+  // victim per sequence); every launch then fits either loop.
+  const size_t lds = lf::decode_lds_bytes(geo, false);
   if (lds == 0) return LF_ERR_UNSUPPORTED;
   int device = -1;
   if (hipGetDevice(&device) != hipSuccess) {
@@ -343,6 +354,7 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->max_splits = max_splits;
   c->forced_splits = 0;
   c->forced_waves = 0;
+  c->forced_loop = 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
     cus = 256;
@@ -405,6 +417,12 @@ lf_status lf_cache_set_splits(lf_cache* c, int32_t splits) {
 lf_status lf_cache_set_waves(lf_cache* c, int32_t waves) {
   if (!c || (waves != 0 && waves != 4 && waves != 8)) return LF_ERR_INVALID_ARG;
   c->forced_waves = waves;
+  return LF_OK;
+}
+
+lf_status lf_cache_set_loop(lf_cache* c, int32_t loop) {
+  if (!c || loop < 0 || loop > 2) return LF_ERR_INVALID_ARG;
+  c->forced_loop = loop;
   return LF_OK;
 }
 
@@ -494,7 +512,7 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
   int32_t n_max = 0;
   for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
   const LaunchShape shape = plan_launch(c, n_max);
-  if (lf::launch_decode(c->geo, p, c->work, shape.splits, shape.waves, q, k_new, v_new, out,
+  if (lf::launch_decode(c->geo, p, c->work, shape.splits, shape.waves, shape.ilv, q, k_new, v_new, out,
                         evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {
     (void)hipGetLastError();
     return LF_ERR_HIP;

@@ -90,6 +90,7 @@ SIGNATURES = [
                                      ctypes.c_void_p]),
     ("lf_cache_set_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_set_waves", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    ("lf_cache_set_loop", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_max_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_fill_levels", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_cache_destroy", None, [ctypes.c_void_p]),
@@ -232,6 +233,14 @@ def lf_cache_set_waves(handle: int, waves: int) -> None:
            "lf_cache_set_waves")
 
 
+LOOPS = {"auto": 0, "phased": 1, "interleaved": 2}
+
+
+def lf_cache_set_loop(handle: int, loop) -> None:
+    value = LOOPS[loop] if isinstance(loop, str) else int(loop)
+    _check(load_library().lf_cache_set_loop(ctypes.c_void_p(handle), value), "lf_cache_set_loop")
+
+
 def lf_cache_max_splits(handle: int) -> int:
     v = ctypes.c_int32(0)
     _check(load_library().lf_cache_max_splits(ctypes.c_void_p(handle), ctypes.byref(v)),
@@ -354,6 +363,10 @@ class LongFlowCache:
 
     def set_waves(self, waves: int) -> None:
         lf_cache_set_waves(self.handle, waves)
+
+    def set_loop(self, loop) -> None:
+        """'auto' (or 0), 'phased' (1) or 'interleaved' (2)."""
+        lf_cache_set_loop(self.handle, loop)
 
     @property
     def max_splits(self) -> int:

@@ -228,6 +228,15 @@ lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits);
  * values. */
 lf_status lf_cache_set_waves(lf_cache* c, int32_t waves);
 
+/* Loop of the decode launches. By default a launch whose workgroups each
+ * stream at most 1024 slots uses the interleaved loop (each wave streams the
+ * K and the V of the same 16 slots together, with its own online softmax),
+ * and longer streams the phased loop (all K, then all V). 1 forces the
+ * phased loop, 2 the interleaved one, 0 restores the automatic choice.
+ * Results do not depend on it except for float32 rounding of the output and
+ * of the scores. Errors: LF_ERR_INVALID_ARG for other values. */
+lf_status lf_cache_set_loop(lf_cache* c, int32_t loop);
+
 /* Host-side copy of the fill levels of one layer, [batch] int32 into the
  * caller's HOST array. Tracked on the host from the calls made (no device
  * access, no synchronisation). */

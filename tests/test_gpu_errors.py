@@ -112,6 +112,10 @@ def test_reset_and_tuning_errors(cache):
     with pytest.raises(native.LongFlowError) as ei:
         cache.set_splits(-1)
     assert ei.value.status == native.LF_ERR_INVALID_ARG
+    for loop in (3, -1):
+        with pytest.raises(native.LongFlowError) as ei:
+            cache.set_loop(loop)
+        assert ei.value.status == native.LF_ERR_INVALID_ARG
     _same(before, _state(cache))
 
 

@@ -46,11 +46,12 @@ def test_tiny_f32_full_trajectory():
     ("f32", 2, 128, 16, 16, 20),
 ])
 @pytest.mark.parametrize("waves", [4, 8])
-def test_small_shapes_every_pair(dtype, G, d, budget, prefill, steps, waves):
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_small_shapes_every_pair(dtype, G, d, budget, prefill, steps, waves, loop):
     wl = WORKLOADS["tiny_f32"].with_(dtype=dtype, batch=3, num_kv_heads=2, num_q_heads=2 * G,
                                      head_dim=d, budget=budget, prefill=prefill, steps=steps)
-    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps} waves={waves}")
-    rep = run_lockstep(wl, steps, check_cache_every=10, waves=waves)
+    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps} waves={waves} {loop}")
+    rep = run_lockstep(wl, steps, check_cache_every=10, waves=waves, loop=loop)
     assert rep.steps == steps
 
 
@@ -70,12 +71,14 @@ def test_sinks_are_protected():
     assert rep.evictions == 256
 
 
-def test_full_mode_multi_chunk():
-    """Full-KV baseline: no eviction, cache grows past one LDS chunk (2048 slots)."""
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_full_mode_multi_chunk(loop):
+    """Full-KV baseline: no eviction, the cache grows past one LDS chunk of
+    the phased loop (2048 slots); the interleaved loop keeps no logits."""
     wl = WORKLOADS["llama8b_layer"].with_(batch=2, prefill=2040)
-    _say("bf16 FULL mode, capacity 2200, prefill 2040 -> 2060 (two chunks)")
+    _say(f"bf16 FULL mode, capacity 2200, prefill 2040 -> 2060 (two chunks), {loop}")
     rep = run_lockstep(wl, 20, mode="full", capacity=2200, pairs=[(0, 0), (1, 7), (0, 3)],
-                       check_cache_every=10)
+                       check_cache_every=10, loop=loop)
     assert rep.appends == 60 and rep.evictions == 0
 
 
@@ -98,23 +101,27 @@ def test_full_mode_capacity_error():
         c.close()
 
 
-def test_qwen3_0p6b_layer_sampled_pairs():
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_qwen3_0p6b_layer_sampled_pairs(loop):
     wl = WORKLOADS["qwen3_0p6b_layer"]
     pairs = [(0, 0), (3, 5), (17, 2), (31, 7), (8, 1), (22, 4), (12, 6), (29, 3)]
-    _say("qwen3_0p6b_layer full shape (32x16/8x128, B 1024), 24 steps, 8 sampled pairs")
-    rep = run_lockstep(wl, 24, pairs=pairs, check_cache_every=24)
+    _say(f"qwen3_0p6b_layer full shape (32x16/8x128, B 1024), 24 steps, 8 sampled pairs, {loop}")
+    rep = run_lockstep(wl, 24, pairs=pairs, check_cache_every=24, loop=loop)
     assert rep.evictions == 24 * len(pairs)
 
 
-@pytest.mark.parametrize("waves", [0, 8])
-def test_llama8b_layer_fill_then_evict_sampled_pairs(waves):
+@pytest.mark.parametrize("waves,loop", [(0, "auto"), (8, "auto"), (4, "interleaved")])
+def test_llama8b_layer_fill_then_evict_sampled_pairs(waves, loop):
     """Full Llama-8B layer shape; prefill 3270 so the run crosses into eviction
-    (0: the automatic launch, 4 waves; 8 forced)."""
+    (0: the automatic launch, 4 waves, phased loop; 8 waves forced; the
+    interleaved loop forced)."""
     wl = WORKLOADS["llama8b_layer"]
     pairs = [(0, 0), (63, 7), (10, 3), (41, 5), (5, 6), (33, 1), (57, 2), (20, 4)]
     n = np.full(wl.batch, 3270, dtype=np.int32)
-    _say(f"llama8b_layer full shape (64x32/8x128, B 3277), prefill 3270, 16 steps, 8 pairs, waves {waves}")
-    rep = run_lockstep(wl, 16, pairs=pairs, prefill_n=n, check_cache_every=16, waves=waves)
+    _say(f"llama8b_layer full shape (64x32/8x128, B 3277), prefill 3270, 16 steps, 8 pairs, "
+         f"waves {waves}, {loop}")
+    rep = run_lockstep(wl, 16, pairs=pairs, prefill_n=n, check_cache_every=16, waves=waves,
+                       loop=loop)
     assert rep.appends == 7 * len(pairs) and rep.evictions == 9 * len(pairs)
 
 
@@ -127,13 +134,14 @@ def test_ragged_fill_levels():
     assert rep.appends > 0 and rep.evictions > 0
 
 
-@pytest.mark.parametrize("budget", [512, 4096])
-def test_qwen3_8b_duplicate_ties(budget):
+@pytest.mark.parametrize("budget,loop", [(512, "auto"), (4096, "auto"), (512, "phased"),
+                                         (4096, "interleaved")])
+def test_qwen3_8b_duplicate_ties(budget, loop):
     """10% duplicated tokens: exact score collisions must resolve to the lowest slot."""
     wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(batch=16, budget=budget, prefill=budget)
     pairs = [(b, h) for b in range(0, 16, 3) for h in (0, 5)]
-    _say(f"qwen3_8b ties, B {budget}, batch 16, prefill full, 40 steps, {len(pairs)} pairs")
-    rep = run_lockstep(wl, 40, pairs=pairs, check_cache_every=40)
+    _say(f"qwen3_8b ties, B {budget}, batch 16, prefill full, 40 steps, {len(pairs)} pairs, {loop}")
+    rep = run_lockstep(wl, 40, pairs=pairs, check_cache_every=40, loop=loop)
     print(f"near-ties {rep.near_ties}, exact ties {rep.exact_ties}, "
           f"lowest index taken {rep.tie_lowest_index}")
     assert rep.tie_lowest_index == rep.exact_ties

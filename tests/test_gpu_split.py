@@ -43,11 +43,13 @@ def test_tiny_f32_split(splits, waves):
     ("bf16", 1, 128, 520, 500, 30, 16),
 ])
 @pytest.mark.parametrize("waves", [4, 8])
-def test_small_shapes_split(dtype, G, d, budget, prefill, steps, splits, waves):
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_small_shapes_split(dtype, G, d, budget, prefill, steps, splits, waves, loop):
     wl = WORKLOADS["tiny_f32"].with_(dtype=dtype, batch=3, num_kv_heads=2, num_q_heads=2 * G,
                                      head_dim=d, budget=budget, prefill=prefill, steps=steps)
-    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps} splits={splits} waves={waves}")
-    rep = run_lockstep(wl, steps, splits=splits, check_cache_every=10, waves=waves)
+    _say(f"{dtype} G={G} d={d} B={budget} prefill={prefill} steps={steps} splits={splits} "
+         f"waves={waves} {loop}")
+    rep = run_lockstep(wl, steps, splits=splits, check_cache_every=10, waves=waves, loop=loop)
     assert rep.steps == steps
 
 
