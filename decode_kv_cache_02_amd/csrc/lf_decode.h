@@ -1499,13 +1499,13 @@ inline int resident_per_cu(std::atomic<uint64_t>& memo, const void* kern, int th
   return blocks;
 }
 
-// Workgroups of a launch of `units` units. One per unit while they all fit
-// at once (resident workgroups per CU x CUs), and also when the units fill
-// whole rounds of resident workgroups. Otherwise the last round would run
-// part of the device only: the launch then takes the rounds it needs with
-// the units spread evenly over fewer workgroups, each taking its units in
-// turn. forced_grid > 0 caps the grid instead; cus <= 0 gives one workgroup
-// per unit.
+// Workgroups of a launch of `units` units of equal length. One per unit while
+// they all fit at once (resident workgroups per CU x CUs), and also when the
+// units fill whole rounds of resident workgroups. Otherwise the last round
+// would run part of the device only: the launch then takes the rounds it
+// needs with the units spread evenly over fewer workgroups, each taking its
+// units in turn. forced_grid > 0 caps the grid instead; cus <= 0 gives one
+// workgroup per unit (the runtime passes 0 for layers of unequal lengths).
 inline int decode_grid(int units, int resident, int cus, int forced_grid) {
   if (forced_grid > 0) return units < forced_grid ? units : forced_grid;
   if (cus <= 0) return units;

@@ -517,10 +517,16 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
   DeviceScope dev(c->device);
   if (!dev.ok()) return LF_ERR_HIP;
   const lf::LayerPtrs p = layer_ptrs(c, layer);
-  int32_t n_max = 0;
-  for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
+  int32_t n_max = 0, n_min = fh[0];
+  for (int32_t b = 0; b < c->cfg.batch; ++b) {
+    n_max = std::max(n_max, fh[b]);
+    n_min = std::min(n_min, fh[b]);
+  }
   const LaunchShape shape = plan_launch(c, n_max);
-  const int cus = c->forced_grid == -1 ? 0 : c->cus;
+  // Workgroups that take several pairs each are balanced only when every
+  // pair has the same length; ragged layers keep one workgroup per unit,
+  // which the hardware hands out as workgroups finish.
+  const int cus = c->forced_grid == -1 || n_min != n_max ? 0 : c->cus;
   const int forced_grid = c->forced_grid > 0 ? c->forced_grid : 0;
   if (lf::launch_decode(c->geo, p, c->work, shape.splits, shape.waves, shape.ilv, cus, forced_grid, q,
                         k_new, v_new, out, evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {

@@ -4,9 +4,9 @@ A launch with more units (pairs, or pairs x splits) than fit on the device
 at once gets as many workgroups as fit, each taking units w, w + grid, ...
 lf_cache_set_grid caps the grid so that small shapes take the same path:
 every loop, wave count, split count and variant runs here with a handful of
-workgroups. The full Qwen3-8B layer shape (2048 pairs) takes it on its own,
-and with -1 (one workgroup per unit) for comparison. Same lockstep protocol
-and tolerances as test_gpu_parity.
+workgroups. A full Llama-8B layer at batch 102 (816 pairs) takes it on its
+own, and with -1 (one workgroup per unit) for comparison. Same lockstep
+protocol and tolerances as test_gpu_parity.
 """
 import pytest
 
@@ -81,12 +81,24 @@ def test_full_mode_capped_grid():
     assert rep.appends == 20 * 6
 
 
-@pytest.mark.parametrize("budget,grid", [(512, 0), (512, -1), (1024, 0)])
-def test_qwen3_8b_layer_many_pairs(budget, grid):
-    """Batch 256 x 8 KV heads = 2048 pairs: the automatic launch puts several
-    pairs on each workgroup (grid 0); -1 gives each pair its own."""
-    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=budget, prefill=budget)
+@pytest.mark.parametrize("grid", [0, -1])
+def test_llama8b_layer_816_pairs(grid):
+    """Batch 102 x 8 KV heads = 816 pairs, every sequence full: the automatic
+    launch (grid 0) runs 408 workgroups of 2 pairs each instead of a full
+    round of 512 and a partial one; -1 gives each pair its own workgroup."""
+    wl = WORKLOADS["llama8b_layer"].with_(batch=102, prefill=3277)
+    pairs = [(0, 0), (101, 7), (51, 3), (50, 4), (77, 1), (25, 6), (90, 2), (13, 5)]
+    _say(f"llama8b layer, batch 102, B 3277 full, 8 steps, {len(pairs)} sampled pairs, grid {grid}")
+    rep = run_lockstep(wl, 8, pairs=pairs, check_cache_every=8, grid=grid)
+    assert rep.evictions == 8 * len(pairs)
+
+
+@pytest.mark.parametrize("grid", [0, 512])
+def test_qwen3_8b_layer_2048_pairs(grid):
+    """Batch 256 x 8 KV heads = 2048 pairs: four whole rounds, one workgroup
+    per pair by default; 512 forces four pairs per workgroup."""
+    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=512, prefill=512)
     pairs = [(0, 0), (255, 7), (64, 3), (128, 5), (191, 1), (37, 6), (200, 2), (99, 4)]
-    _say(f"qwen3_8b layer, batch 256, B {budget}, 12 steps, {len(pairs)} sampled pairs, grid {grid}")
+    _say(f"qwen3_8b layer, batch 256, B 512, 12 steps, {len(pairs)} sampled pairs, grid {grid}")
     rep = run_lockstep(wl, 12, pairs=pairs, check_cache_every=12, grid=grid)
     assert rep.evictions == 12 * len(pairs)
