@@ -45,8 +45,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "lf_internal.h"
 
 namespace lf {
@@ -311,7 +309,6 @@ struct DecodeParams {
   // Split-K across workgroups (SPLIT kernels only).
   int32_t pairs;        // pairs of the layer
   int32_t splits;       // workgroups per pair
-  int32_t units;        // (pair, split) units of the launch: pairs * splits
   float* ws_part;       // [pairs][splits][2G + G*D]: m, l, unnormalised output
   float* ws_logit;      // [pairs][slots_pad][G]: raw logits (cache full only)
   int32_t* arrive;      // [pairs]: arrivals, back to 0 after every launch
@@ -376,13 +373,12 @@ __device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 /*
- * One decode step of one unit of work, by the whole workgroup.
- *   SPLIT = false: a unit is a pair (unit = pair).
- *   SPLIT = true : a unit is one of the `splits` parts of a pair (unit =
- *                  split * pairs + pair), a contiguous range of 16-slot
- *                  tiles. Each split publishes its partial softmax state
- *                  (m, l, output) and, when the cache is full, its raw
- *                  logits; the last split to
+ * One decode step.
+ *   SPLIT = false: one workgroup per pair (blockIdx.x = pair).
+ *   SPLIT = true : `splits` workgroups per pair (blockIdx.x = split * pairs +
+ *                  pair), each over a contiguous range of 16-slot tiles. Each
+ *                  publishes its partial softmax state (m, l, output) and,
+ *                  when the cache is full, its raw logits; the last split to
  *                  arrive combines the partials, scores every slot against
  *                  the global max and sum, takes the argmin and writes the
  *                  output and the new token. No workgroup ever waits.
@@ -395,7 +391,7 @@ __device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off
  */
 template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT,
           bool VAR, bool ILV>
-__device__ __forceinline__ void decode_unit(const DecodeParams& P, const int unit) {
+__global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel(DecodeParams P) {
   constexpr int kBytes = Elem<T>::kBytes;
   constexpr int NT = WAVES * kWave;
   constexpr int kChunks = D * kBytes / 64;  // 16-byte K loads per lane per 16-slot tile
@@ -428,16 +424,11 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
   (void)sh_fac;
   (void)sh_ticket;
 
-  // The thread index is re-read for every unit: the compiler then computes
-  // the lane roles and addresses inside the unit loop instead of keeping
-  // them in registers across it.
-  int tid_v = threadIdx.x;
-  asm volatile("" : "+v"(tid_v));
-  const int tid = tid_v;
+  const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
-  const int pair = SPLIT ? static_cast<int>(static_cast<uint32_t>(unit) % static_cast<uint32_t>(P.pairs)) : unit;
-  const int split = SPLIT ? static_cast<int>(static_cast<uint32_t>(unit) / static_cast<uint32_t>(P.pairs)) : 0;
+  const int pair = SPLIT ? static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.pairs)) : blockIdx.x;
+  const int split = SPLIT ? static_cast<int>(blockIdx.x / static_cast<uint32_t>(P.pairs)) : 0;
   const int b = pair / P.num_kv_heads;
   const int h = pair - b * P.num_kv_heads;
   const int64_t slots_pad = P.pair_elems / D;
@@ -1467,59 +1458,11 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
   if (tid == 0) P.vnorm[static_cast<int64_t>(pair) * slots_pad + slot] = sh_vn_new;
 }
 
-/*
- * The decode launch: workgroup w takes units w, w + grid, w + 2 * grid, ...
- * in turn. With at most as many units as fit on the device at once this is
- * one unit per workgroup; beyond that the grid is capped so that every
- * workgroup stays resident and takes the same number of units, and no
- * workgroup is launched after another has finished.
- */
-template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT,
-          bool VAR, bool ILV>
-__global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel(DecodeParams P) {
-  for (int unit = blockIdx.x; unit < P.units; unit += gridDim.x) {
-    // The previous unit's last LDS reads are done before this unit writes.
-    if (unit != static_cast<int>(blockIdx.x)) __syncthreads();
-    decode_unit<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR, ILV>(P, unit);
-  }
-}
-
-// Workgroups of one kernel instance resident on one compute unit at a
-// dynamic LDS size. `memo` belongs to the instance and keeps the last answer
-// as (lds + 1) << 32 | workgroups, so the query runs once per size.
-inline int resident_per_cu(std::atomic<uint64_t>& memo, const void* kern, int threads, size_t lds) {
-  const uint64_t m = memo.load(std::memory_order_relaxed);
-  if ((m >> 32) == lds + 1) return static_cast<int>(m & 0xffffffffu);
-  int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, threads, lds) != hipSuccess || blocks < 1) {
-    (void)hipGetLastError();
-    blocks = 1;
-  }
-  memo.store(((static_cast<uint64_t>(lds) + 1) << 32) | static_cast<uint32_t>(blocks), std::memory_order_relaxed);
-  return blocks;
-}
-
-// Workgroups of a launch of `units` units of equal length. One per unit while
-// they all fit at once (resident workgroups per CU x CUs), and also when the
-// units fill whole rounds of resident workgroups. Otherwise the last round
-// would run part of the device only: the launch then takes the rounds it
-// needs with the units spread evenly over fewer workgroups, each taking its
-// units in turn. forced_grid > 0 caps the grid instead; cus <= 0 gives one
-// workgroup per unit (the runtime passes 0 for layers of unequal lengths).
-inline int decode_grid(int units, int resident, int cus, int forced_grid) {
-  if (forced_grid > 0) return units < forced_grid ? units : forced_grid;
-  if (cus <= 0) return units;
-  const int cap = resident * cus;
-  if (units <= cap || units % cap == 0) return units;
-  const int rounds = (units + cap - 1) / cap;
-  return (units + rounds - 1) / rounds;
-}
-
 template <typename T, int D, int G, bool EVICT, bool SPLIT, bool VAR, int WAVES, bool ILV,
           int UA = 1, int UB = 4, int POLICY = kStream>
 hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitWork& W, int splits,
-                           int cus, int forced_grid, const void* q, const void* k_new,
-                           const void* v_new, void* out, int32_t* evicted, hipStream_t stream) {
+                           const void* q, const void* k_new, const void* v_new, void* out,
+                           int32_t* evicted, hipStream_t stream) {
   DecodeParams P;
   P.q = q;
   P.k_new = k_new;
@@ -1548,7 +1491,6 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   const int pairs = geo.batch * geo.num_kv_heads;
   P.pairs = pairs;
   P.splits = SPLIT ? splits : 1;
-  P.units = pairs * P.splits;
   P.ws_part = W.part;
   P.ws_logit = W.logit;
   P.arrive = W.arrive;
@@ -1565,10 +1507,7 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  static std::atomic<uint64_t> memo{0};
-  const int resident =
-      cus > 0 && forced_grid <= 0 ? resident_per_cu(memo, reinterpret_cast<const void*>(kern), WAVES * kWave, lds) : 1;
-  const dim3 grid(decode_grid(P.units, resident, cus, forced_grid));
+  const dim3 grid(SPLIT ? pairs * splits : pairs);
   const dim3 block(WAVES * kWave);
   hipLaunchKernelGGL(kern, grid, block, lds, stream, P);
   return hipGetLastError();
@@ -1578,12 +1517,11 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
 // one workgroup size and loop kind.
 template <int WAVES, bool ILV>
 hipError_t launch_decode_waves(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
-                               int cus, int forced_grid, const void* q, const void* k_new,
-                               const void* v_new, void* out, int32_t* evicted, hipStream_t stream) {
+                               const void* q, const void* k_new, const void* v_new, void* out,
+                               int32_t* evicted, hipStream_t stream) {
   const bool var = g.order != 0 || g.scope != 0;
-#define LF_LAUNCH(T, D, G, EVICT, SPLIT, VAR)                                                   \
-  launch_decode_t<T, D, G, EVICT, SPLIT, VAR, WAVES, ILV>(g, L, W, SPLIT ? splits : 1, cus, forced_grid, q, \
-                                                          k_new, v_new, out, evicted, stream)
+#define LF_LAUNCH(T, D, G, EVICT, SPLIT, VAR) \
+  launch_decode_t<T, D, G, EVICT, SPLIT, VAR, WAVES, ILV>(g, L, W, SPLIT ? splits : 1, q, k_new, v_new, out, evicted, stream)
 #define LF_CASE(T, D, G)                                                                      \
   if (g.head_dim == D && g.group == G) {                                                     \
     if (g.mode != 0)                                                                         \

@@ -75,20 +75,17 @@ size_t split_part_floats(const Geometry& g);
 // LDS bytes one workgroup may use on the current device.
 size_t device_lds_limit();
 
-// splits == 1: one unit of work per pair. splits > 1: split-K, `splits`
-// units per pair (W must then hold room for that many). waves: 4 or 8 waves
-// of 64 lanes per workgroup (8 when one workgroup per CU is all the launch
-// has). ilv: the interleaved loop instead of the phased one. cus > 0: a
-// launch with more units than fit on the device at once gets as many
-// workgroups as fit, each taking units in turn; cus <= 0: one workgroup per
-// unit. forced_grid > 0 caps the workgroups instead.
+// splits == 1: one workgroup per pair. splits > 1: split-K over `splits`
+// workgroups per pair (W must then hold room for that many). waves: 4 or 8
+// waves of 64 lanes per workgroup (8 when one workgroup per CU is all the
+// launch has). ilv: the interleaved loop instead of the phased one.
 hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits, int waves,
-                         bool ilv, int cus, int forced_grid, const void* q, const void* k_new,
-                         const void* v_new, void* out, int32_t* evicted, hipStream_t stream);
+                         bool ilv, const void* q, const void* k_new, const void* v_new, void* out,
+                         int32_t* evicted, hipStream_t stream);
 #define LF_DECLARE_DECODE_UNIT(NAME)                                                          \
   hipError_t NAME(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,    \
-                  int cus, int forced_grid, const void* q, const void* k_new,               \
-                  const void* v_new, void* out, int32_t* evicted, hipStream_t stream);
+                  const void* q, const void* k_new, const void* v_new, void* out,           \
+                  int32_t* evicted, hipStream_t stream);
 LF_DECLARE_DECODE_UNIT(launch_decode_w4)   // lf_decode_w4.hip: 4 waves, phased
 LF_DECLARE_DECODE_UNIT(launch_decode_w8)   // lf_decode_w8.hip: 8 waves, phased
 LF_DECLARE_DECODE_UNIT(launch_decode_w4i)  // lf_decode_w4i.hip: 4 waves, interleaved

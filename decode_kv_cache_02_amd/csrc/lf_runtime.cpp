@@ -45,7 +45,6 @@ struct lf_cache {
   int32_t forced_splits;           // 0: plan automatically
   int32_t forced_waves;            // 0: plan automatically
   int32_t forced_loop;             // 0: plan automatically, 1: phased, 2: interleaved
-  int32_t forced_grid;             // 0: automatic, -1: one workgroup per unit, > 0: at most that many
   int32_t cus;                     // compute units of the device
   size_t lds_limit;                // LDS bytes one workgroup may use
 };
@@ -356,7 +355,6 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->forced_splits = 0;
   c->forced_waves = 0;
   c->forced_loop = 0;
-  c->forced_grid = 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
     cus = 256;
@@ -425,12 +423,6 @@ lf_status lf_cache_set_waves(lf_cache* c, int32_t waves) {
 lf_status lf_cache_set_loop(lf_cache* c, int32_t loop) {
   if (!c || loop < 0 || loop > 2) return LF_ERR_INVALID_ARG;
   c->forced_loop = loop;
-  return LF_OK;
-}
-
-lf_status lf_cache_set_grid(lf_cache* c, int32_t workgroups) {
-  if (!c || workgroups < -1) return LF_ERR_INVALID_ARG;
-  c->forced_grid = workgroups;
   return LF_OK;
 }
 
@@ -517,19 +509,11 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
   DeviceScope dev(c->device);
   if (!dev.ok()) return LF_ERR_HIP;
   const lf::LayerPtrs p = layer_ptrs(c, layer);
-  int32_t n_max = 0, n_min = fh[0];
-  for (int32_t b = 0; b < c->cfg.batch; ++b) {
-    n_max = std::max(n_max, fh[b]);
-    n_min = std::min(n_min, fh[b]);
-  }
+  int32_t n_max = 0;
+  for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
   const LaunchShape shape = plan_launch(c, n_max);
-  // Workgroups that take several pairs each are balanced only when every
-  // pair has the same length; ragged layers keep one workgroup per unit,
-  // which the hardware hands out as workgroups finish.
-  const int cus = c->forced_grid == -1 || n_min != n_max ? 0 : c->cus;
-  const int forced_grid = c->forced_grid > 0 ? c->forced_grid : 0;
-  if (lf::launch_decode(c->geo, p, c->work, shape.splits, shape.waves, shape.ilv, cus, forced_grid, q,
-                        k_new, v_new, out, evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {
+  if (lf::launch_decode(c->geo, p, c->work, shape.splits, shape.waves, shape.ilv, q, k_new, v_new, out,
+                        evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {
     (void)hipGetLastError();
     return LF_ERR_HIP;
   }

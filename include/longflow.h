@@ -237,18 +237,6 @@ lf_status lf_cache_set_waves(lf_cache* c, int32_t waves);
  * of the scores. Errors: LF_ERR_INVALID_ARG for other values. */
 lf_status lf_cache_set_loop(lf_cache* c, int32_t loop);
 
-/* Workgroups of the decode launches. A launch has one unit of work per pair
- * (per pair and split with split-K). By default each unit gets its own
- * workgroup, except when every sequence of the layer holds the same number
- * of tokens and the units overflow the workgroups that fit on the device at
- * once without filling whole rounds of them: then the launch gets units /
- * rounds workgroups and each takes its units one after the other, so no
- * round runs on part of the device. A positive `workgroups` caps the grid
- * at that many (workgroup w takes units w, w + workgroups, ...); -1 always
- * gives one workgroup per unit; 0 restores the automatic choice. Results do
- * not depend on it. Errors: LF_ERR_INVALID_ARG for values below -1. */
-lf_status lf_cache_set_grid(lf_cache* c, int32_t workgroups);
-
 /* Host-side copy of the fill levels of one layer, [batch] int32 into the
  * caller's HOST array. Tracked on the host from the calls made (no device
  * access, no synchronisation). */

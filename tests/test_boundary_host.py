@@ -126,7 +126,6 @@ def test_null_arguments_rejected(lib):
     assert lib.lf_seq_reset(None, None, 0, None) == native.LF_ERR_INVALID_ARG
     assert lib.lf_cache_set_waves(None, 4) == native.LF_ERR_INVALID_ARG
     assert lib.lf_cache_set_loop(None, 1) == native.LF_ERR_INVALID_ARG
-    assert lib.lf_cache_set_grid(None, 0) == native.LF_ERR_INVALID_ARG
     assert lib.lf_cache_set_splits(None, 2) == native.LF_ERR_INVALID_ARG
     assert lib.lf_probe_stream_read(None, 16, 1, None, None) == native.LF_ERR_INVALID_ARG
     assert lib.lf_fill_levels(None, 0, None) == native.LF_ERR_INVALID_ARG

@@ -116,10 +116,6 @@ def test_reset_and_tuning_errors(cache):
         with pytest.raises(native.LongFlowError) as ei:
             cache.set_loop(loop)
         assert ei.value.status == native.LF_ERR_INVALID_ARG
-    for grid in (-2, -100):
-        with pytest.raises(native.LongFlowError) as ei:
-            cache.set_grid(grid)
-        assert ei.value.status == native.LF_ERR_INVALID_ARG
     _same(before, _state(cache))
 
 
