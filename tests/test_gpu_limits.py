@@ -31,11 +31,15 @@ def _gpu():
 
 @pytest.mark.parametrize("G,d,budget,dtype", [(4, 128, 9216, "bf16"), (1, 128, 36864, "bf16"),
                                               (2, 64, 18432, "f32")])
-def test_largest_budget(G, d, budget, dtype):
+@pytest.mark.parametrize("splits,loop", [(0, "auto"), (1, "phased"), (1, "interleaved")])
+def test_largest_budget(G, d, budget, dtype, splits, loop):
+    """The automatic launch splits these 4 pairs 16 ways; one workgroup per
+    pair holds all of a pair's logits in LDS, with either loop."""
     wl = WORKLOADS["tiny_f32"].with_(dtype=dtype, batch=2, num_kv_heads=2, num_q_heads=2 * G,
                                      head_dim=d, budget=budget, prefill=budget - 2)
-    _say(f"{dtype} G={G} d={d} B={budget} (LDS cap), prefill {budget - 2}, 5 steps, every pair")
-    rep = run_lockstep(wl, 5, check_cache_every=5)
+    _say(f"{dtype} G={G} d={d} B={budget} (LDS cap), prefill {budget - 2}, 5 steps, every pair, "
+         f"splits {splits or 'auto'}, {loop}")
+    rep = run_lockstep(wl, 5, check_cache_every=5, splits=splits, loop=loop)
     assert rep.appends == 2 * 4 and rep.evictions == 3 * 4
 
 
