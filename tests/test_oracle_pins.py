@@ -172,6 +172,30 @@ def test_p3_full_mode_is_textbook_attention():
             layer.step(st.q, st.k_new, st.v_new)
 
 
+def test_p3_layer_gqa_matches_torch_grouped_attention():
+    """The whole layer's output against torch's grouped-query attention
+    (enable_gqa: query head j reads KV head j // G), float64 on the CPU, with
+    no eviction, for G = 1, 2, 4 and several KV heads and sequences."""
+    for hq, hkv in ((4, 4), (4, 2), (8, 2)):
+        wl = WORKLOADS["tiny_f32"].with_(num_q_heads=hq, num_kv_heads=hkv, batch=3)
+        ts = TokenStream(wl, seed_offset=23)
+        n = np.array([12, 5, 9])
+        pf = ts.prefill(n_max=12, n_per_seq=n)
+        layer = lo.LayerCache(3, hq, hkv, 64, budget=40, evict=False)
+        layer.prefill(pf.k, pf.v, n)
+        st = ts.step()
+        out = layer.output(layer.step(st.q, st.k_new, st.v_new))
+        for b in range(3):
+            keys = np.concatenate([pf.k[b, :n[b]], st.k_new[b][None]]).astype(np.float64)  # [m][Hkv][d]
+            vals = np.concatenate([pf.v[b, :n[b]], st.v_new[b][None]]).astype(np.float64)
+            qt = torch.from_numpy(st.q[b].astype(np.float64))[None, :, None, :]         # [1][Hq][1][d]
+            kt = torch.from_numpy(keys).permute(1, 0, 2)[None].contiguous()             # [1][Hkv][m][d]
+            vt = torch.from_numpy(vals).permute(1, 0, 2)[None].contiguous()
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=1 / 8.0,
+                                                                   enable_gqa=True)
+            np.testing.assert_allclose(out[b], ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+
+
 def test_p3_fill_phase_is_textbook_attention():
     K, V, q, kn, vn = _tiny_case(11)
     c = lo.PairCache(64, 64)
@@ -442,3 +466,24 @@ def test_planted_transposed_output_is_caught(monkeypatch):
     monkeypatch.setattr(lo, "attention_output",
                         lambda alpha, values: (alpha[:, ::-1] @ np.asarray(values, np.float64)))
     assert _fails(test_p3_fill_phase_is_textbook_attention)
+
+
+def test_planted_interleaved_gqa_groups_are_caught(monkeypatch):
+    """Query head j on KV head j % Hkv instead of j // G."""
+    def interleaved(self, q, k_new, v_new):
+        return {(b, h): c.attend(q[b, h::self.hkv], k_new[b, h], v_new[b, h])
+                for (b, h), c in self.cache.items()}
+    monkeypatch.setattr(lo.LayerCache, "attend", interleaved)
+    assert _fails(test_p3_layer_gqa_matches_torch_grouped_attention)
+
+
+def test_planted_missing_softmax_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(lo, "default_scale", lambda d: 1.0)
+    assert _fails(test_p3_layer_gqa_matches_torch_grouped_attention)
+    assert _fails(test_p3_full_mode_is_textbook_attention)
+
+
+def test_planted_score_of_first_head_only_is_caught(monkeypatch):
+    monkeypatch.setattr(lo, "longflow_scores",
+                        lambda alpha, vnorm: np.asarray(vnorm, np.float64) * alpha[0])
+    assert _fails(test_golden_gqa_normalised)
