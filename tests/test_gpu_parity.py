@@ -64,10 +64,11 @@ def test_empty_cache_and_budget_one():
     assert rep.appends == 4 and rep.evictions == 16
 
 
-def test_sinks_are_protected():
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_sinks_are_protected(loop):
     wl = WORKLOADS["tiny_f32"]
-    _say("tiny_f32 with sink_size=4, 256 steps")
-    rep = run_lockstep(wl, 256, sink_size=4, check_cache_every=128)
+    _say(f"tiny_f32 with sink_size=4, 256 steps, {loop}")
+    rep = run_lockstep(wl, 256, sink_size=4, check_cache_every=128, loop=loop)
     assert rep.evictions == 256
 
 

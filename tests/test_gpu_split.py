@@ -53,10 +53,11 @@ def test_small_shapes_split(dtype, G, d, budget, prefill, steps, splits, waves, 
     assert rep.steps == steps
 
 
-def test_split_sinks():
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_split_sinks(loop):
     wl = WORKLOADS["tiny_f32"].with_(budget=300, prefill=300)
-    _say("tiny_f32 B=300 sink 4, 3 splits")
-    rep = run_lockstep(wl, 64, sink_size=4, splits=3, check_cache_every=32)
+    _say(f"tiny_f32 B=300 sink 4, 3 splits, {loop}")
+    rep = run_lockstep(wl, 64, sink_size=4, splits=3, check_cache_every=32, loop=loop)
     assert rep.evictions == 64
 
 

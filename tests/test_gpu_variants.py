@@ -47,10 +47,11 @@ def test_deferred_tiny_f32(prefill):
     assert rep.evictions == 200 - (64 - prefill) + (1 if prefill < 64 else 0)
 
 
-def test_deferred_sinks_and_tiny_budget():
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_deferred_sinks_and_tiny_budget(loop):
     wl = WORKLOADS["tiny_f32"].with_(budget=8, prefill=3)
-    _say("f32 deferred, B 8, sink 4, 60 steps")
-    rep = run_lockstep(wl, 60, order="deferred", sink_size=4, check_cache_every=10)
+    _say(f"f32 deferred, B 8, sink 4, 60 steps, {loop}")
+    rep = run_lockstep(wl, 60, order="deferred", sink_size=4, check_cache_every=10, loop=loop)
     assert rep.replaced == 55
 
 
@@ -59,11 +60,13 @@ def test_deferred_sinks_and_tiny_budget():
     ("bf16", 2, 64, 300, 290, 30, 3),
     ("f32", 4, 128, 520, 500, 30, 4),
 ])
-def test_deferred_small_shapes(dtype, G, d, budget, prefill, steps, splits):
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_deferred_small_shapes(dtype, G, d, budget, prefill, steps, splits, loop):
     wl = WORKLOADS["tiny_f32"].with_(dtype=dtype, batch=3, num_kv_heads=2, num_q_heads=2 * G,
                                      head_dim=d, budget=budget, prefill=prefill, steps=steps)
-    _say(f"deferred {dtype} G={G} d={d} B={budget} prefill={prefill} splits={splits}")
-    rep = run_lockstep(wl, steps, order="deferred", splits=splits, check_cache_every=10)
+    _say(f"deferred {dtype} G={G} d={d} B={budget} prefill={prefill} splits={splits}, {loop}")
+    rep = run_lockstep(wl, steps, order="deferred", splits=splits, check_cache_every=10,
+                       loop=loop)
     assert rep.replaced >= steps - (budget - prefill)
 
 
@@ -80,31 +83,35 @@ def test_deferred_llama_layer_sampled_pairs():
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("order", ["same_step", "deferred"])
-def test_shared_scope_tiny(order):
-    _say(f"f32 shared scope ({order}), batch 3, 2 KV heads, 120 steps")
-    rep = run_lockstep(TINY_MULTI, 120, scope="sequence", order=order, check_cache_every=20)
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_shared_scope_tiny(order, loop):
+    _say(f"f32 shared scope ({order}), batch 3, 2 KV heads, 120 steps, {loop}")
+    rep = run_lockstep(TINY_MULTI, 120, scope="sequence", order=order, check_cache_every=20,
+                       loop=loop)
     assert rep.evictions >= 120 * 6 - 6
 
 
 @pytest.mark.parametrize("order,splits", [("same_step", 2), ("deferred", 4), ("same_step", 0)])
-def test_shared_scope_bf16(order, splits):
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_shared_scope_bf16(order, splits, loop):
     wl = WORKLOADS["tiny_f32"].with_(dtype="bf16", batch=4, num_q_heads=32, num_kv_heads=8,
                                      head_dim=128, budget=400, prefill=380)
-    _say(f"bf16 shared scope ({order}), 8 KV heads, B 400, splits {splits}, 40 steps")
+    _say(f"bf16 shared scope ({order}), 8 KV heads, B 400, splits {splits}, 40 steps, {loop}")
     rep = run_lockstep(wl, 40, scope="sequence", order=order, splits=splits,
-                       check_cache_every=20)
+                       check_cache_every=20, loop=loop)
     assert rep.steps == 40
 
 
 @pytest.mark.parametrize("order", ["same_step", "deferred"])
-def test_shared_scope_exact_ties(order):
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_shared_scope_exact_ties(order, loop):
     """Tokens duplicated in every KV head give exactly equal head sums; the
     lowest slot must win."""
     wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(batch=4, budget=512, prefill=512,
                                                   dup_scope="sequence", dup_frac=0.2)
-    _say(f"bf16 shared scope ties ({order}), batch 4, B 512, 40 steps")
+    _say(f"bf16 shared scope ties ({order}), batch 4, B 512, 40 steps, {loop}")
     rep = run_lockstep(wl, 40, pairs=[(0, 0), (2, 0)], scope="sequence", order=order,
-                       check_cache_every=40)
+                       check_cache_every=40, loop=loop)
     print(f"near-ties {rep.near_ties}, exact ties {rep.exact_ties}, "
           f"lowest index taken {rep.tie_lowest_index}")
     assert rep.exact_ties > 0
@@ -126,10 +133,11 @@ def test_shared_scope_llama_layer_sampled_sequences():
     ("same_step", "kv_head", 0), ("same_step", "kv_head", 4),
     ("deferred", "sequence", 0), ("deferred", "sequence", 2),
 ])
-def test_l2_norm(order, scope, splits):
-    _say(f"f32 l2 score ({order}, {scope}, splits {splits}), 80 steps")
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_l2_norm(order, scope, splits, loop):
+    _say(f"f32 l2 score ({order}, {scope}, splits {splits}), 80 steps, {loop}")
     rep = run_lockstep(TINY_MULTI, 80, norm="l2", order=order, scope=scope, splits=splits,
-                       check_cache_every=20)
+                       check_cache_every=20, loop=loop)
     assert rep.steps == 80
 
 
@@ -146,13 +154,14 @@ def test_l2_bf16_layer_shape():
 
 @pytest.mark.parametrize("order,scope", [("same_step", "kv_head"), ("deferred", "kv_head"),
                                          ("same_step", "sequence")])
-def test_recycling(order, scope):
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_recycling(order, scope, loop):
     """Sequences finish and new prompts take their slots mid-run: reset to 0,
     a partial prefill (the others untouched), and decode continues."""
     wl = TINY_MULTI.with_(budget=48, prefill=30)
     plan = {25: ([1], 20), 50: ([0, 2], 48), 70: ([1], 0)}
-    _say(f"f32 recycling ({order}, {scope}), 100 steps, resets at {sorted(plan)}")
-    rep = run_lockstep(wl, 100, order=order, scope=scope, recycle=plan, check_cache_every=5)
+    _say(f"f32 recycling ({order}, {scope}), 100 steps, resets at {sorted(plan)}, {loop}")
+    rep = run_lockstep(wl, 100, order=order, scope=scope, recycle=plan, check_cache_every=5, loop=loop)
     assert rep.recycled == 4
 
 
