@@ -85,6 +85,9 @@ def parse_args():
     ap.add_argument("--workload", default="llama8b_layer")
     ap.add_argument("--budget", type=int, default=0, help="override the budget")
     ap.add_argument("--batch", type=int, default=0, help="override the batch")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="override the KV heads, keeping the group width (1 gives one GPU's share "
+                         "under tensor parallelism over 8 KV heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-kv", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -545,6 +548,8 @@ def main():
         wl = wl.with_(budget=args.budget)
     if args.batch:
         wl = wl.with_(batch=args.batch)
+    if args.kv_heads:
+        wl = wl.with_(num_kv_heads=args.kv_heads, num_q_heads=args.kv_heads * wl.group)
     e = 2 if wl.dtype == "bf16" else 4
     torch.cuda.set_device(0)
     print(f"[bench] {wl.name}: batch {wl.batch}, {wl.num_q_heads}/{wl.num_kv_heads} heads, "
