@@ -65,6 +65,18 @@ def test_empty_cache_and_budget_one():
 
 
 @pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_long_run_bf16(loop):
+    """1000 steps (944 of them evicting) on every pair of a G = 4 bf16 shape:
+    the cache, the sidecar and the fill levels stay identical to the oracle's
+    (checked every 100 steps), with no drift."""
+    wl = WORKLOADS["tiny_f32"].with_(dtype="bf16", batch=2, num_kv_heads=2, num_q_heads=8,
+                                     head_dim=128, budget=256, prefill=200)
+    _say(f"bf16 G=4 B=256 prefill 200, 1000 steps, every pair, {loop}")
+    rep = run_lockstep(wl, 1000, check_cache_every=100, loop=loop)
+    assert rep.appends == 56 * 4 and rep.evictions == 944 * 4
+
+
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
 def test_sinks_are_protected(loop):
     wl = WORKLOADS["tiny_f32"]
     _say(f"tiny_f32 with sink_size=4, 256 steps, {loop}")
