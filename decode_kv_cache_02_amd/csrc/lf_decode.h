@@ -1,7 +1,8 @@
 #pragma once
 // gfx950 (MI355X) decode kernel of the LongFlow fused decode + score + evict
 // step, as a template shared by the translation units that instantiate it
-// (one per workgroup size) and the device helpers the fill kernel also uses.
+// (one per workgroup size and loop) and the device helpers the fill kernel
+// also uses.
 //
 // The step is defined on the LongFlow pages: attention weights and output
 // (LongFlow Guide, §Mathematical Derivation of the LongFlow Score, alpha and
@@ -14,24 +15,26 @@
 // design below keeps that property for gfx950:
 //
 //   one workgroup = one pair (sequence, KV head), 4 or 8 waves of 64 lanes
-//   (split-K: a contiguous range of the pair's 16-slot tiles).
-//   Stream   each wave takes every WAVES-th 16-slot tile and streams its K
-//            and the V rows of the same slots together, two tiles in
-//            flight. K is stored in MFMA operand order, so 16-byte loads
-//            land straight in the B operand of v_mfma_f32_16x16x32_bf16
-//            (16x16x4 f32 for float32 caches); the query group is
-//            replicated over the 16 A rows, so each lane holds all G logits
-//            of one slot. The raw logits go to LDS (kept for the score);
-//            p = exp2(s - m) against the wave's own running maximum is
-//            staged in a small per-wave strip of LDS and the V rows are
-//            accumulated against it (online softmax, one per wave).
-//   Combine  after one barrier: the workgroup's max M and sum L (the new
-//            token included) and each wave's rescaling factor, in a fixed
-//            order; output written.
+//   (split-K: a contiguous range of the pair's 16-slot tiles). K is stored
+//   in MFMA operand order, so 16-byte loads land straight in the B operand
+//   of v_mfma_f32_16x16x32_bf16 (16x16x4 f32 for float32 caches); the query
+//   group is replicated over the 16 A rows, so each lane holds all G logits
+//   of one slot. The raw logits of the whole range stay in LDS.
+//   Phased loop (long streams)
+//            K stream: logits to LDS, two register sets in flight.
+//            Transition: max M and sum L (the new token included), p in
+//            place, the score and its argmin, while the first V rows are in
+//            flight. V stream: o += p v, two register sets in flight.
+//   Interleaved loop (streams of up to 1024 slots per workgroup)
+//            each wave takes every WAVES-th tile and streams its K and the V
+//            rows of the same slots together, two tiles in flight, with its
+//            own online softmax (p staged in a per-wave strip of LDS). After
+//            one barrier: M, L and each wave's rescaling factor in a fixed
+//            order, the output, then the score from the raw logits.
 //   Score    score_i = ||v_i|| * sum_g exp2(s_{g,i} - M_g)/L_g from the raw
-//            logits in LDS and the float32 sidecar; (score, slot) argmin
-//            through DPP and LDS, lowest slot on ties; the new token's K, V
-//            and ||v|| are written in place.
+//            logits and the float32 sidecar; (score, slot) argmin through DPP
+//            and LDS, lowest slot on ties; the new token's K, V and ||v|| are
+//            written in place.
 //   Split-K  every split publishes its (m, l, o) and, when scoring, its raw
 //            logits; the last split to arrive combines, scores and writes.
 //            No workgroup waits for another.
@@ -39,9 +42,8 @@
 //            run-time flags of separate instances (the main instance carries
 //            neither).
 //
-// Every cached byte is read once and no barrier interrupts the stream: the
-// score needs no second pass over HBM because the raw logits of the whole
-// pair stay in LDS until M and L are known.
+// Every cached byte is read once: the score needs no second pass over HBM
+// because the raw logits stay in LDS until M and L are known.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
