@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from decode_kv_cache_02_amd.synth import WORKLOADS, TokenStream
-from lockstep import run_lockstep, to_device, torch_dtype, row_rel_err
+from lockstep import run_lockstep, to_device
 
 pytestmark = pytest.mark.gpu
 
