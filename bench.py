@@ -427,6 +427,56 @@ def tiny_latency(wl, steps: int = 2000, per_graph: int = 64):
         cache.close()
 
 
+def stack_graph(wl, layers, model_steps, seed=0):
+    """A stack with every pair full, one model step (an lf_decode_step per
+    layer) captured in one HIP graph and replayed `model_steps` times with the
+    same inputs (the step's cost depends on fill levels, not values). Returns
+    (ms per model step, algorithmic bytes per model step)."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import device_prefill
+    e = 2 if wl.dtype == "bf16" else 4
+    torch.cuda.empty_cache()
+    cache = LongFlowCache(layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                          dtype=wl.dtype)
+    try:
+        n = np.full(wl.batch, wl.budget, dtype=np.int32)
+        for layer in range(layers):
+            k, v = device_prefill(wl.with_(), wl.budget, seed=seed * 1000 + layer)
+            cache.prefill(layer, k, v, n)
+            del k, v
+        q, kn, vn = make_ring(wl, wl.dtype)[0]
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=q.dtype, device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                for layer in range(layers):
+                    cache.step_prepared(cache.step_args(layer, q, kn, vn, out, ev))
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for layer in range(layers):
+                cache.step_prepared(cache.step_args(layer, q, kn, vn, out, ev))
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(model_steps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / model_steps
+        per_layer = wl.batch * wl.num_kv_heads * algorithmic_bytes_per_pair(wl.budget, wl.group,
+                                                                            wl.head_dim, e, True)
+        return ms, per_layer * layers
+    finally:
+        cache.close()
+
+
 def batch_gain(wl):
     """Each method on the 32-layer ragged stack at the largest batch its own
     cache allows in 0.95 x 288 GB, with the same start-offset distribution:
@@ -525,6 +575,9 @@ def suite(args):
         w = wl5.with_(budget=budget)
         ms, nb = steady_state(w, min(steps, 30), 3, layers=36, seed=5)
         emit(f"qwen3_8b_stack36 B={budget}", w, ms, nb, 36)
+    w = wl5.with_(budget=512)
+    ms, nb = stack_graph(w, 36, min(steps, 30), seed=5)
+    emit("qwen3_8b_stack36 B=512, one HIP graph per model step", w, ms, nb, 36)
 
 
 def main():
