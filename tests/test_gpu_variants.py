@@ -54,6 +54,18 @@ def test_deferred_sinks_and_tiny_budget(loop):
     assert rep.replaced == 55
 
 
+@pytest.mark.parametrize("order", ["same_step", "deferred"])
+@pytest.mark.parametrize("loop", ["phased", "interleaved"])
+def test_one_candidate_slot(order, loop):
+    """sink_size = budget - 1 leaves one slot that can be evicted (same-step
+    order: it is replaced every step) or none once the written slot is
+    shielded (deferred order: no victim is kept, the last slot is used)."""
+    wl = TINY_MULTI.with_(budget=8, prefill=5)
+    _say(f"f32 B 8, sink 7, {order} order, 40 steps, {loop}")
+    rep = run_lockstep(wl, 40, order=order, sink_size=7, check_cache_every=5, loop=loop)
+    assert rep.steps == 40
+
+
 @pytest.mark.parametrize("dtype,G,d,budget,prefill,steps,splits", [
     ("bf16", 4, 128, 200, 200, 40, 0),
     ("bf16", 2, 64, 300, 290, 30, 3),
