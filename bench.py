@@ -158,10 +158,11 @@ def cpu_baseline(wl, seconds: float):
                 break
     sps = steps / el
     return {"value": sps * wl.batch, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "steps_per_s": sps,
+            "steps_per_s": sps, "host_cores_available": len(os.sched_getaffinity(0)),
             "sample": f"{steps} whole-batch steps of {wl.name} with every pair full "
                       f"({wl.batch * wl.num_kv_heads} pairs x {wl.budget} slots), float64 NumPy, "
-                      f"one BLAS thread, {el:.1f} s"}
+                      f"one BLAS thread (the oracle steps one pair at a time; its G x n products "
+                      f"are too small for BLAS threads to help), {el:.1f} s"}
 
 
 def full_kv_baseline(wl, steps, warmup, fills=(8704, 16384)):
