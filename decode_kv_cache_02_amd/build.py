@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "liblongflow.so")
 SOURCES = ("lf_decode_w4.hip", "lf_decode_w8.hip", "lf_decode_w4i.hip", "lf_decode_w8i.hip",
-           "lf_kernels.hip", "lf_runtime.cpp", "lf_probe.hip")
+           "lf_kernels.hip", "lf_runtime.cpp", "lf_probe.hip", "lf_scratch.hip")
 HEADERS = ("lf_decode.h", "lf_internal.h")
 ARCH = os.environ.get("LONGFLOW_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

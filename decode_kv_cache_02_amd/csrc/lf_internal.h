@@ -110,4 +110,18 @@ hipError_t launch_seq_reset(const Geometry& g, int32_t num_layers, int32_t* fill
 
 constexpr int kFillSeqPerLaunch = 256;
 
+// Static scratch of lf_decode_step_noalloc (lf_scratch.hip): one device array
+// per GPU. The first kScratchCounterBytes hold arrival counters only (zero
+// between launches): split-K counters at word 0 + pair, per-sequence counters
+// at word kScratchSeqCounterWord + sequence. The rest holds the workspace
+// of one launch.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+constexpr size_t kScratchCounterBytes = size_t{64} << 10;
+constexpr int32_t kScratchSeqCounterWord = 8192;
+// Looks up the array's device address on `device` (which must be current)
+// and clears its counters, once per device. Never called under capture.
+hipError_t scratch_setup(int device);
+// The address kept by scratch_setup, or null before it has run.
+void* scratch_ptr(int device);
+
 }  // namespace lf

@@ -261,6 +261,74 @@ LaunchShape plan_launch(const lf_cache* c, int32_t n_max) {
   return {s, waves, ilv};
 }
 
+// Workspace of one decode launch carved out of the device's static scratch:
+// counters at fixed words of the counter area, the rest after it. Returns
+// false if the launch needs more than the array holds.
+bool scratch_work(const lf_cache* c, char* base, int32_t splits, lf::SplitWork* w) {
+  const lf::Geometry& g = c->geo;
+  const size_t pairs = static_cast<size_t>(c->layer_pairs);
+  const bool split = splits > 1;
+  const bool shared = g.scope == LF_SCOPE_SEQUENCE;
+  if (split && pairs > static_cast<size_t>(lf::kScratchSeqCounterWord)) return false;
+  if (shared && (static_cast<size_t>(lf::kScratchSeqCounterWord) + g.batch) * 4 > lf::kScratchCounterBytes)
+    return false;
+  size_t off = lf::kScratchCounterBytes;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return base + at;
+  };
+  // Each size is at most the cache's own K region, so none overflows.
+  const size_t part = split ? pairs * splits * lf::split_part_floats(g) * 4 : 0;
+  const size_t logit = split && g.mode == LF_MODE_EVICT ? pairs * g.slots_pad * g.group * 4 : 0;
+  const size_t score = shared ? pairs * g.slots_pad * 4 : 0;
+  const size_t nnorm = shared ? pairs * 4 : 0;
+  if (part > lf::kScratchBytes || logit > lf::kScratchBytes || score > lf::kScratchBytes) return false;
+  w->part = reinterpret_cast<float*>(take(part));
+  w->logit = reinterpret_cast<float*>(take(logit));
+  w->score = reinterpret_cast<float*>(take(score));
+  w->new_norm = reinterpret_cast<float*>(take(nnorm));
+  w->arrive = reinterpret_cast<int32_t*>(base);
+  w->seq_arrive = reinterpret_cast<int32_t*>(base) + lf::kScratchSeqCounterWord;
+  return off <= lf::kScratchBytes;
+}
+
+// One decode step of one layer; `static_scratch` takes the launch's
+// workspace from the device's static array instead of the cache's own.
+lf_status decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                      void* out, int32_t* evicted_slot, void* stream, bool static_scratch) {
+  if (!c || !q || !k_new || !v_new || !out || !evicted_slot || layer < 0 ||
+      layer >= c->cfg.num_layers)
+    return LF_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+    return LF_ERR_INVALID_ARG;
+  int32_t* fh = c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch;
+  if (c->cfg.mode == LF_MODE_FULL) {
+    for (int32_t b = 0; b < c->cfg.batch; ++b)
+      if (fh[b] >= c->cfg.budget) return LF_ERR_CAPACITY;
+  }
+  int32_t n_max = 0;
+  for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
+  const LaunchShape shape = plan_launch(c, n_max);
+  lf::SplitWork work = c->work;
+  if (static_scratch) {
+    char* base = static_cast<char*>(lf::scratch_ptr(c->device));
+    if (!base) return LF_ERR_HIP;  // set up by lf_cache_create on this device
+    if (!scratch_work(c, base, shape.splits, &work)) return LF_ERR_SCRATCH;
+  }
+  DeviceScope dev(c->device);
+  if (!dev.ok()) return LF_ERR_HIP;
+  const lf::LayerPtrs p = layer_ptrs(c, layer);
+  if (lf::launch_decode(c->geo, p, work, shape.splits, shape.waves, shape.ilv, q, k_new, v_new, out,
+                        evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
+    return LF_ERR_HIP;
+  }
+  for (int32_t b = 0; b < c->cfg.batch; ++b)
+    if (fh[b] < c->cfg.budget) ++fh[b];
+  return LF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -273,6 +341,7 @@ const char* lf_status_str(lf_status s) {
     case LF_ERR_CAPACITY: return "LF_ERR_CAPACITY";
     case LF_ERR_OOM: return "LF_ERR_OOM";
     case LF_ERR_HIP: return "LF_ERR_HIP";
+    case LF_ERR_SCRATCH: return "LF_ERR_SCRATCH";
   }
   return "LF_ERR_UNKNOWN";
 }
@@ -334,7 +403,11 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   }
   e = hipMemsetAsync(base, 0, L.total, nullptr);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  // The device's static scratch (lf_decode_step_noalloc) is set up here,
+  // outside any stream capture, once per device.
+  if (e == hipSuccess) e = lf::scratch_setup(device);
   if (e != hipSuccess) {
+    (void)hipGetLastError();
     (void)hipFree(base);
     delete c;
     return LF_ERR_HIP;
@@ -496,30 +569,12 @@ lf_status lf_seq_reset(lf_cache* c, const int32_t* seqs, int32_t count, void* st
 
 lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_new,
                          const void* v_new, void* out, int32_t* evicted_slot, void* stream) {
-  if (!c || !q || !k_new || !v_new || !out || !evicted_slot || layer < 0 ||
-      layer >= c->cfg.num_layers)
-    return LF_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
-    return LF_ERR_INVALID_ARG;
-  int32_t* fh = c->fill_host.data() + static_cast<size_t>(layer) * c->cfg.batch;
-  if (c->cfg.mode == LF_MODE_FULL) {
-    for (int32_t b = 0; b < c->cfg.batch; ++b)
-      if (fh[b] >= c->cfg.budget) return LF_ERR_CAPACITY;
-  }
-  DeviceScope dev(c->device);
-  if (!dev.ok()) return LF_ERR_HIP;
-  const lf::LayerPtrs p = layer_ptrs(c, layer);
-  int32_t n_max = 0;
-  for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
-  const LaunchShape shape = plan_launch(c, n_max);
-  if (lf::launch_decode(c->geo, p, c->work, shape.splits, shape.waves, shape.ilv, q, k_new, v_new, out,
-                        evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {
-    (void)hipGetLastError();
-    return LF_ERR_HIP;
-  }
-  for (int32_t b = 0; b < c->cfg.batch; ++b)
-    if (fh[b] < c->cfg.budget) ++fh[b];
-  return LF_OK;
+  return decode_step(c, layer, q, k_new, v_new, out, evicted_slot, stream, false);
+}
+
+lf_status lf_decode_step_noalloc(lf_cache* c, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, void* out, int32_t* evicted_slot, void* stream) {
+  return decode_step(c, layer, q, k_new, v_new, out, evicted_slot, stream, true);
 }
 
 }  // extern "C"

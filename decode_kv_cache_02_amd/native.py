@@ -22,6 +22,7 @@ LF_ERR_UNSUPPORTED = 2
 LF_ERR_CAPACITY = 3
 LF_ERR_OOM = 4
 LF_ERR_HIP = 5
+LF_ERR_SCRATCH = 6
 
 LF_DTYPE_F32 = 0
 LF_DTYPE_BF16 = 1
@@ -82,6 +83,9 @@ SIGNATURES = [
     ("lf_decode_step", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]),
+    ("lf_decode_step_noalloc", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p]),
     ("lf_cache_view", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(lf_view)]),
     ("lf_cache_snapshot", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -197,6 +201,16 @@ def lf_decode_step(handle: int, layer: int, q, k_new, v_new, out, evicted_slot, 
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(evicted_slot.data_ptr()),
         ctypes.c_void_p(_stream_ptr(stream)))
     _check(st, "lf_decode_step")
+
+
+def lf_decode_step_noalloc(handle: int, layer: int, q, k_new, v_new, out, evicted_slot,
+                           stream=None) -> None:
+    st = load_library().lf_decode_step_noalloc(
+        ctypes.c_void_p(handle), int(layer), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(evicted_slot.data_ptr()),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check(st, "lf_decode_step_noalloc")
 
 
 def lf_cache_view(handle: int, layer: int) -> lf_view:
@@ -326,14 +340,17 @@ class LongFlowCache:
             self._check_tensor(v, (self.batch, n_max, self.hkv, self.head_dim), "v")
         lf_prefill_fill(self.handle, layer, k, v, n_per_seq, n_max, stream)
 
-    def decode_step(self, layer, q, k_new, v_new, out, evicted_slot, stream=None):
+    def decode_step(self, layer, q, k_new, v_new, out, evicted_slot, stream=None,
+                    noalloc: bool = False):
+        """lf_decode_step, or lf_decode_step_noalloc when `noalloc`."""
         import torch
         self._check_tensor(q, (self.batch, self.hq, self.head_dim), "q")
         self._check_tensor(k_new, (self.batch, self.hkv, self.head_dim), "k_new")
         self._check_tensor(v_new, (self.batch, self.hkv, self.head_dim), "v_new")
         self._check_tensor(out, (self.batch, self.hq, self.head_dim), "out")
         self._check_tensor(evicted_slot, (self.batch, self.hkv), "evicted_slot", torch.int32)
-        lf_decode_step(self.handle, layer, q, k_new, v_new, out, evicted_slot, stream)
+        fn = lf_decode_step_noalloc if noalloc else lf_decode_step
+        fn(self.handle, layer, q, k_new, v_new, out, evicted_slot, stream)
 
     def seq_reset(self, seqs, stream=None) -> None:
         lf_seq_reset(self.handle, seqs, stream)

@@ -83,7 +83,9 @@ typedef enum {
   LF_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, group, sizes    */
   LF_ERR_CAPACITY = 3,    /* prefill longer than the budget; FULL cache full */
   LF_ERR_OOM = 4,         /* the one device allocation failed               */
-  LF_ERR_HIP = 5          /* a HIP runtime or launch error                  */
+  LF_ERR_HIP = 5,         /* a HIP runtime or launch error                  */
+  LF_ERR_SCRATCH = 6      /* lf_decode_step_noalloc: the launch needs more
+                             workspace than the static scratch array holds  */
 } lf_status;
 
 typedef enum { LF_DTYPE_F32 = 0, LF_DTYPE_BF16 = 1 } lf_dtype;
@@ -191,6 +193,35 @@ lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void*
 lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_new,
                          const void* v_new, void* out, int32_t* evicted_slot,
                          void* stream);
+
+/* lf_decode_step without any allocation of its own, for callers that cannot
+ * allocate device memory at step time: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments, launches,
+ * kernels and results as lf_decode_step (bit for bit); the only difference is
+ * where the launch's cross-workgroup workspace lives (split-K partial states,
+ * raw logits and arrival counters; the score vectors, new-token norms and
+ * counters of LF_SCOPE_SEQUENCE). Here it comes from one static device array
+ * of the library, 16 MiB per GPU, held by every GPU the library runs on until
+ * the process ends, instead of the cache's own allocation. The array's
+ * address is looked up, and its counters cleared, by the first
+ * lf_cache_create on each device; the counters are back at zero after every
+ * launch. The call itself allocates and frees nothing.
+ *
+ * Every call on one GPU shares that GPU's array: calls on one GPU whose work
+ * may overlap (other streams, other handles, other threads) race and give
+ * undefined results. Serialise them on one stream.
+ *
+ * Errors: those of lf_decode_step, and LF_ERR_SCRATCH (nothing queued) when
+ * the launch's workspace does not fit in the array: split-K launches need
+ * pairs * splits * (2G + G*head_dim) * 4 bytes of partial states plus
+ * pairs * slots_padded * G * 4 bytes of logits (EVICT mode); LF_SCOPE_SEQUENCE
+ * needs pairs * (slots_padded + 1) * 4 bytes, with each region rounded up to
+ * 256 bytes, in 16 MiB - 64 KiB; split-K launches also need pairs <= 8192 and
+ * LF_SCOPE_SEQUENCE batch <= 8192. One-workgroup-per-pair launches of
+ * LF_SCOPE_KV_HEAD use no workspace and always fit. */
+lf_status lf_decode_step_noalloc(lf_cache* c, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, void* out, int32_t* evicted_slot,
+                                 void* stream);
 
 /* Fill the view of one layer. */
 lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view);

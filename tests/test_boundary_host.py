@@ -51,6 +51,7 @@ def test_binding_covers_every_declared_symbol():
 def test_status_strings(lib):
     assert native.status_str(0) == "LF_OK"
     assert native.status_str(3) == "LF_ERR_CAPACITY"
+    assert native.status_str(6) == "LF_ERR_SCRATCH"
     assert native.status_str(99) == "LF_ERR_UNKNOWN"
 
 
