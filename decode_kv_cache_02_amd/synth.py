@@ -307,3 +307,100 @@ def device_prefill(wl: Workload, n: int, seed: int, device: str = "cuda"):
         v[b0:b1] = (vv * scale).to(dt)
         del vv, scale
     return k, v
+
+
+@dataclass
+class PairTokenStream:
+    """Deterministic inputs of ONE pair (sequence b, KV head h) of one layer.
+
+    The same value recipe as TokenStream, drawn for this pair alone from
+    SeedSequence([cfg_id, layer, seed_offset, b, h, 1]), so a long trajectory
+    can be checked on a few sampled pairs without drawing the whole batch:
+    K and V rows N(0, 1), one lognormal(0, 0.5) scale per V row, the G query
+    heads' correlated walks, and (with dup_frac > 0) duplicated tokens that
+    copy both rows of a uniformly chosen earlier token of the pair. Everything
+    is rounded once to the storage dtype.
+    """
+
+    wl: Workload
+    b: int
+    h: int
+    layer: int = 0
+    seed_offset: int = 0
+    _rngs: dict = field(init=False, repr=False)
+    _q: np.ndarray = field(init=False, repr=False)
+    _hist_k: np.ndarray = field(init=False, repr=False)
+    _hist_v: np.ndarray = field(init=False, repr=False)
+    tokens_emitted: int = field(init=False, default=0)
+
+    def __post_init__(self):
+        ss = np.random.SeedSequence([self.wl.cfg_id, self.layer, self.seed_offset,
+                                     self.b, self.h, 1])
+        self._rngs = {name: np.random.Generator(np.random.PCG64(k))
+                      for name, k in zip(_STREAMS, ss.spawn(len(_STREAMS)))}
+        self._q = _normalise_rows(self._rngs["q_walk"].standard_normal(
+            (self.wl.group, self.wl.head_dim)))
+        self._hist_k = np.zeros((0, self.wl.head_dim), dtype=np.float32)
+        self._hist_v = np.zeros((0, self.wl.head_dim), dtype=np.float32)
+
+    def _rows(self, count: int, k_stream: str, v_stream: str):
+        wl = self.wl
+        k = self._rngs[k_stream].standard_normal((count, wl.head_dim), dtype=np.float32)
+        v = self._rngs[v_stream].standard_normal((count, wl.head_dim), dtype=np.float32)
+        scale = self._rngs["v_scale"].lognormal(0.0, V_LOGNORMAL_SIGMA, size=count)
+        v = v * scale.astype(np.float32)[:, None]
+        k, v = round_to_dtype(k, wl.dtype), round_to_dtype(v, wl.dtype)
+        if wl.dup_frac > 0.0:
+            # Two uniforms per token, drawn in token order, so the stream does
+            # not depend on how the tokens are grouped into calls.
+            t0 = self.tokens_emitted
+            du = self._rngs["dup"].random((count, 2))
+            pick = du[:, 0] < wl.dup_frac
+            u = du[:, 1]
+            hist_k = np.concatenate([self._hist_k, k])
+            hist_v = np.concatenate([self._hist_v, v])
+            for j in np.flatnonzero(pick):
+                t = t0 + int(j)
+                if t == 0:
+                    continue
+                s = min(int(u[j] * t), t - 1)   # uniform over the t earlier tokens
+                hist_k[t] = hist_k[s]
+                hist_v[t] = hist_v[s]
+            k, v = hist_k[t0:].copy(), hist_v[t0:].copy()
+            self._hist_k, self._hist_v = hist_k, hist_v
+        self.tokens_emitted += count
+        return k, v
+
+    def prefill(self, n: int):
+        """The first n tokens: K, V [n][head_dim]."""
+        return self._rows(n, "prefill_k", "prefill_v")
+
+    def steps(self, count: int):
+        """The next `count` decode steps: q [count][G][d], k_new and v_new
+        [count][d]."""
+        k, v = self._rows(count, "decode_k", "decode_v")
+        q = np.empty((count, self.wl.group, self.wl.head_dim), dtype=np.float32)
+        for t in range(count):
+            q[t] = round_to_dtype(self._q.astype(np.float32), self.wl.dtype)
+            z = self._rngs["q_walk"].standard_normal(self._q.shape)
+            self._q = _normalise_rows(QUERY_WALK_KEEP * self._q + QUERY_WALK_NOISE * z)
+        return q, k, v
+
+
+def device_steps(wl: Workload, count: int, seed: int, device: str = "cuda"):
+    """`count` decode-step inputs for the whole batch drawn on the device:
+    q [count][batch][num_q_heads][d] (unit-RMS rows), k_new and v_new
+    [count][batch][num_kv_heads][d] (V rows scaled by lognormal(0, 0.5)), in
+    the storage dtype. Load for the pairs a test does not check."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = torch.randn((count, wl.batch, wl.num_q_heads, wl.head_dim), generator=g, device=device)
+    q = q * (wl.head_dim ** 0.5) / q.norm(dim=-1, keepdim=True)
+    kv_shape = (count, wl.batch, wl.num_kv_heads, wl.head_dim)
+    k = torch.randn(kv_shape, generator=g, device=device)
+    v = torch.randn(kv_shape, generator=g, device=device)
+    scale = torch.empty(kv_shape[:3] + (1,), device=device)
+    scale.log_normal_(0.0, V_LOGNORMAL_SIGMA, generator=g)
+    return q.to(dt), k.to(dt), (v * scale).to(dt)

@@ -27,6 +27,18 @@ from oracle.longflow_oracle import LayerCache
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
+# bfloat16 outputs are float32 accumulators rounded to nearest even. A correct
+# kernel's float32 value y lies within the float32 gate (e = 1e-5 of the row
+# maximum) of the exact output x, so its bfloat16 output RNE(y) lies between
+# RNE(x - e) and RNE(x + e), and equals RNE(x) unless x sits within e of a
+# rounding boundary (a midpoint, or for outputs near zero, where one
+# bfloat16 step is smaller than e, any boundary). Anything outside that range
+# (truncation, a dropped or extra term worth a fraction of an ulp) is a
+# violation.
+BF16_MID_TOL = 1e-5
+# Midpoint exceptions allowed, as a share of the output elements checked.
+BF16_MID_SHARE = 1e-3
+
 
 def torch_dtype(dtype: str):
     import torch
@@ -45,6 +57,28 @@ def row_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float((num / den).max())
 
 
+def rne_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> the nearest bfloat16 value, ties to even (8 significant bits),
+    as float64; no intermediate float32 rounding."""
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def bf16_rounding_check(gpu: np.ndarray, ref: np.ndarray, mid_tol: float = BF16_MID_TOL):
+    """Compare bfloat16 outputs `gpu` [..., d] with the float64 oracle `ref`
+    [..., d] element by element, e = mid_tol x (row max |ref|). Returns
+    (exceptions, violations, elements): an exception differs from RNE(ref)
+    but lies in [RNE(ref - e), RNE(ref + e)]; a violation lies outside."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    diff = gpu != rne_bf16(ref)
+    if not diff.any():
+        return 0, 0, int(gpu.size)
+    e = mid_tol * np.abs(ref).max(axis=-1, keepdims=True)
+    inside = (gpu >= rne_bf16(ref - e)) & (gpu <= rne_bf16(ref + e))
+    return int((diff & inside).sum()), int((diff & ~inside).sum()), int(gpu.size)
+
+
 @dataclass
 class LockstepReport:
     steps: int = 0
@@ -58,6 +92,21 @@ class LockstepReport:
     notes: list = field(default_factory=list)
     replaced: int = 0                 # deferred: steps that replaced a cached token
     recycled: int = 0
+    bf16_elements: int = 0            # bfloat16 outputs checked against RNE(oracle)
+    bf16_mid_exceptions: int = 0      # of which != RNE(oracle), within the float32 gate of a boundary
+
+    def summary(self) -> str:
+        s = (f"steps {self.steps}, evictions {self.evictions}, appends {self.appends}, "
+             f"near-ties {self.near_ties}, exact ties {self.exact_ties} "
+             f"(lowest index {self.tie_lowest_index}), max rel err {self.max_rel_err:.3g}")
+        if self.bf16_elements:
+            s += (f", bf16 = RNE(oracle) on {self.bf16_elements - self.bf16_mid_exceptions}"
+                  f"/{self.bf16_elements} ({self.bf16_mid_exceptions} boundary exceptions)")
+        return s
+
+    def check_bf16(self) -> None:
+        assert self.bf16_mid_exceptions <= max(4, BF16_MID_SHARE * self.bf16_elements), (
+            f"{self.bf16_mid_exceptions} boundary exceptions in {self.bf16_elements} outputs")
 
 
 def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
@@ -125,6 +174,12 @@ def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
                 rep.max_rel_err = max(rep.max_rel_err, err)
                 assert err <= TOL[wl.dtype], (
                     f"step {t} pair {(b, h)}: out rel err {err:.3g} > {TOL[wl.dtype]}")
+                if wl.dtype == "bf16":
+                    exc, bad, cnt = bf16_rounding_check(gout[b, h * g:(h + 1) * g], r.out)
+                    assert bad == 0, (
+                        f"step {t} pair {(b, h)}: {bad} bf16 outputs differ from RNE(oracle)")
+                    rep.bf16_mid_exceptions += exc
+                    rep.bf16_elements += cnt
                 e = int(gev[b, h])
                 if scope == "sequence":
                     first = int(gev[b, 0])
@@ -166,6 +221,8 @@ def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
         if check_cache_every:
             compare_cache(cache, oracle, layer, wl, check_victims=deferred and not pending_ties(pending))
         rep.max_splits = cache.max_splits
+        rep.check_bf16()
+        print(f"[lockstep] {wl.name}: {rep.summary()}", flush=True)
         return rep
     finally:
         cache.close()

@@ -82,4 +82,5 @@ def test_qwen3_8b_stack36_full_shape(budget):
     _say(f"qwen3_8b stack36, batch 256, B {budget}, layer 20 of 36, 4 steps, pairs {pairs}")
     rep = run_lockstep(wl, 4, pairs=pairs, layer=20, num_layers=36, check_cache_every=4)
     assert rep.evictions == 4 * len(pairs)
+    assert rep.exact_ties > 0
     assert rep.tie_lowest_index == rep.exact_ties

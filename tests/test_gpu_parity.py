@@ -157,6 +157,7 @@ def test_qwen3_8b_duplicate_ties(budget, loop):
     rep = run_lockstep(wl, 40, pairs=pairs, check_cache_every=40, loop=loop)
     print(f"near-ties {rep.near_ties}, exact ties {rep.exact_ties}, "
           f"lowest index taken {rep.tie_lowest_index}")
+    assert rep.exact_ties > 0
     assert rep.tie_lowest_index == rep.exact_ties
 
 

@@ -79,6 +79,7 @@ def test_duplicate_ties_across_splits(budget, splits):
     rep = run_lockstep(wl, 40, pairs=pairs, splits=splits, check_cache_every=40)
     print(f"near-ties {rep.near_ties}, exact ties {rep.exact_ties}, "
           f"lowest index taken {rep.tie_lowest_index}")
+    assert rep.exact_ties > 0
     assert rep.tie_lowest_index == rep.exact_ties
 
 

@@ -1,0 +1,66 @@
+"""Whole trajectories at the workloads' full shapes, checked against the oracle
+on 8 sampled pairs (tests/trajectory.py): every step's output rows and evicted
+slot, and the pairs' cache regions every 1024 steps.
+
+  * Llama-8B layer: batch 64, 32/8 heads, B = 3277, prompt 512, then 16,384
+    steps with the automatic launch. The pairs fill for 2,765 steps and evict
+    from then on (LongFlow Guide, §Static Memory Pre-Allocation and In-Place
+    Eviction, items 1-3: fill, then evict every step); the launch moves from
+    the interleaved loop to the phased one when the cache passes 1024 slots.
+  * Qwen3-0.6B layer: batch 32, 16/8 heads, B = 1024, full prompt, all 4,096
+    evicting steps.
+  * Qwen3-8B layer at batch 256 with 10% duplicated tokens, B = 2048 and 4096
+    (the suite's one-workgroup-per-pair launches): prompt 512, then filling
+    and 512 evicting steps. Duplicates make exact score ties; each must go to
+    the lowest slot.
+Each test prints its near-tie and exact-tie counts.
+"""
+import pytest
+
+from decode_kv_cache_02_amd.synth import WORKLOADS
+import trajectory
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, steps, prefill, check_every=1024, pairs=8, seed=0):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sampled = trajectory.sample_pairs(wl, pairs, seed=seed)
+    print(f"\n[case] {wl.name} B={wl.budget} batch={wl.batch}: prompt {prefill}, {steps} steps, "
+          f"pairs {sampled}", flush=True)
+    rec = trajectory.record_trajectory(wl, steps, sampled, prefill, check_every=check_every)
+    print(f"[case] recorded; checking {len(sampled)} pairs in the oracle", flush=True)
+    reports = trajectory.check_trajectory(rec)
+    print(trajectory.summary(rec, reports), flush=True)
+    return reports
+
+
+def test_llama8b_layer_whole_trajectory():
+    wl = WORKLOADS["llama8b_layer"]
+    reports = _run(wl, wl.steps, wl.prefill, seed=3)
+    fill_steps = wl.budget - wl.prefill
+    for r in reports:
+        assert r.appends == fill_steps and r.evictions == wl.steps - fill_steps
+        assert r.fill_to_evict_step == fill_steps
+        assert r.snapshots == wl.steps // 1024
+
+
+def test_qwen3_0p6b_layer_whole_trajectory():
+    wl = WORKLOADS["qwen3_0p6b_layer"]
+    reports = _run(wl, wl.steps, wl.budget, seed=2)
+    for r in reports:
+        assert r.evictions == wl.steps and r.appends == 0
+
+
+@pytest.mark.parametrize("budget", [2048, 4096])
+def test_qwen3_8b_layer_budget_with_ties(budget):
+    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=budget)
+    steps = budget - wl.prefill + 512
+    reports = _run(wl, steps, wl.prefill, seed=5)
+    for r in reports:
+        assert r.appends == budget - wl.prefill and r.evictions == 512
+    exact = sum(r.exact_ties for r in reports)
+    assert exact > 0
+    assert sum(r.tie_lowest_index for r in reports) == exact

@@ -1,0 +1,284 @@
+"""Whole-trajectory parity on sampled pairs: a workload's full decode run on
+the GPU, checked pair by pair against the oracle afterwards.
+
+A layer's pairs never interact, so a long trajectory at full batch can be
+checked on a few sampled pairs. Their inputs (prompt, then every step's query
+group, k_new and v_new) come from synth.PairTokenStream, one seeded stream per
+pair. Every other pair of the batch runs on device-drawn inputs of the same
+distributions (synth.device_prefill, a ring of synth.device_steps), so the
+launches have the workload's real shape and fill levels throughout.
+
+1. record_trajectory() runs the whole trajectory through the C ABI with the
+   library's automatic launch plan (or a forced one) and records, for the
+   sampled pairs, every step's output rows and evicted slot, plus snapshots of
+   their cache regions (K, V, sidecar, fill level) every `check_every` steps.
+2. check_trajectory() replays each sampled pair in the oracle, one forked
+   worker per pair, and applies the lockstep rules of lockstep.py to the
+   record: output rows within the dtype's tolerance (bfloat16 outputs also
+   equal to RNE of the oracle except within the float32 gate of a rounding
+   boundary), the evicted slot
+   bit-exact except at a near-tie, where it must be in the near-tie set and
+   the oracle adopts it (the GPU never depends on the oracle, so adopting from
+   the record is the same as adopting step by step), and the snapshots
+   bit-equal to the oracle's cache (sidecar within 2e-6).
+"""
+from __future__ import annotations
+
+import multiprocessing
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from decode_kv_cache_02_amd.synth import PairTokenStream, Workload, device_prefill, device_steps
+from lockstep import (BF16_MID_SHARE, TOL, bf16_rounding_check, row_rel_err)
+
+BLOCK = 256      # steps of host inputs uploaded at a time
+RING = 64        # device-drawn steps cycled by the pairs not checked
+
+
+def sample_pairs(wl: Workload, count: int, seed: int = 0):
+    """`count` distinct (sequence, KV head) pairs: the first and the last pair
+    of the layer and the rest drawn at random."""
+    rng = np.random.default_rng(seed)
+    total = wl.batch * wl.num_kv_heads
+    picks = [0, total - 1]
+    for p in rng.permutation(total):
+        if len(picks) >= min(count, total):
+            break
+        if int(p) not in picks:
+            picks.append(int(p))
+    return sorted((p // wl.num_kv_heads, p % wl.num_kv_heads) for p in picks)
+
+
+@dataclass
+class Record:
+    wl: Workload
+    pairs: list
+    steps: int
+    prefill: int
+    seed_offset: int
+    out: np.ndarray                       # [steps][pairs][G][d] float32 (dtype-exact)
+    evicted: np.ndarray                   # [steps][pairs] int32
+    snapshots: list = field(default_factory=list)   # (steps done, K, V, vnorm, fill) per pair axis
+    launch: str = ""
+
+
+def record_trajectory(wl: Workload, steps: int, pairs, prefill: int, check_every: int = 0,
+                      seed_offset: int = 0, splits: int = 0, waves: int = 0,
+                      loop: str = "auto") -> Record:
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    G, d, P = wl.group, wl.head_dim, len(pairs)
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, d, wl.budget,
+                          sink_size=wl.sink_size, dtype=wl.dtype)
+    try:
+        if splits:
+            cache.set_splits(splits)
+        if waves:
+            cache.set_waves(waves)
+        if loop != "auto":
+            cache.set_loop(loop)
+        cuda = torch.device("cuda")
+        bq = torch.tensor([b for b, h in pairs for _ in range(G)], device=cuda)
+        hq = torch.tensor([h * G + g for b, h in pairs for g in range(G)], device=cuda)
+        bk = torch.tensor([b for b, _ in pairs], device=cuda)
+        hk = torch.tensor([h for _, h in pairs], device=cuda)
+        streams = [PairTokenStream(wl, b, h, seed_offset=seed_offset) for b, h in pairs]
+        seed = 1000 * wl.cfg_id + seed_offset
+        if prefill > 0:
+            kp, vp = device_prefill(wl, prefill, seed=seed)
+            for s, (b, h) in zip(streams, pairs):
+                K, V = s.prefill(prefill)
+                kp[b, :, h] = torch.from_numpy(K).to(cuda, dt)
+                vp[b, :, h] = torch.from_numpy(V).to(cuda, dt)
+            cache.prefill(0, kp, vp, np.full(wl.batch, prefill, dtype=np.int32))
+            del kp, vp
+        else:
+            cache.prefill(0, None, None, np.zeros(wl.batch, dtype=np.int32))
+        ring_q, ring_k, ring_v = device_steps(wl, RING, seed=seed + 1)
+        q_buf, k_buf, v_buf = torch.empty_like(ring_q[0]), torch.empty_like(ring_k[0]), \
+            torch.empty_like(ring_v[0])
+        out = torch.empty_like(q_buf)
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device=cuda)
+        rec_out = torch.empty((steps, P * G, d), dtype=dt, device=cuda)
+        rec_ev = torch.empty((steps, P), dtype=torch.int32, device=cuda)
+        snaps = []
+
+        def snapshot(done):
+            k, v, vn, fill = cache.snapshot(0)
+            snaps.append((done, k[bk, hk].float().cpu().numpy(), v[bk, hk].float().cpu().numpy(),
+                          vn[bk, hk].cpu().numpy(), fill[bk, hk].cpu().numpy()))
+
+        for t0 in range(0, steps, BLOCK):
+            cnt = min(BLOCK, steps - t0)
+            host = [s.steps(cnt) for s in streams]
+            hq_blk = torch.from_numpy(np.stack([x[0] for x in host], axis=1).reshape(cnt, P * G, d))
+            hk_blk = torch.from_numpy(np.stack([x[1] for x in host], axis=1))
+            hv_blk = torch.from_numpy(np.stack([x[2] for x in host], axis=1))
+            hq_blk, hk_blk, hv_blk = (x.to(cuda, dt) for x in (hq_blk, hk_blk, hv_blk))
+            for j in range(cnt):
+                t = t0 + j
+                q_buf.copy_(ring_q[t % RING])
+                k_buf.copy_(ring_k[t % RING])
+                v_buf.copy_(ring_v[t % RING])
+                q_buf[bq, hq] = hq_blk[j]
+                k_buf[bk, hk] = hk_blk[j]
+                v_buf[bk, hk] = hv_blk[j]
+                cache.decode_step(0, q_buf, k_buf, v_buf, out, ev)
+                rec_out[t] = out[bq, hq]
+                rec_ev[t] = ev[bk, hk]
+                if check_every and (t + 1) % check_every == 0 and t + 1 < steps:
+                    snapshot(t + 1)
+        snapshot(steps)
+        torch.cuda.synchronize()
+        return Record(wl, list(pairs), steps, prefill, seed_offset,
+                      rec_out.float().cpu().numpy().reshape(steps, P, G, d),
+                      rec_ev.cpu().numpy(), snaps,
+                      launch=f"splits={splits or 'auto'} waves={waves or 'auto'} loop={loop}")
+    finally:
+        cache.close()
+
+
+# ---------------------------------------------------------------------------
+# Checking (forked workers, one per sampled pair)
+# ---------------------------------------------------------------------------
+
+_RECORD = None   # set before the pool forks; the workers read it from inherited memory
+
+
+@dataclass
+class PairReport:
+    pair: tuple
+    steps: int = 0
+    evictions: int = 0
+    appends: int = 0
+    near_ties: int = 0
+    exact_ties: int = 0
+    tie_lowest_index: int = 0
+    max_rel_err: float = 0.0
+    bf16_elements: int = 0
+    bf16_mid_exceptions: int = 0
+    snapshots: int = 0
+    fill_to_evict_step: int = -1      # first step that evicted
+    failures: list = field(default_factory=list)
+
+
+def _fail(rep: PairReport, msg: str) -> bool:
+    rep.failures.append(msg)
+    return len(rep.failures) >= 5     # stop after a few
+
+
+def _check_pair(index: int) -> PairReport:
+    from threadpoolctl import threadpool_limits
+    from oracle.longflow_oracle import PairCache
+
+    rec = _RECORD
+    wl = rec.wl
+    b, h = rec.pairs[index]
+    rep = PairReport((b, h))
+    with threadpool_limits(1):
+        ps = PairTokenStream(wl, b, h, seed_offset=rec.seed_offset)
+        oc = PairCache(wl.budget, wl.head_dim, sink_size=wl.sink_size)
+        if rec.prefill > 0:
+            K, V = ps.prefill(rec.prefill)
+            oc.prefill(K, V)
+        snaps = {s[0]: s for s in rec.snapshots}
+        tol = TOL[wl.dtype]
+        for t0 in range(0, rec.steps, BLOCK):
+            cnt = min(BLOCK, rec.steps - t0)
+            q, kn, vn = ps.steps(cnt)
+            for j in range(cnt):
+                t = t0 + j
+                res = oc.attend(q[j], kn[j], vn[j])
+                gout = rec.out[t, index]
+                err = row_rel_err(gout, res.out)
+                rep.max_rel_err = max(rep.max_rel_err, err)
+                if err > tol and _fail(rep, f"step {t}: out rel err {err:.3g} > {tol}"):
+                    return rep
+                if wl.dtype == "bf16":
+                    exc, bad, n = bf16_rounding_check(gout, res.out)
+                    rep.bf16_mid_exceptions += exc
+                    rep.bf16_elements += n
+                    if bad and _fail(rep, f"step {t}: {bad} bf16 outputs differ from RNE(oracle)"):
+                        return rep
+                e = int(rec.evicted[t, index])
+                chosen = None
+                if res.evicted < 0:
+                    rep.appends += 1
+                    if e != -1 and _fail(rep, f"step {t}: expected an append, GPU evicted {e}"):
+                        return rep
+                else:
+                    rep.evictions += 1
+                    if rep.fill_to_evict_step < 0:
+                        rep.fill_to_evict_step = t
+                    if res.near_tie:
+                        rep.near_ties += 1
+                        finite = np.sort(res.scores[np.isfinite(res.scores)])
+                        if finite.size >= 2 and finite[0] == finite[1]:
+                            rep.exact_ties += 1
+                            rep.tie_lowest_index += int(e == res.evicted)
+                        if e not in res.legal:
+                            if _fail(rep, f"step {t}: GPU slot {e} outside near-tie set {res.legal}"):
+                                return rep
+                        else:
+                            chosen = e
+                    elif e != res.evicted:
+                        if _fail(rep, f"step {t}: GPU evicted {e}, oracle {res.evicted}"):
+                            return rep
+                oc.commit(res, kn[j], vn[j], chosen)
+                rep.steps += 1
+                if t + 1 in snaps:
+                    _, Ks, Vs, VNs, Fs = snaps[t + 1]
+                    n = oc.n
+                    rep.snapshots += 1
+                    if int(Fs[index]) != n:
+                        _fail(rep, f"after step {t + 1}: fill {int(Fs[index])} != {n}")
+                    elif not (np.array_equal(Ks[index, :n], oc.K[:n])
+                              and np.array_equal(Vs[index, :n], oc.V[:n])):
+                        _fail(rep, f"after step {t + 1}: cached K/V rows differ")
+                    elif not np.allclose(VNs[index, :n], oc.vnorm[:n], rtol=2e-6, atol=0):
+                        _fail(rep, f"after step {t + 1}: sidecar differs")
+                    if rep.failures:
+                        return rep
+    return rep
+
+
+def check_trajectory(rec: Record, workers: int = 0):
+    """Replay every sampled pair in the oracle; returns the per-pair reports.
+    Fails (AssertionError) with the first failures of each failing pair."""
+    global _RECORD
+    if workers <= 0:
+        workers = min(len(rec.pairs), len(os.sched_getaffinity(0)), 8)
+    _RECORD = rec
+    try:
+        if workers == 1:
+            reports = [_check_pair(i) for i in range(len(rec.pairs))]
+        else:
+            # fork: the workers inherit the record and run NumPy only (they
+            # never touch the GPU), and no program is exec'd.
+            with multiprocessing.get_context("fork").Pool(workers) as pool:
+                reports = pool.map(_check_pair, range(len(rec.pairs)), chunksize=1)
+    finally:
+        _RECORD = None
+    bad = [r for r in reports if r.failures]
+    assert not bad, "; ".join(f"pair {r.pair}: {r.failures}" for r in bad)
+    total = sum(r.bf16_elements for r in reports)
+    exc = sum(r.bf16_mid_exceptions for r in reports)
+    assert exc <= max(4, BF16_MID_SHARE * total), f"{exc} bf16 boundary exceptions in {total}"
+    return reports
+
+
+def summary(rec: Record, reports) -> str:
+    tot = lambda k: sum(getattr(r, k) for r in reports)
+    s = (f"{rec.wl.name} B={rec.wl.budget} batch={rec.wl.batch} ({rec.launch}): "
+         f"{len(reports)} pairs x {rec.steps} steps, evictions {tot('evictions')}, "
+         f"appends {tot('appends')}, near-ties {tot('near_ties')}, exact ties "
+         f"{tot('exact_ties')} (lowest index {tot('tie_lowest_index')}), max rel err "
+         f"{max(r.max_rel_err for r in reports):.3g}, snapshots {tot('snapshots')}")
+    if rec.wl.dtype == "bf16":
+        s += (f", bf16 = RNE(oracle) except {tot('bf16_mid_exceptions')} boundary "
+              f"exceptions in {tot('bf16_elements')}")
+    return s
