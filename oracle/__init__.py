@@ -8,8 +8,7 @@ Both sides consume the same seeded inputs from the input-generator module,
 which holds none of the method's arithmetic.
 
 Modules:
-  longflow_oracle  the step as the pages define it, in float64 (NumPy)
-  page_step        an independent second re-expression of the blog's own
-                   step semantics (deferred eviction, head-summed score),
-                   used to pin the first one
+  longflow_oracle  the step as the pages define it, in float64 (NumPy), with
+                   the variants (l2 score, deferred order, one victim per
+                   sequence) as options
 """

@@ -31,8 +31,9 @@ Readings taken where the pages are silent or ambiguous (each listed in the
 design notes): the score is summed over the G query heads of one KV head and
 uses each head's own normalised alpha (the blog's code sums over all heads of
 a sequence); the ordering is score -> argmin -> write within one step (the
-blog defers the write to the next step; the two evict the same tokens, see
-page_step.py); sinks default to 0; ||v||_1 is taken over the stored values.
+blog defers the write to the next step; run with one more slot, that order
+evicts the same tokens, which the tests check against order="deferred");
+sinks default to 0; ||v||_1 is taken over the stored values.
 
 Variants (each a runtime option of the same step; the defaults above are the
 main path):

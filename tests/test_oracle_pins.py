@@ -2,8 +2,9 @@
 
 Nothing here touches a GPU. Each test checks the oracle against something other
 than itself: hand-derived worked examples, an independent library routine,
-closed forms, brute force on tiny inputs, invariants, and an independent
-re-expression of the blog engine's step semantics.
+closed forms, brute force on tiny inputs, invariants, and the equivalence
+of the same-step order with the blog engine's deferred order at one more
+slot.
 """
 import glob
 import json
@@ -15,7 +16,6 @@ import torch
 
 from decode_kv_cache_02_amd.synth import WORKLOADS, TokenStream
 from oracle import longflow_oracle as lo
-from oracle.page_step import DeferredEvictionEngine
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -79,7 +79,8 @@ def test_golden_fill_no_evict():
 
 def test_golden_fixture_set_is_complete():
     names = sorted(os.path.basename(p) for p in glob.glob(os.path.join(GOLDEN, "*.json")))
-    assert names == ["hand_deferred_order.json", "hand_fill_no_evict.json",
+    assert names == ["hand_deferred_order.json", "hand_deferred_shared.json",
+                     "hand_fill_no_evict.json",
                      "hand_gqa_normalised.json", "hand_l2_vs_l1.json",
                      "hand_mha_two_steps.json", "hand_tie_and_sinks.json"]
 
@@ -273,31 +274,37 @@ def test_p5_query_approximation_reported():
 
 
 # ----------------------------------------------------------------------------
-# P6: the blog engine's deferred step evicts the same tokens (budget B+1)
+# P6: the engine's deferred order at budget B+1 replaces the same tokens
 # ----------------------------------------------------------------------------
 
-def test_p6_matches_blog_engine_semantics():
+def test_p6_deferred_order_at_b_plus_1_replaces_the_same_tokens():
+    """The Guide engine (§End-to-End Implementation) writes each token into
+    the victim chosen by the previous call. Run with one more slot, it attends
+    exactly the token set the same-step order attends at budget B, so the
+    outputs agree and the token the same-step order evicts at step t is the
+    token the deferred order replaces at step t + 1 (reading R1). The two
+    orders are separate code in the oracle; a ledger maps slots to tokens."""
     wl = WORKLOADS["tiny_f32"]          # 1 KV head, 2 query heads, B = 64
     ts = TokenStream(wl)
     pf = ts.prefill()
-    c = lo.PairCache(wl.budget, wl.head_dim)
-    c.prefill(pf.k[0, :, 0], pf.v[0, :, 0])
-    eng = DeferredEvictionEngine(2, wl.head_dim, wl.budget + 1)
-    rep = lambda x: np.repeat(np.asarray(x, np.float64)[None], 2, axis=0)
-    eng.load(rep(pf.k[0, :, 0]), rep(pf.v[0, :, 0]), np.arange(64))
-    token_in_slot = list(range(64))
+    same = lo.PairCache(wl.budget, wl.head_dim)
+    defer = lo.PairCache(wl.budget + 1, wl.head_dim, order="deferred")
+    for c in (same, defer):
+        c.prefill(pf.k[0, :, 0], pf.v[0, :, 0])
+    led_s = list(range(64))
+    led_d = list(range(64)) + [-1]
     ours, theirs = [], []
     for t in range(wl.steps):
         st = ts.step()
-        r = c.step(st.q[0], st.k_new[0, 0], st.v_new[0, 0])
-        assert not r.near_tie
-        ours.append(token_in_slot[r.evicted])
-        token_in_slot[r.evicted] = 64 + t
-        out, replaced = eng.advance(st.q[0].astype(np.float64), rep(st.k_new[0, 0]),
-                                    rep(st.v_new[0, 0]), 64 + t)
-        np.testing.assert_allclose(out, r.out, rtol=1e-12, atol=1e-13)
-        theirs.append(replaced)
-    # the engine replaces at call t+1 the token it picked at call t
+        r = same.step(st.q[0], st.k_new[0, 0], st.v_new[0, 0])
+        rd = defer.step(st.q[0], st.k_new[0, 0], st.v_new[0, 0])
+        assert not r.near_tie and not rd.near_tie
+        np.testing.assert_allclose(rd.out, r.out, rtol=1e-12, atol=1e-13)
+        ours.append(led_s[r.evicted])
+        led_s[r.evicted] = 64 + t
+        theirs.append(-1 if rd.evicted < 0 else led_d[rd.evicted])
+        led_d[rd.slot] = 64 + t
+    # the deferred order replaces at call t+1 the token it picked at call t
     assert theirs[0] == -1
     assert ours[:-1] == theirs[1:]
     assert len(set(ours)) == len(ours)
