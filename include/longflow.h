@@ -147,12 +147,16 @@ typedef struct {
 } lf_view;
 
 /* Bytes lf_cache_create would allocate for `cfg` (nothing is allocated).
- * Lets a caller size the batch to the device memory. */
+ * Lets a caller size the batch to the device memory. The size follows from
+ * the static buffer of `budget` slots per pair fixed up front (LongFlow
+ * Guide, §Static Memory Pre-Allocation and In-Place Eviction). */
 lf_status lf_cache_bytes(const lf_config* cfg, size_t* bytes);
 
 /* Validate `cfg`, make the one device allocation on the current device, zero
  * it (every fill level starts at 0) and return the handle in *out. On error
- * *out is set to NULL and nothing stays allocated. */
+ * *out is set to NULL and nothing stays allocated. This is the static
+ * pre-allocation of LongFlow Guide, §Static Memory Pre-Allocation and
+ * In-Place Eviction: one fixed buffer per pair, never resized or compacted. */
 lf_status lf_cache_create(const lf_config* cfg, lf_cache** out);
 
 /* Initial fill of one layer (LongFlow Guide, §Static Memory..., item 1).
@@ -169,7 +173,13 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out);
 lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void* v,
                           const int32_t* n_per_seq, int32_t n_max, void* stream);
 
-/* One fused decode step of every pair of one layer (the hot path).
+/* One fused decode step of every pair of one layer (the hot path): the
+ * attention output (LongFlow Guide, §Mathematical Derivation of the LongFlow
+ * Score, the alpha and o_t equations), the score alpha * ||v||_1 of every
+ * cached token (same section, the c_{t,i} and Score equations; gist.science
+ * summary, §2.1), and the argmin slot overwritten in place by the new token
+ * (Guide, §Static Memory Pre-Allocation and In-Place Eviction, items 2-3),
+ * in one pass over the cache (gist.science summary, §2.3).
  *   q             device [batch][num_q_heads][head_dim], cfg.dtype
  *   k_new, v_new  device [batch][num_kv_heads][head_dim], cfg.dtype
  *   out           device [batch][num_q_heads][head_dim], cfg.dtype; written
@@ -223,12 +233,15 @@ lf_status lf_decode_step_noalloc(lf_cache* c, int32_t layer, const void* q, cons
                                  const void* v_new, void* out, int32_t* evicted_slot,
                                  void* stream);
 
-/* Fill the view of one layer. */
+/* Fill the view of one layer: where the static buffer of LongFlow Guide,
+ * §Static Memory Pre-Allocation and In-Place Eviction, sits in device
+ * memory. */
 lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view);
 
-/* Snapshot of one layer into caller-owned DEVICE buffers, stream-ordered
- * device-to-device copies (tests, checkpoints; the static layout makes each a
- * single contiguous copy):
+/* Snapshot of one layer (the static buffer of LongFlow Guide, §Static Memory
+ * Pre-Allocation and In-Place Eviction) into caller-owned DEVICE buffers,
+ * stream-ordered device-to-device copies (tests, checkpoints; the static
+ * layout makes each a single contiguous copy):
  *   k, v    [batch][num_kv_heads][slots_padded*head_dim] cfg.dtype, in the
  *           layouts of lf_view (K tiled, V row-major)
  *   vnorm   [batch][num_kv_heads][slots_padded] float32
@@ -238,7 +251,12 @@ lf_status lf_cache_view(const lf_cache* c, int32_t layer, lf_view* view);
 lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, float* vnorm,
                             int32_t* fill, int32_t* victim, void* stream);
 
-/* Split-K tuning. By default each launch picks how many workgroups share a
+/* Launch-shape tuning of the fused pass (LongFlow Guide, §Fused
+ * High-Performance Triton Attention Kernel: one pass over the cache per
+ * step; these calls only choose how that pass is spread over workgroups and
+ * never change what it computes beyond float32 rounding).
+ *
+ * Split-K. By default each launch picks how many workgroups share a
  * pair: 1 when the layer has at least as many pairs as the device has
  * compute units; otherwise about (compute units / pairs), at most
  * lf_cache_max_splits and 16, with at least 256 slots per split. The
@@ -250,7 +268,7 @@ lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, 
 lf_status lf_cache_set_splits(lf_cache* c, int32_t splits);
 lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits);
 
-/* Workgroup size of the decode launches. By default a launch that holds at
+/* Launch-shape tuning (as above): workgroup size of the decode launches. By default a launch that holds at
  * most one workgroup per compute unit uses 8 waves (512 threads) per
  * workgroup, and any larger launch 4 waves, two workgroups per compute unit.
  * 4 or 8 forces that size (8 falls back to 4 where its LDS does not fit); 0
@@ -259,7 +277,7 @@ lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits);
  * values. */
 lf_status lf_cache_set_waves(lf_cache* c, int32_t waves);
 
-/* Loop of the decode launches. By default a launch whose workgroups each
+/* Launch-shape tuning (as above): loop of the decode launches. By default a launch whose workgroups each
  * stream at most 1024 slots uses the interleaved loop (each wave streams the
  * K and the V of the same 16 slots together, with its own online softmax),
  * and longer streams the phased loop (all K, then all V). 1 forces the
@@ -268,7 +286,9 @@ lf_status lf_cache_set_waves(lf_cache* c, int32_t waves);
  * of the scores. Errors: LF_ERR_INVALID_ARG for other values. */
 lf_status lf_cache_set_loop(lf_cache* c, int32_t loop);
 
-/* Host-side copy of the fill levels of one layer, [batch] int32 into the
+/* Host-side copy of the fill levels of one layer (tokens held per pair: the
+ * initial fill of LongFlow Guide, §Static Memory Pre-Allocation and In-Place
+ * Eviction, item 1, grows to the budget), [batch] int32 into the
  * caller's HOST array. Tracked on the host from the calls made (no device
  * access, no synchronisation). */
 lf_status lf_fill_levels(const lf_cache* c, int32_t layer, int32_t* fill_host);
@@ -289,11 +309,14 @@ lf_status lf_fill_levels(const lf_cache* c, int32_t layer, int32_t* fill_host);
  * range. */
 lf_status lf_seq_reset(lf_cache* c, const int32_t* seqs, int32_t count, void* stream);
 
-/* Release the handle and its device memory. NULL is a no-op. The caller must
- * make sure no queued work still uses the cache. */
+/* Release the handle and its device memory (the static buffer of LongFlow
+ * Guide, §Static Memory Pre-Allocation and In-Place Eviction, freed once).
+ * NULL is a no-op. The caller must make sure no queued work still uses the
+ * cache. */
 void lf_cache_destroy(lf_cache* c);
 
-/* Static string naming a status code. */
+/* Static string naming a status code. No page defines it: it names this
+ * library's own error codes. */
 const char* lf_status_str(lf_status s);
 
 #ifdef __cplusplus
