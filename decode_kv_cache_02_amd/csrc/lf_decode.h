@@ -1428,7 +1428,11 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
                                : load16(static_cast<const T*>(P.v_new) + pr * D + (j - kRowLoads) * EPL));
           }
         }
-        if (tid < hk) P.vnorm[(static_cast<int64_t>(b) * hk + tid) * slots_pad + choice] = pre_norm;
+        // Every head's ||v_new|| at the victim slot (heads past the first NT
+        // read theirs now; the first NT were prefetched).
+        for (int hh = tid; hh < hk; hh += NT)
+          P.vnorm[(static_cast<int64_t>(b) * hk + hh) * slots_pad + choice] =
+              hh == tid ? pre_norm : ws_load(P.ws_nnorm + static_cast<int64_t>(b) * hk + hh);
       }
       for (int hh = tid; hh < hk; hh += NT) P.evicted[static_cast<int64_t>(b) * hk + hh] = choice;
       return;

@@ -129,6 +129,17 @@ def test_shared_scope_exact_ties(order, loop):
     assert rep.tie_lowest_index == rep.exact_ties
 
 
+@pytest.mark.parametrize("order", ["same_step", "deferred"])
+def test_shared_scope_more_kv_heads_than_threads(order):
+    """600 KV heads per sequence (600 pairs: 4-wave workgroups of 256
+    threads): the deciding workgroup writes every head's new row and norm,
+    including the heads past its thread count (checked in the cache)."""
+    wl = WORKLOADS["tiny_f32"].with_(num_q_heads=600, num_kv_heads=600)
+    _say(f"f32 shared scope ({order}), batch 1, 600 KV heads, B 64, 20 steps")
+    rep = run_lockstep(wl, 20, scope="sequence", order=order, check_cache_every=5)
+    assert rep.evictions >= 19 * 600
+
+
 def test_shared_scope_llama_layer_sampled_sequences():
     wl = WORKLOADS["llama8b_layer"].with_(prefill=3277)
     _say("llama8b layer, shared scope, steady state, 4 steps, sequences 0 and 63")
