@@ -401,7 +401,9 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   constexpr int LPS = D / EPL;              // lanes per V row
   constexpr int SPI = kWave / LPS;          // V rows per wave-wide load
   constexpr uint32_t kRowBytes = D * kBytes;
-  constexpr int kScoreBatch = 16;           // sidecar loads in flight per thread
+  // sidecar loads in flight per thread: the first batch covers NT * kScoreBatch
+  // slots (4096 for either workgroup size); later batches load in the loop
+  constexpr int kScoreBatch = WAVES >= 8 ? 8 : 16;
   constexpr int kRowLoads = D * kBytes / 16;
   constexpr int kVLoads = 16 / SPI;         // wave-wide V loads per 16-slot tile (= kChunks)
   static_assert(G == 1 || G == 2 || G == 4, "group width");
