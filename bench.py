@@ -107,23 +107,37 @@ def prepared_ring(cache, ring, out, ev, layers=1):
             for q, kn, vn in ring]
 
 
-def time_steps(cache, ring, out, ev, steps, warmup):
-    """Run warmup + timed steps on the current stream; returns ms per step."""
+REPEATS = 5
+
+
+def timed_windows(run, steps, repeats=REPEATS):
+    """Time `steps` calls of run(t) as `repeats` consecutive windows, each
+    bracketed by HIP events on the current stream (the one the library's
+    kernels are queued on). Returns ms per step of every window."""
     import torch
+    stream = torch.cuda.current_stream()
+    bounds = [round(steps * r / repeats) for r in range(repeats + 1)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    torch.cuda.synchronize()
+    events[0].record(stream)
+    for r in range(repeats):
+        for t in range(bounds[r], bounds[r + 1]):
+            run(t)
+        events[r + 1].record(stream)
+    torch.cuda.synchronize()
+    return [events[r].elapsed_time(events[r + 1]) / max(1, bounds[r + 1] - bounds[r])
+            for r in range(repeats)]
+
+
+def time_steps(cache, ring, out, ev, steps, warmup):
+    """Warmup, then `steps` timed steps in 5 windows; returns (median ms per
+    step, the windows' ms per step)."""
     args = prepared_ring(cache, ring, out, ev)
     step = cache.step_prepared
     for t in range(warmup):
         step(args[t % RING][0])
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for t in range(steps):
-        step(args[t % RING][0])
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    windows = timed_windows(lambda t: step(args[t % RING][0]), steps)
+    return float(np.median(windows)), windows
 
 
 def make_ring(wl, dtype):
@@ -135,34 +149,68 @@ def make_ring(wl, dtype):
     return [(dev(q[i]), dev(k[i]), dev(v[i])) for i in range(RING)]
 
 
-def cpu_baseline(wl, seconds: float):
-    """The float64 oracle on a bounded sample of the same workload (all pairs,
-    cache full, as many whole-batch steps as fit in ~`seconds`, at least 1)."""
+def _cpu_worker(wl, pairs, seconds, start, results):
+    """One host core: step its share of the pairs through the oracle, every
+    pair full, for about `seconds` after the common start. Inputs are drawn
+    before the start (they are resident, as on the GPU)."""
     from threadpoolctl import threadpool_limits
-    from decode_kv_cache_02_amd.synth import TokenStream
-    from oracle.longflow_oracle import LayerCache
+    from decode_kv_cache_02_amd.synth import PairTokenStream
+    from oracle.longflow_oracle import PairCache
     with threadpool_limits(limits=1):
-        ts = TokenStream(wl, seed_offset=99)
-        pf = ts.prefill(n_max=wl.budget)
-        layer = LayerCache(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget)
-        layer.prefill(pf.k, pf.v, pf.n_per_seq)
-        del pf
+        caches, inputs = [], []
+        for b, h in pairs:
+            ps = PairTokenStream(wl, b, h, seed_offset=99)
+            c = PairCache(wl.budget, wl.head_dim)
+            c.prefill(*ps.prefill(wl.budget))
+            caches.append(c)
+            inputs.append(ps.steps(RING))
+        start.wait()
         steps = 0
         t0 = time.perf_counter()
         while True:
-            st = ts.step()
-            layer.step(st.q, st.k_new, st.v_new)
+            for c, (q, kn, vn) in zip(caches, inputs):
+                i = steps % RING
+                c.step(q[i], kn[i], vn[i])
             steps += 1
             el = time.perf_counter() - t0
-            if el >= seconds or steps >= 64:
+            if el >= seconds:
                 break
-    sps = steps / el
-    return {"value": sps * wl.batch, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "steps_per_s": sps, "host_cores_available": len(os.sched_getaffinity(0)),
-            "sample": f"{steps} whole-batch steps of {wl.name} with every pair full "
-                      f"({wl.batch * wl.num_kv_heads} pairs x {wl.budget} slots), float64 NumPy, "
-                      f"one BLAS thread (the oracle steps one pair at a time; its G x n products "
-                      f"are too small for BLAS threads to help), {el:.1f} s"}
+    results.put((len(pairs), steps, el))
+
+
+def cpu_baseline(wl, seconds: float):
+    """The float64 oracle on every host core, on a bounded sample of the same
+    workload: one process per core (one BLAS thread each), the pairs dealt out
+    round robin, every pair full. Each process steps all of its pairs once per
+    round, for about `seconds`. Must run before the process touches the GPU
+    (the workers are forked)."""
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    all_pairs = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+    workers = max(1, min(cores, len(all_pairs)))
+    ctx = mp.get_context("fork")
+    start = ctx.Barrier(workers + 1)
+    results = ctx.Queue()
+    procs = [ctx.Process(target=_cpu_worker,
+                         args=(wl, all_pairs[w::workers], seconds, start, results))
+             for w in range(workers)]
+    for p in procs:
+        p.start()
+    start.wait()
+    got = [results.get() for _ in procs]
+    for p in procs:
+        p.join()
+    pair_steps_per_s = sum(n * st / el for n, st, el in got)
+    tokens_per_s = pair_steps_per_s / wl.num_kv_heads
+    pair_steps = sum(n * st for n, st, _ in got)
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "steps_per_s": tokens_per_s / wl.batch, "pair_steps_per_s": pair_steps_per_s,
+            "host_cores_available": cores,
+            "sample": f"{wl.name} with every pair full ({len(all_pairs)} pairs x {wl.budget} "
+                      f"slots): {workers} processes, one per host core, each stepping its "
+                      f"share of the pairs through the float64 NumPy oracle (one BLAS thread) "
+                      f"for {seconds:.0f} s; {pair_steps} pair-steps in all. tokens/s = "
+                      f"pair-steps/s / {wl.num_kv_heads} KV heads"}
 
 
 def full_kv_baseline(wl, steps, warmup, fills=(8704, 16384)):
@@ -184,11 +232,11 @@ def full_kv_baseline(wl, steps, warmup, fills=(8704, 16384)):
             cache.prefill(0, k, v, np.full(wl.batch, n, dtype=np.int32))
             del k, v
             torch.cuda.synchronize()
-            ms = time_steps(cache, ring, out, ev, steps, warmup)
+            ms, win = time_steps(cache, ring, out, ev, steps, warmup)
             nb = wl.batch * wl.num_kv_heads * algorithmic_bytes_per_pair(
                 n + warmup + steps // 2, wl.group, wl.head_dim, 2 if wl.dtype == "bf16" else 4,
                 False)
-            res[str(n)] = {"ms_per_step": ms, "tokens_per_s": wl.batch / ms * 1e3,
+            res[str(n)] = {"ms_per_step": ms, "ms_windows": win, "tokens_per_s": wl.batch / ms * 1e3,
                            "achieved_GBs": nb / ms / 1e6}
     finally:
         cache.close()
@@ -199,7 +247,8 @@ def full_kv_baseline(wl, steps, warmup, fills=(8704, 16384)):
 def steady_state(wl, steps, warmup, fill=None, mode="evict", layers=1, capacity=None,
                  ragged=None, seed=0, order="same_step", scope="kv_head", norm="l1"):
     """Time `steps` model steps (one lf_decode_step per layer) at the given
-    fill levels; returns (ms per model step, algorithmic bytes per model step)."""
+    fill levels, in 5 windows; returns (median ms per model step, algorithmic
+    bytes per model step, the windows' ms per model step)."""
     import torch
     from decode_kv_cache_02_amd.native import LongFlowCache
     from decode_kv_cache_02_amd.synth import device_prefill
@@ -229,16 +278,13 @@ def steady_state(wl, steps, warmup, fill=None, mode="evict", layers=1, capacity=
         for t in range(warmup):
             for a in args[t % RING]:
                 step(a)
-        torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for t in range(steps):
-            for a in args[t % RING]:
+
+        def model_step(t):
+            for a in args[(warmup + t) % RING]:
                 step(a)
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / steps
+
+        windows = timed_windows(model_step, steps)
+        ms = float(np.median(windows))
         # fill levels during the timed window (EVICT caps at the budget)
         n_mid = n + warmup + steps // 2
         if mode == "evict":
@@ -246,7 +292,7 @@ def steady_state(wl, steps, warmup, fill=None, mode="evict", layers=1, capacity=
         evict_flags = (n + warmup >= wl.budget) if mode == "evict" else np.zeros_like(n, bool)
         per_layer = sum(algorithmic_bytes_per_pair(int(nb), wl.group, wl.head_dim, e, bool(ev_))
                         for nb, ev_ in zip(n_mid, evict_flags)) * wl.num_kv_heads
-        return ms, per_layer * layers
+        return ms, per_layer * layers, windows
     finally:
         cache.close()
 
@@ -400,7 +446,7 @@ def tiny_latency(wl, steps: int = 2000, per_graph: int = 64):
         out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=ring[0][0].dtype,
                           device="cuda")
         ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
-        eager = time_steps(cache, ring, out, ev, steps, 50)
+        eager, _ = time_steps(cache, ring, out, ev, steps, 50)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -432,7 +478,8 @@ def stack_graph(wl, layers, model_steps, seed=0):
     """A stack with every pair full, one model step (an lf_decode_step per
     layer) captured in one HIP graph and replayed `model_steps` times with the
     same inputs (the step's cost depends on fill levels, not values). Returns
-    (ms per model step, algorithmic bytes per model step)."""
+    (median ms per model step over 5 windows, algorithmic bytes per model
+    step, the windows)."""
     import torch
     from decode_kv_cache_02_amd.native import LongFlowCache
     from decode_kv_cache_02_amd.synth import device_prefill
@@ -462,27 +509,21 @@ def stack_graph(wl, layers, model_steps, seed=0):
                 cache.step_prepared(cache.step_args(layer, q, kn, vn, out, ev))
         for _ in range(3):
             graph.replay()
-        torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(model_steps):
-            graph.replay()
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / model_steps
+        windows = timed_windows(lambda t: graph.replay(), model_steps)
+        ms = float(np.median(windows))
         per_layer = wl.batch * wl.num_kv_heads * algorithmic_bytes_per_pair(wl.budget, wl.group,
                                                                             wl.head_dim, e, True)
-        return ms, per_layer * layers
+        return ms, per_layer * layers, windows
     finally:
         cache.close()
 
 
-def batch_gain(wl):
+def batch_gain(wl, model_steps):
     """Each method on the 32-layer ragged stack at the largest batch its own
     cache allows in 0.95 x 288 GB, with the same start-offset distribution:
     the comparison of tokens/s at each method's own batch. Yields (workload,
-    ms per model step, algorithmic bytes per model step, extra fields)."""
+    ms per model step, algorithmic bytes per model step, windows, extra
+    fields)."""
     from decode_kv_cache_02_amd.native import lf_cache_bytes, make_config
     from decode_kv_cache_02_amd.synth import TokenStream
     rate = {}
@@ -490,28 +531,32 @@ def batch_gain(wl):
         b = int(0.95 * 288e9 // lf_cache_bytes(make_config(32, 1, 32, 8, 128, cap, mode=mode)))
         w = wl.with_(batch=b)
         offs = TokenStream(w).start_offsets()
-        ms, nb = steady_state(w, 10, 2, layers=32, mode=mode, capacity=cap,
-                              ragged=np.minimum(offs, cap) if mode == "evict" else offs, seed=6)
+        ms, nb, win = steady_state(w, model_steps, 2, layers=32, mode=mode, capacity=cap,
+                                   ragged=np.minimum(offs, cap) if mode == "evict" else offs, seed=6)
         rate[method] = b / ms
         extra = {"method": method,
                  "batch_rule": "largest batch with this method's cache alone in 0.95 x 288 GB"}
         if method == "full-KV":
             extra["longflow_tokens_per_s_over_full_kv"] = rate["LongFlow"] / rate["full-KV"]
-        yield w, ms, nb, extra
+        yield w, ms, nb, win, extra
 
 
 def suite(args):
-    """One JSON line per workload shape (steady state unless stated)."""
-    import torch
+    """One JSON line per workload shape (steady state unless stated). Lines
+    timed in windows report the median of 5 windows and every window."""
     from decode_kv_cache_02_amd.native import lf_cache_bytes, make_config
     from decode_kv_cache_02_amd.synth import WORKLOADS, TokenStream
 
-    def emit(name, wl, ms, nbytes, layers=1, extra=None):
+    def emit(name, wl, ms, nbytes, layers=1, extra=None, windows=None, steps=None):
         line = {"workload": name, "batch": wl.batch, "heads": f"{wl.num_q_heads}/{wl.num_kv_heads}",
                 "head_dim": wl.head_dim, "budget": wl.budget, "layers": layers,
                 "ms_per_model_step": ms, "tokens_per_s": wl.batch / ms * 1e3,
                 "achieved_GBs": nbytes / ms / 1e6,
                 "frac_of_peak": nbytes / ms / 1e6 / HBM_PEAK_GBS}
+        if steps is not None:
+            line["timed_model_steps"] = steps
+        if windows is not None:
+            line["ms_windows"] = windows
         line.update(extra or {})
         print(json.dumps(line), flush=True)
 
@@ -522,39 +567,42 @@ def suite(args):
     emit("tiny_f32 (launch-latency bound), one call per step", wl1, e_ms, nb1)
     emit("tiny_f32 (launch-latency bound), 64 steps per HIP graph replay", wl1, g_ms, nb1)
     wl2 = WORKLOADS["qwen3_0p6b_layer"]
-    ms, nb = steady_state(wl2, steps, warmup)
-    emit("qwen3_0p6b_layer", wl2, ms, nb)
+    ms, nb, win = steady_state(wl2, steps, warmup)
+    emit("qwen3_0p6b_layer", wl2, ms, nb, windows=win, steps=steps)
     wl3 = WORKLOADS["llama8b_layer"]
     for fill in (512, 1638, 3000):
-        ms, nb = steady_state(wl3, steps, warmup, fill=fill)
-        emit(f"llama8b_layer fill {fill} (appending)", wl3, ms, nb)
-    ms, nb = steady_state(wl3, steps, warmup)
-    emit("llama8b_layer steady state", wl3, ms, nb)
+        ms, nb, win = steady_state(wl3, steps, warmup, fill=fill)
+        emit(f"llama8b_layer fill {fill} (appending)", wl3, ms, nb, windows=win, steps=steps)
+    ms, nb, win = steady_state(wl3, steps, warmup)
+    emit("llama8b_layer steady state", wl3, ms, nb, windows=win, steps=steps)
     # a whole 16k-token generation from a 512-token prompt, LongFlow vs full-KV
     ms_lf, nb_lf = trajectory(wl3, 16384, 512, "evict")
     ms_fk, nb_fk = trajectory(wl3, 16384, 512, "full")
     emit("llama8b_layer whole generation: prompt 512 + 16384 tokens, LongFlow", wl3, ms_lf, nb_lf,
-         extra={"steps": 16384, "fill_steps": wl3.budget - 512})
+         extra={"fill_steps": wl3.budget - 512}, steps=16384)
     emit("llama8b_layer whole generation: prompt 512 + 16384 tokens, full-KV", wl3, ms_fk, nb_fk,
-         extra={"steps": 16384, "speedup_of_longflow": ms_fk / ms_lf})
+         extra={"speedup_of_longflow": ms_fk / ms_lf}, steps=16384)
     for label, kw in (("deferred order (the blog engine's)", dict(order="deferred")),
                       ("one victim per sequence", dict(scope="sequence")),
                       ("one victim per sequence, deferred order", dict(scope="sequence", order="deferred")),
                       ("l2 score", dict(norm="l2"))):
-        ms, nb = steady_state(wl3, steps, warmup, **kw)
-        emit(f"llama8b_layer steady state, {label}", wl3, ms, nb, extra={"variant": kw})
+        ms, nb, win = steady_state(wl3, steps, warmup, **kw)
+        emit(f"llama8b_layer steady state, {label}", wl3, ms, nb, extra={"variant": kw},
+             windows=win, steps=steps)
     ms, nb = churn(wl3, min(steps, 256), warmup)
     emit("llama8b_layer churn: 4 sequences recycled every 16 steps (512-token prompts)", wl3, ms, nb,
-         extra={"note": "reset + prefill inside the timed window; bytes include the prompts"})
+         extra={"note": "reset + prefill inside the timed window; bytes include the prompts"},
+         steps=min(steps, 256))
     shard = wl3.with_(num_q_heads=4, num_kv_heads=1)
-    ms, nb = steady_state(shard, steps, warmup)
-    emit("llama8b_layer tp8 shard (1 KV head per GPU)", shard, ms, nb)
+    ms, nb, win = steady_state(shard, steps, warmup)
+    emit("llama8b_layer tp8 shard (1 KV head per GPU)", shard, ms, nb, windows=win, steps=steps)
     # small batches: fewer pairs than CUs, so every launch is split-K
     for b in (1, 4, 16):
         small = wl3.with_(batch=b)
-        ms, nb = steady_state(small, steps, warmup)
-        emit(f"llama8b_layer batch {b} (split-K)", small, ms, nb)
-    # 32-layer ragged stack at the batch where both caches fit 0.95 x 288 GB
+        ms, nb, win = steady_state(small, steps, warmup)
+        emit(f"llama8b_layer batch {b} (split-K)", small, ms, nb, windows=win, steps=steps)
+    # 32-layer ragged stack at the batch where both caches fit 0.95 x 288 GB,
+    # over the workload's 512-step window (fill levels advance through it)
     wl4 = WORKLOADS["llama8b_stack32_ragged"]
     cfg_c = make_config(32, 1, 32, 8, 128, wl4.budget)
     cfg_f = make_config(32, 1, 32, 8, 128, 16384 + 512 + 64, mode="full")
@@ -562,23 +610,29 @@ def suite(args):
     batch = int(0.95 * 288e9 // per_seq)
     wl4 = wl4.with_(batch=batch)
     offsets = TokenStream(wl4).start_offsets()
-    ms, nb = steady_state(wl4, min(steps, 50), 5, layers=32,
-                          ragged=np.minimum(offsets, wl4.budget), seed=4)
+    ms, nb, win = steady_state(wl4, wl4.steps, 5, layers=32,
+                               ragged=np.minimum(offsets, wl4.budget), seed=4)
     emit("llama8b_stack32_ragged LongFlow", wl4, ms, nb, 32,
-         {"batch_rule": "largest batch with both caches in 0.95 x 288 GB", "evicting_seqs": int(np.sum(offsets >= wl4.budget))})
-    ms, nb = steady_state(wl4, min(steps, 20), 2, layers=32, mode="full",
-                          capacity=16384 + 512 + 64, ragged=offsets, seed=4)
-    emit("llama8b_stack32_ragged full-KV", wl4, ms, nb, 32)
-    for w, ms, nb, extra in batch_gain(wl4):
-        emit(f"llama8b_stack32_ragged {extra.pop('method')} at its own largest batch", w, ms, nb, 32, extra)
+         {"batch_rule": "largest batch with both caches in 0.95 x 288 GB",
+          "evicting_seqs": int(np.sum(offsets >= wl4.budget))}, windows=win, steps=wl4.steps)
+    ms, nb, win = steady_state(wl4, wl4.steps, 2, layers=32, mode="full",
+                               capacity=16384 + 512 + 64, ragged=offsets, seed=4)
+    emit("llama8b_stack32_ragged full-KV", wl4, ms, nb, 32, windows=win, steps=wl4.steps)
+    for w, ms, nb, win, extra in batch_gain(wl4, 50):
+        emit(f"llama8b_stack32_ragged {extra.pop('method')} at its own largest batch", w, ms, nb, 32,
+             extra, windows=win, steps=50)
+    # Qwen3-8B stack at every budget of the sweep, every pair full: 512 model
+    # steps each (of the workload's 16,384; the GPU time of a suite run bounds
+    # the window)
     wl5 = WORKLOADS["qwen3_8b_stack36_ties"]
     for budget in (512, 1024, 2048, 4096):
         w = wl5.with_(budget=budget)
-        ms, nb = steady_state(w, min(steps, 30), 3, layers=36, seed=5)
-        emit(f"qwen3_8b_stack36 B={budget}", w, ms, nb, 36)
+        ms, nb, win = steady_state(w, 512, 3, layers=36, seed=5)
+        emit(f"qwen3_8b_stack36 B={budget}", w, ms, nb, 36, windows=win, steps=512)
     w = wl5.with_(budget=512)
-    ms, nb = stack_graph(w, 36, min(steps, 30), seed=5)
-    emit("qwen3_8b_stack36 B=512, one HIP graph per model step", w, ms, nb, 36)
+    ms, nb, win = stack_graph(w, 36, 512, seed=5)
+    emit("qwen3_8b_stack36 B=512, one HIP graph per model step", w, ms, nb, 36, windows=win,
+         steps=512)
 
 
 def main():
@@ -593,8 +647,6 @@ def main():
               f"(each (sequence, KV head) pair is independent: a multi-GPU run would shard "
               f"the batch with no exchange).", file=sys.stderr)
         sys.exit(2)
-    import torch
-    from decode_kv_cache_02_amd.native import LongFlowCache
     from decode_kv_cache_02_amd.synth import WORKLOADS, device_prefill
 
     wl = WORKLOADS[args.workload]
@@ -605,6 +657,16 @@ def main():
     if args.kv_heads:
         wl = wl.with_(num_kv_heads=args.kv_heads, num_q_heads=args.kv_heads * wl.group)
     e = 2 if wl.dtype == "bf16" else 4
+    # The CPU baseline forks one worker per host core, so it runs before this
+    # process touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        print(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores",
+              file=sys.stderr, flush=True)
+
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache, lf_probe_hbm_attributes
     torch.cuda.set_device(0)
     print(f"[bench] {wl.name}: batch {wl.batch}, {wl.num_q_heads}/{wl.num_kv_heads} heads, "
           f"d {wl.head_dim}, B {wl.budget}, {wl.dtype}", file=sys.stderr, flush=True)
@@ -620,7 +682,7 @@ def main():
     ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
 
-    ms = time_steps(cache, ring, out, ev, args.steps, args.warmup)
+    ms, windows = time_steps(cache, ring, out, ev, args.steps, args.warmup)
     ev_host = ev.cpu().numpy()
     assert np.all(ev_host >= 0), "steady state must evict on every pair"
     pairs = wl.batch * wl.num_kv_heads
@@ -646,11 +708,8 @@ def main():
     if not args.no_full_kv:
         full = full_kv_baseline(wl, min(args.steps, 200), 10)
         print(f"[bench] full-KV: {json.dumps(full['at_fill'])}", file=sys.stderr, flush=True)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
-        print(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s", file=sys.stderr, flush=True)
-
+    mem_clock_khz, bus_bits = lf_probe_hbm_attributes()
+    per_transfer = mem_clock_khz * 1e3 * bus_bits / 8 / 1e9     # GB/s at one transfer per clock
     line = {
         "metric": METRIC,
         "value": steps_per_s * wl.batch,
@@ -669,6 +728,18 @@ def main():
                    "budget": wl.budget, "fill": wl.budget,
                    "phase": "steady state: every pair full, one eviction per pair per step"},
         "steps_per_s": steps_per_s,
+        "timing": {"ms_per_step": "median of 5 consecutive windows of steps/5 steps each, "
+                                  "HIP events on the stream the kernels run on",
+                   "ms_windows": windows, "ms_mean": float(np.mean(windows))},
+        "hbm_peak_device": {
+            "memory_clock_khz": mem_clock_khz, "bus_width_bits": bus_bits,
+            "GBs_at_2_transfers_per_clock": 2 * per_transfer,
+            "GBs_at_4_transfers_per_clock": 4 * per_transfer,
+            "consistent_with_measured": [k for k, m in (("2 per clock", 2), ("4 per clock", 4))
+                                         if m * per_transfer >= achieved],
+            "note": "clock x bus width / 8 per transfer, from the device attributes; a rate "
+                    "below the measured algorithmic GB/s is ruled out. roofline.peak stays "
+                    "the 8 TB/s vendor figure"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": bytes_launch,

@@ -1,6 +1,7 @@
-// Streaming-read probe (include/longflow_probe.h): every workgroup reads its
-// own contiguous region once with 16-byte non-temporal buffer loads, the same
-// loads the decode kernel uses for K and V, and XORs what it read.
+// Measurement probes (include/longflow_probe.h). Streaming read: every
+// workgroup reads its own contiguous region once with 16-byte non-temporal
+// buffer loads, the same loads the decode kernel uses for K and V, and XORs
+// what it read. HBM attributes: the device's own memory clock and bus width.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,4 +48,18 @@ extern "C" lf_status lf_probe_stream_read(const void* buf, size_t bytes, int32_t
                      static_cast<hipStream_t>(stream), static_cast<const char*>(buf),
                      static_cast<uint32_t>(region), static_cast<u32x4_t*>(sink));
   return hipGetLastError() == hipSuccess ? LF_OK : LF_ERR_HIP;
+}
+
+extern "C" lf_status lf_probe_hbm_attributes(int32_t* mem_clock_khz, int32_t* bus_width_bits) {
+  if (!mem_clock_khz || !bus_width_bits) return LF_ERR_INVALID_ARG;
+  int dev = 0, clock = 0, width = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&clock, hipDeviceAttributeMemoryClockRate, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&width, hipDeviceAttributeMemoryBusWidth, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return LF_ERR_HIP;
+  }
+  *mem_clock_khz = clock;
+  *bus_width_bits = width;
+  return LF_OK;
 }

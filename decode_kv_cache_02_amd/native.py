@@ -102,6 +102,8 @@ SIGNATURES = [
     # include/longflow_probe.h
     ("lf_probe_stream_read", ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                              ctypes.c_void_p, ctypes.c_void_p]),
+    ("lf_probe_hbm_attributes", ctypes.c_int, [ctypes.POINTER(ctypes.c_int32),
+                                                ctypes.POINTER(ctypes.c_int32)]),
 ]
 
 _lib = None
@@ -281,6 +283,15 @@ def lf_probe_stream_read(buf, workgroups: int, sink, stream=None) -> None:
         ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel() * buf.element_size()),
         int(workgroups), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))),
         "lf_probe_stream_read")
+
+
+def lf_probe_hbm_attributes():
+    """(memory clock kHz, bus width bits) of the current device
+    (include/longflow_probe.h)."""
+    clk, width = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load_library().lf_probe_hbm_attributes(ctypes.byref(clk), ctypes.byref(width)),
+           "lf_probe_hbm_attributes")
+    return int(clk.value), int(width.value)
 
 
 def untile_k(k_tiled, head_dim: int):

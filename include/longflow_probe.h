@@ -1,11 +1,12 @@
 /*
  * longflow_probe.h -- measurement helper shipped in liblongflow.so.
  *
- * Not part of the decode step. It reads a device buffer once with the same
- * loads the decode kernel uses for K and V (16-byte buffer loads,
- * non-temporal cache policy) and keeps an XOR of what it read, so a
+ * Not part of the decode step. lf_probe_stream_read reads a device buffer
+ * once with the same loads the decode kernel uses for K and V (16-byte buffer
+ * loads, non-temporal cache policy) and keeps an XOR of what it read, so a
  * benchmark can report the streaming-read bandwidth this GPU attains next to
- * the decode kernel's.
+ * the decode kernel's; lf_probe_hbm_attributes reports the device's own memory
+ * clock and bus width.
  */
 #ifndef LONGFLOW_PROBE_H
 #define LONGFLOW_PROBE_H
@@ -29,6 +30,14 @@ extern "C" {
  * LF_ERR_HIP if the launch fails. */
 lf_status lf_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups, void* sink,
                                void* stream);
+
+/* The memory attributes the current device reports about itself
+ * (hipDeviceAttributeMemoryClockRate in kHz, hipDeviceAttributeMemoryBusWidth
+ * in bits), from which a benchmark derives an HBM peak: clock x bus width / 8
+ * bytes per transfer per clock, times the transfers per clock of the memory.
+ * Host-only query; nothing is launched. Errors: LF_ERR_INVALID_ARG on a NULL
+ * pointer; LF_ERR_HIP if the runtime cannot report either attribute. */
+lf_status lf_probe_hbm_attributes(int32_t* mem_clock_khz, int32_t* bus_width_bits);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,7 @@ int main(void) {
   if (lf_decode_step(NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL) != LF_ERR_INVALID_ARG) return 6;
   if (lf_probe_stream_read(NULL, 16, 1, NULL, NULL) != LF_ERR_INVALID_ARG) return 7;
   if (lf_decode_step_noalloc(NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL) != LF_ERR_INVALID_ARG) return 8;
+  if (lf_probe_hbm_attributes(NULL, NULL) != LF_ERR_INVALID_ARG) return 9;
   lf_cache_destroy(NULL);
   printf("ok %zu\n", bytes2);
   return 0;

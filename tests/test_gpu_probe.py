@@ -38,3 +38,16 @@ def test_probe_rejects_bad_sizes():
     with pytest.raises(native.LongFlowError) as ei:
         native.lf_probe_stream_read(buf[:999], 1, sink)
     assert ei.value.status == native.LF_ERR_INVALID_ARG
+
+
+def test_hbm_attributes():
+    """The device reports its memory clock and bus width (MI355X: eight
+    1024-bit HBM3E stacks)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_kv_cache_02_amd.native import lf_probe_hbm_attributes
+    clock_khz, bus_bits = lf_probe_hbm_attributes()
+    print(f"\nHBM attributes: memory clock {clock_khz} kHz, bus {bus_bits} bits", flush=True)
+    assert clock_khz > 0
+    assert bus_bits % 1024 == 0 and bus_bits >= 4096
