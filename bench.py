@@ -96,6 +96,8 @@ def parse_args():
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--suite", action="store_true",
                     help="measure every workload shape (one JSON line each) instead of the bench line")
+    ap.add_argument("--wg-timing", action="store_true",
+                    help="per-workgroup timing records: how each launch spreads over the XCDs")
     return ap.parse_args()
 
 
@@ -635,8 +637,118 @@ def suite(args):
          steps=512)
 
 
+TICK_US = 0.01          # the device's constant clock (s_memrealtime): 100 MHz
+
+
+def summarize_wg_records(rec):
+    """Per-XCD and per-CU view of one launch's timing records ([wgs][4]
+    int64: start, end, XCC id | hardware id << 32, workgroup; 100 MHz)."""
+    rec = np.asarray(rec, dtype=np.int64)
+    start, end = rec[:, 0], rec[:, 1]
+    xcc = rec[:, 2] & 0xFFFF
+    hw = (rec[:, 2] >> 32) & 0xFFFFFFFF
+    cu_key = xcc * 256 + ((hw >> 8) & 0xFF)     # XCC, then the CU, SH and SE fields of HW_ID
+    t0 = int(start.min())
+    dur = (end - start) * TICK_US
+    xcds = []
+    for x in sorted(set(int(v) for v in xcc)):
+        m = xcc == x
+        xcds.append({"xcd": x, "workgroups": int(m.sum()), "mean_wg_us": float(dur[m].mean()),
+                     "mean_end_us": float(((end[m] - t0) * TICK_US).mean()),
+                     "last_end_us": float(((end[m] - t0) * TICK_US).max())})
+    busy = []
+    for k in set(int(v) for v in cu_key):
+        iv = sorted(zip(start[cu_key == k], end[cu_key == k]))
+        covered, cur_s, cur_e = 0, iv[0][0], iv[0][1]
+        for a, b in iv[1:]:
+            if a > cur_e:
+                covered += cur_e - cur_s
+                cur_s, cur_e = a, b
+            else:
+                cur_e = max(cur_e, b)
+        covered += cur_e - cur_s
+        busy.append(covered)
+    span = (int(end.max()) - t0) * TICK_US
+    ends = [x["last_end_us"] for x in xcds]
+    return {"workgroups": int(len(rec)), "span_us": span, "mean_wg_us": float(dur.mean()),
+            "cus": len(busy), "workgroups_per_cu_max": int(np.bincount(
+                np.unique(cu_key, return_inverse=True)[1]).max()),
+            "cu_busy_frac_mean": float(np.mean(busy) * TICK_US / span),
+            "xcd_last_end_spread_us": float(max(ends) - min(ends)), "xcd": xcds}
+
+
+def wg_timing(args):
+    """Per-workgroup timing records (lf_probe_decode_timing,
+    lf_probe_stream_read_timing) of the decode kernel on the benchmark shapes
+    and of the bare streaming read over the same bytes: how each launch
+    spreads over the XCDs. One JSON line per case: the launch with the median
+    span of 5 recorded launches (after warmup)."""
+    import torch
+    from decode_kv_cache_02_amd.native import (LongFlowCache, lf_probe_decode_timing,
+                                               lf_probe_stream_read_timing)
+    from decode_kv_cache_02_amd.synth import WORKLOADS, device_prefill
+    w3 = WORKLOADS["llama8b_layer"]
+    cases = [("llama8b_layer steady state", w3),
+             ("llama8b_layer tp8 shard", w3.with_(num_q_heads=4, num_kv_heads=1)),
+             ("qwen3_8b layer B=512 (batch 256)", WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=512))]
+    for name, wl in cases:
+        e = 2 if wl.dtype == "bf16" else 4
+        cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                              dtype=wl.dtype)
+        try:
+            k, v = device_prefill(wl, wl.budget, seed=wl.cfg_id)
+            cache.prefill(0, k, v, np.full(wl.batch, wl.budget, dtype=np.int32))
+            del k, v
+            ring = make_ring(wl, wl.dtype)
+            out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=ring[0][0].dtype,
+                              device="cuda")
+            ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+            recs = torch.zeros((wl.batch * wl.num_kv_heads * 16, 4), dtype=torch.int64, device="cuda")
+            args_ = prepared_ring(cache, ring, out, ev)
+            for t in range(20):
+                cache.step_prepared(args_[t % RING][0])
+            runs = []
+            for t in range(5):
+                q, kn, vn = ring[t % RING]
+                n = lf_probe_decode_timing(cache.handle, 0, q, kn, vn, out, ev, recs)
+                torch.cuda.synchronize()
+                runs.append(summarize_wg_records(recs[:n].cpu().numpy()))
+            runs.sort(key=lambda r: r["span_us"])
+            r = runs[2]
+            nb = wl.batch * wl.num_kv_heads * algorithmic_bytes_per_pair(
+                wl.budget, wl.group, wl.head_dim, e, True)
+            r.update({"case": f"decode_kernel, {name}", "algorithmic_bytes": nb,
+                      "GBs_over_span": nb / r["span_us"] / 1e3})
+            print(json.dumps(r), flush=True)
+        finally:
+            cache.close()
+    for name, total, wgs in (("read probe, the Llama-8B layer's bytes", 860_160_000, 512),
+                             ("read probe, the Qwen3-8B B=512 layer's bytes", 537_001_984, 2048)):
+        total -= total % (16 * wgs)
+        buf = torch.ones(total // 2, dtype=torch.int16, device="cuda")
+        sink = torch.empty(wgs * 256 * 4, dtype=torch.int32, device="cuda")
+        recs = torch.zeros((wgs, 4), dtype=torch.int64, device="cuda")
+        runs = []
+        for t in range(8):
+            lf_probe_stream_read_timing(buf, wgs, sink, recs)
+            torch.cuda.synchronize()
+            if t >= 3:
+                runs.append(summarize_wg_records(recs.cpu().numpy()))
+        runs.sort(key=lambda r: r["span_us"])
+        r = runs[2]
+        r.update({"case": f"{name} ({wgs} workgroups)", "algorithmic_bytes": total,
+                  "GBs_over_span": total / r["span_us"] / 1e3})
+        print(json.dumps(r), flush=True)
+        del buf, sink, recs
+
+
 def main():
     args = parse_args()
+    if args.wg_timing:
+        import torch
+        torch.cuda.set_device(0)
+        wg_timing(args)
+        return
     if args.suite:
         import torch
         torch.cuda.set_device(0)

@@ -318,6 +318,30 @@ struct DecodeParams {
   float* ws_score;      // [batch][num_kv_heads][slots_pad]: every head's score vector
   float* ws_nnorm;      // [batch][num_kv_heads]: every head's ||v_new||
   int32_t* seq_arrive;  // [batch]: KV heads done, back to 0 after every launch
+  uint64_t* wg_clock;   // optional: per-workgroup timing records (null: none)
+};
+
+// hwreg encodings for s_getreg: XCC_ID (the accelerator complex die a
+// workgroup runs on) and HW_ID (its SE, SH, CU, SIMD and wave slot).
+constexpr int kHwRegXccId = (15 << 11) | 20;
+constexpr int kHwRegHwId = (31 << 11) | 4;
+
+// Timing record of one workgroup, written by thread 0 when it returns: start
+// and end of thread 0 on the device's constant 100 MHz clock, where it ran,
+// and the workgroup index. Measurement only; a null record costs one
+// uniform branch at entry and at return.
+struct ClockRecord {
+  uint64_t* rec;
+  uint64_t start;
+  __device__ __forceinline__ ~ClockRecord() {
+    if (rec) {
+      rec[0] = start;
+      rec[1] = __builtin_amdgcn_s_memrealtime();
+      rec[2] = static_cast<uint64_t>(__builtin_amdgcn_s_getreg(kHwRegXccId)) |
+               (static_cast<uint64_t>(__builtin_amdgcn_s_getreg(kHwRegHwId)) << 32);
+      rec[3] = blockIdx.x;
+    }
+  }
 };
 
 // Cross-workgroup data of a split launch goes through relaxed agent-scope
@@ -429,6 +453,9 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   (void)sh_ticket;
 
   const int tid = threadIdx.x;
+  const ClockRecord clock_rec{P.wg_clock && tid == 0 ? P.wg_clock + 4 * static_cast<size_t>(blockIdx.x)
+                                                     : nullptr,
+                              P.wg_clock ? __builtin_amdgcn_s_memrealtime() : 0};
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
   const int pair = SPLIT ? static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.pairs)) : blockIdx.x;
@@ -1502,6 +1529,7 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   P.ws_part = W.part;
   P.ws_logit = W.logit;
   P.arrive = W.arrive;
+  P.wg_clock = W.wg_clock;
   const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits, ILV) : decode_lds_bytes(geo, ILV);
   if (lds == 0) return hipErrorInvalidValue;
   // Phased loop, one workgroup per pair with one victim per sequence: the

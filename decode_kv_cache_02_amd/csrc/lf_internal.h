@@ -48,6 +48,9 @@ struct SplitWork {
   float* score;       // [batch][num_kv_heads][slots_pad]
   float* new_norm;    // [batch][num_kv_heads]: ||v_new|| of every head
   int32_t* seq_arrive;  // [batch]
+  // Optional timing records, one per workgroup of the launch (null: none):
+  // [start, end, XCC id | hardware id << 32, workgroup index], uint64 each.
+  uint64_t* wg_clock = nullptr;
 };
 
 constexpr int kMaxSplits = 16;

@@ -15,8 +15,12 @@ constexpr int kUnroll = 4;           // loads in flight per thread
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kNonTemporal = 3;      // the decode kernel's K/V cache policy
 
+constexpr int kHwRegXccId = (15 << 11) | 20;
+constexpr int kHwRegHwId = (31 << 11) | 4;
+
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* buf, uint32_t region,
-                                                               u32x4_t* sink) {
+                                                               u32x4_t* sink, uint64_t* records) {
+  const uint64_t start = records ? __builtin_amdgcn_s_memrealtime() : 0;
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(buf) + static_cast<size_t>(blockIdx.x) * region, 0,
       static_cast<int>(region), kRsrcWord3);
@@ -31,12 +35,18 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* buf, 
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
   }
   sink[static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x] = acc;
+  if (records && threadIdx.x == 0) {
+    uint64_t* rec = records + 4 * static_cast<size_t>(blockIdx.x);
+    rec[0] = start;
+    rec[1] = __builtin_amdgcn_s_memrealtime();
+    rec[2] = static_cast<uint64_t>(__builtin_amdgcn_s_getreg(kHwRegXccId)) |
+             (static_cast<uint64_t>(__builtin_amdgcn_s_getreg(kHwRegHwId)) << 32);
+    rec[3] = blockIdx.x;
+  }
 }
 
-}  // namespace
-
-extern "C" lf_status lf_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups,
-                                          void* sink, void* stream) {
+lf_status launch_read(const void* buf, size_t bytes, int32_t workgroups, void* sink, uint64_t* records,
+                      void* stream) {
   if (!buf || !sink || workgroups < 1) return LF_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(buf) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 15u))
     return LF_ERR_INVALID_ARG;
@@ -46,8 +56,21 @@ extern "C" lf_status lf_probe_stream_read(const void* buf, size_t bytes, int32_t
   if (region >= (size_t{1} << 31)) return LF_ERR_INVALID_ARG;
   hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const char*>(buf),
-                     static_cast<uint32_t>(region), static_cast<u32x4_t*>(sink));
+                     static_cast<uint32_t>(region), static_cast<u32x4_t*>(sink), records);
   return hipGetLastError() == hipSuccess ? LF_OK : LF_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" lf_status lf_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups,
+                                          void* sink, void* stream) {
+  return launch_read(buf, bytes, workgroups, sink, nullptr, stream);
+}
+
+extern "C" lf_status lf_probe_stream_read_timing(const void* buf, size_t bytes, int32_t workgroups,
+                                                 void* sink, uint64_t* records, void* stream) {
+  if (!records) return LF_ERR_INVALID_ARG;
+  return launch_read(buf, bytes, workgroups, sink, records, stream);
 }
 
 extern "C" lf_status lf_probe_hbm_attributes(int32_t* mem_clock_khz, int32_t* bus_width_bits) {

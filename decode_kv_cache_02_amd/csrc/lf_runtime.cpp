@@ -24,6 +24,7 @@
 #include <vector>
 
 #include "../../include/longflow.h"
+#include "../../include/longflow_probe.h"
 #include "lf_internal.h"
 
 struct lf_cache {
@@ -293,10 +294,19 @@ bool scratch_work(const lf_cache* c, char* base, int32_t splits, lf::SplitWork* 
   return off <= lf::kScratchBytes;
 }
 
+// Optional per-workgroup timing of one decode launch (measurement probe).
+struct Timing {
+  uint64_t* records;   // device [capacity][4]
+  int64_t capacity;
+  int32_t* workgroups; // host: the launch's workgroup count
+};
+
 // One decode step of one layer; `static_scratch` takes the launch's
-// workspace from the device's static array instead of the cache's own.
+// workspace from the device's static array instead of the cache's own;
+// `timing` (may be null) asks for per-workgroup timing records.
 lf_status decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_new, const void* v_new,
-                      void* out, int32_t* evicted_slot, void* stream, bool static_scratch) {
+                      void* out, int32_t* evicted_slot, void* stream, bool static_scratch,
+                      const Timing* timing = nullptr) {
   if (!c || !q || !k_new || !v_new || !out || !evicted_slot || layer < 0 ||
       layer >= c->cfg.num_layers)
     return LF_ERR_INVALID_ARG;
@@ -311,6 +321,12 @@ lf_status decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_n
   for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
   const LaunchShape shape = plan_launch(c, n_max);
   lf::SplitWork work = c->work;
+  if (timing) {
+    const int64_t wgs = c->layer_pairs * shape.splits;
+    if (!timing->records || !timing->workgroups || timing->capacity < wgs) return LF_ERR_INVALID_ARG;
+    *timing->workgroups = static_cast<int32_t>(wgs);
+    work.wg_clock = timing->records;
+  }
   if (static_scratch) {
     char* base = static_cast<char*>(lf::scratch_ptr(c->device));
     if (!base) return LF_ERR_HIP;  // set up by lf_cache_create on this device
@@ -575,6 +591,14 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
 lf_status lf_decode_step_noalloc(lf_cache* c, int32_t layer, const void* q, const void* k_new,
                                  const void* v_new, void* out, int32_t* evicted_slot, void* stream) {
   return decode_step(c, layer, q, k_new, v_new, out, evicted_slot, stream, true);
+}
+
+lf_status lf_probe_decode_timing(lf_cache* c, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, void* out, int32_t* evicted_slot,
+                                 uint64_t* records, int64_t capacity, int32_t* workgroups,
+                                 void* stream) {
+  const Timing t{records, capacity, workgroups};
+  return decode_step(c, layer, q, k_new, v_new, out, evicted_slot, stream, false, &t);
 }
 
 }  // extern "C"

@@ -104,6 +104,12 @@ SIGNATURES = [
                                              ctypes.c_void_p, ctypes.c_void_p]),
     ("lf_probe_hbm_attributes", ctypes.c_int, [ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_int32)]),
+    ("lf_probe_stream_read_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("lf_probe_decode_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
 ]
 
 _lib = None
@@ -283,6 +289,29 @@ def lf_probe_stream_read(buf, workgroups: int, sink, stream=None) -> None:
         ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel() * buf.element_size()),
         int(workgroups), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))),
         "lf_probe_stream_read")
+
+
+def lf_probe_stream_read_timing(buf, workgroups: int, sink, records, stream=None) -> None:
+    """lf_probe_stream_read with per-workgroup timing records (int64 device
+    tensor [workgroups][4]; include/longflow_probe.h)."""
+    _check(load_library().lf_probe_stream_read_timing(
+        ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel() * buf.element_size()),
+        int(workgroups), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(records.data_ptr()),
+        ctypes.c_void_p(_stream_ptr(stream))), "lf_probe_stream_read_timing")
+
+
+def lf_probe_decode_timing(handle: int, layer: int, q, k_new, v_new, out, evicted_slot, records,
+                           stream=None) -> int:
+    """One lf_decode_step writing per-workgroup timing records (int64 device
+    tensor [capacity][4]); returns the launch's workgroup count."""
+    wgs = ctypes.c_int32(0)
+    _check(load_library().lf_probe_decode_timing(
+        ctypes.c_void_p(handle), int(layer), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(evicted_slot.data_ptr()),
+        ctypes.c_void_p(records.data_ptr()), int(records.shape[0]), ctypes.byref(wgs),
+        ctypes.c_void_p(_stream_ptr(stream))), "lf_probe_decode_timing")
+    return int(wgs.value)
 
 
 def lf_probe_hbm_attributes():

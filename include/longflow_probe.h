@@ -5,8 +5,9 @@
  * once with the same loads the decode kernel uses for K and V (16-byte buffer
  * loads, non-temporal cache policy) and keeps an XOR of what it read, so a
  * benchmark can report the streaming-read bandwidth this GPU attains next to
- * the decode kernel's; lf_probe_hbm_attributes reports the device's own memory
- * clock and bus width.
+ * the decode kernel's; the timing variants record when and where each
+ * workgroup of a read or of a decode step ran; lf_probe_hbm_attributes
+ * reports the device's own memory clock and bus width.
  */
 #ifndef LONGFLOW_PROBE_H
 #define LONGFLOW_PROBE_H
@@ -30,6 +31,30 @@ extern "C" {
  * LF_ERR_HIP if the launch fails. */
 lf_status lf_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups, void* sink,
                                void* stream);
+
+/* lf_probe_stream_read with a timing record per workgroup: four uint64
+ * values, [start, end, XCC id | hardware id << 32, workgroup index]; start
+ * and end are thread 0's, on the device's constant 100 MHz clock
+ * (s_memrealtime); the XCC id names the accelerator complex die and the
+ * hardware id register its shader engine, CU, SIMD and wave slot.
+ *   records   device [workgroups][4] uint64
+ * Other arguments and errors as lf_probe_stream_read (records NULL is
+ * LF_ERR_INVALID_ARG). */
+lf_status lf_probe_stream_read_timing(const void* buf, size_t bytes, int32_t workgroups, void* sink,
+                                      uint64_t* records, void* stream);
+
+/* One lf_decode_step (the same launch plan, kernels and results) that also
+ * writes the timing record above for every workgroup of the launch.
+ *   records      device [capacity][4] uint64
+ *   workgroups   HOST out: the launch's workgroup count (pairs x splits)
+ * Errors: those of lf_decode_step, and LF_ERR_INVALID_ARG (nothing queued)
+ * on NULL records or workgroups, or capacity below the workgroup count.
+ * The records show how one launch spreads over the XCDs and CUs; they cost
+ * the decode kernel one uniform branch when not requested. */
+lf_status lf_probe_decode_timing(lf_cache* c, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, void* out, int32_t* evicted_slot,
+                                 uint64_t* records, int64_t capacity, int32_t* workgroups,
+                                 void* stream);
 
 /* The memory attributes the current device reports about itself
  * (hipDeviceAttributeMemoryClockRate in kHz, hipDeviceAttributeMemoryBusWidth

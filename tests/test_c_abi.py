@@ -35,6 +35,8 @@ int main(void) {
   if (lf_probe_stream_read(NULL, 16, 1, NULL, NULL) != LF_ERR_INVALID_ARG) return 7;
   if (lf_decode_step_noalloc(NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL) != LF_ERR_INVALID_ARG) return 8;
   if (lf_probe_hbm_attributes(NULL, NULL) != LF_ERR_INVALID_ARG) return 9;
+  if (lf_probe_stream_read_timing(NULL, 16, 1, NULL, NULL, NULL) != LF_ERR_INVALID_ARG) return 10;
+  if (lf_probe_decode_timing(NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL, NULL) != LF_ERR_INVALID_ARG) return 11;
   lf_cache_destroy(NULL);
   printf("ok %zu\n", bytes2);
   return 0;

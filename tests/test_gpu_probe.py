@@ -51,3 +51,58 @@ def test_hbm_attributes():
     print(f"\nHBM attributes: memory clock {clock_khz} kHz, bus {bus_bits} bits", flush=True)
     assert clock_khz > 0
     assert bus_bits % 1024 == 0 and bus_bits >= 4096
+
+
+def test_timing_records_of_a_read_and_of_a_decode_step():
+    """The timing variants: every workgroup leaves one record (start <= end,
+    an XCC id, its index), and the timed decode step gives exactly what
+    lf_decode_step gives on a twin cache."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_kv_cache_02_amd import native
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import WORKLOADS, TokenStream
+    wgs = 512
+    buf = torch.ones(wgs * 256 * 4 * 16, dtype=torch.int32, device="cuda")
+    sink = torch.empty(wgs * 256 * 4, dtype=torch.int32, device="cuda")
+    rec = torch.zeros((wgs, 4), dtype=torch.int64, device="cuda")
+    native.lf_probe_stream_read_timing(buf, wgs, sink, rec)
+    r = rec.cpu().numpy()
+    assert (r[:, 1] >= r[:, 0]).all() and (r[:, 0] > 0).all()
+    assert sorted(r[:, 3]) == list(range(wgs))
+    xcc = r[:, 2] & 0xFFFF
+    print(f"\nread probe: {wgs} workgroups over XCCs {sorted(set(xcc.tolist()))}", flush=True)
+    assert (xcc < 64).all()
+
+    wl = WORKLOADS["llama8b_layer"].with_(batch=4, budget=600, prefill=600)   # 32 pairs: split-K
+    caches = [LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget)
+              for _ in range(2)]
+    try:
+        pf = TokenStream(wl).prefill()
+        dev = lambda x: torch.from_numpy(x).cuda().to(torch.bfloat16)
+        for c in caches:
+            c.prefill(0, dev(pf.k), dev(pf.v), pf.n_per_seq)
+        st = TokenStream(wl, seed_offset=1).step()
+        q, kn, vn = dev(st.q), dev(st.k_new), dev(st.v_new)
+        outs = [torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16,
+                            device="cuda") for _ in range(2)]
+        evs = [torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+               for _ in range(2)]
+        caches[0].decode_step(0, q, kn, vn, outs[0], evs[0])
+        recs = torch.zeros((1024, 4), dtype=torch.int64, device="cuda")
+        n = native.lf_probe_decode_timing(caches[1].handle, 0, q, kn, vn, outs[1], evs[1], recs)
+        torch.cuda.synchronize()
+        assert n % 32 == 0 and n >= 32
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+        assert torch.equal(evs[0], evs[1])
+        r = recs[:n].cpu().numpy()
+        assert (r[:, 1] >= r[:, 0]).all() and (r[:, 0] > 0).all()
+        assert sorted(r[:, 3]) == list(range(n))
+        assert not recs[n:].any()
+        with pytest.raises(native.LongFlowError) as ei:
+            native.lf_probe_decode_timing(caches[1].handle, 0, q, kn, vn, outs[1], evs[1], recs[:n - 1])
+        assert ei.value.status == native.LF_ERR_INVALID_ARG
+    finally:
+        for c in caches:
+            c.close()
