@@ -120,7 +120,7 @@ def _oracle_record(wl, pairs, steps, prefill):
     snapshots = [(t, np.stack([x[0] for x in v]), np.stack([x[1] for x in v]),
                   np.stack([x[2] for x in v]), np.array([x[3] for x in v]))
                  for t, v in sorted(snaps.items())]
-    return trajectory.Record(wl, pairs, steps, prefill, 0, out, ev, snapshots)
+    return trajectory.Record(wl, pairs, steps, prefill, 0, out, ev, snapshots, capacity=wl.budget)
 
 
 def test_trajectory_checker_passes_the_oracle_and_fails_planted_mistakes():

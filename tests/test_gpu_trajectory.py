@@ -13,6 +13,14 @@ slot, and the pairs' cache regions every 1024 steps.
     (the suite's one-workgroup-per-pair launches): prompt 512, then filling
     and 512 evicting steps. Duplicates make exact score ties; each must go to
     the lowest slot.
+  * Split-K over the Llama-8B layer's whole trajectory: one GPU's share under
+    8-way tensor parallelism (64 pairs of one KV head) and batch 1 (8 pairs,
+    all checked). The planned split count grows with the cache (2 splits at
+    512 slots; 4 and 12 once it is full), so the trajectory crosses launch
+    shapes as well as the fill -> evict boundary.
+  * The full-KV baseline growing past 16k tokens (14,976 -> 16,896, the
+    Llama-8B layer at batch 8: split-K, each split streaming its ~4k slots
+    in 2048-slot LDS chunks).
 Each test prints its near-tie and exact-tie counts.
 """
 import pytest
@@ -23,14 +31,15 @@ import trajectory
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, steps, prefill, check_every=1024, pairs=8, seed=0):
+def _run(wl, steps, prefill, check_every=1024, pairs=8, seed=0, mode="evict"):
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     sampled = trajectory.sample_pairs(wl, pairs, seed=seed)
-    print(f"\n[case] {wl.name} B={wl.budget} batch={wl.batch}: prompt {prefill}, {steps} steps, "
-          f"pairs {sampled}", flush=True)
-    rec = trajectory.record_trajectory(wl, steps, sampled, prefill, check_every=check_every)
+    print(f"\n[case] {wl.name} {mode} B={wl.budget} batch={wl.batch} {wl.num_q_heads}/"
+          f"{wl.num_kv_heads}: prompt {prefill}, {steps} steps, pairs {sampled}", flush=True)
+    rec = trajectory.record_trajectory(wl, steps, sampled, prefill, check_every=check_every,
+                                       mode=mode)
     print(f"[case] recorded; checking {len(sampled)} pairs in the oracle", flush=True)
     reports = trajectory.check_trajectory(rec)
     print(trajectory.summary(rec, reports), flush=True)
@@ -64,3 +73,28 @@ def test_qwen3_8b_layer_budget_with_ties(budget):
     exact = sum(r.exact_ties for r in reports)
     assert exact > 0
     assert sum(r.tie_lowest_index for r in reports) == exact
+
+
+def _check_fill_then_evict(wl, reports):
+    fill_steps = wl.budget - wl.prefill
+    for r in reports:
+        assert r.appends == fill_steps and r.evictions == wl.steps - fill_steps
+        assert r.fill_to_evict_step == fill_steps
+
+
+def test_tp8_shard_whole_trajectory():
+    wl = WORKLOADS["llama8b_layer"].with_(num_q_heads=4, num_kv_heads=1)
+    _check_fill_then_evict(wl, _run(wl, wl.steps, wl.prefill, seed=7))
+
+
+def test_llama8b_batch1_whole_trajectory():
+    wl = WORKLOADS["llama8b_layer"].with_(batch=1)
+    _check_fill_then_evict(wl, _run(wl, wl.steps, wl.prefill, seed=1))
+
+
+def test_full_kv_growing_past_16k():
+    wl = WORKLOADS["llama8b_layer"].with_(batch=8)
+    prompt, steps = 14976, 1920
+    reports = _run(wl, steps, prompt, check_every=640, seed=4, mode="full")
+    for r in reports:
+        assert r.appends == steps and r.evictions == 0 and r.snapshots == 3

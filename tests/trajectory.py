@@ -62,18 +62,22 @@ class Record:
     evicted: np.ndarray                   # [steps][pairs] int32
     snapshots: list = field(default_factory=list)   # (steps done, K, V, vnorm, fill) per pair axis
     launch: str = ""
+    mode: str = "evict"                   # "full": the full-KV baseline (no eviction)
+    capacity: int = 0                     # slots per pair (the budget when evicting)
+    max_splits: int = 1                   # split-K workgroups the cache allows per pair
 
 
 def record_trajectory(wl: Workload, steps: int, pairs, prefill: int, check_every: int = 0,
                       seed_offset: int = 0, splits: int = 0, waves: int = 0,
-                      loop: str = "auto") -> Record:
+                      loop: str = "auto", mode: str = "evict") -> Record:
     import torch
     from decode_kv_cache_02_amd.native import LongFlowCache
 
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     G, d, P = wl.group, wl.head_dim, len(pairs)
-    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, d, wl.budget,
-                          sink_size=wl.sink_size, dtype=wl.dtype)
+    capacity = wl.budget if mode == "evict" else prefill + steps
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, d, capacity,
+                          sink_size=wl.sink_size, dtype=wl.dtype, mode=mode)
     try:
         if splits:
             cache.set_splits(splits)
@@ -137,7 +141,8 @@ def record_trajectory(wl: Workload, steps: int, pairs, prefill: int, check_every
         return Record(wl, list(pairs), steps, prefill, seed_offset,
                       rec_out.float().cpu().numpy().reshape(steps, P, G, d),
                       rec_ev.cpu().numpy(), snaps,
-                      launch=f"splits={splits or 'auto'} waves={waves or 'auto'} loop={loop}")
+                      launch=f"splits={splits or 'auto'} waves={waves or 'auto'} loop={loop}",
+                      mode=mode, capacity=capacity, max_splits=cache.max_splits)
     finally:
         cache.close()
 
@@ -181,7 +186,8 @@ def _check_pair(index: int) -> PairReport:
     rep = PairReport((b, h))
     with threadpool_limits(1):
         ps = PairTokenStream(wl, b, h, seed_offset=rec.seed_offset)
-        oc = PairCache(wl.budget, wl.head_dim, sink_size=wl.sink_size)
+        oc = PairCache(rec.capacity or wl.budget, wl.head_dim, sink_size=wl.sink_size,
+                       evict=rec.mode == "evict")
         if rec.prefill > 0:
             K, V = ps.prefill(rec.prefill)
             oc.prefill(K, V)
@@ -273,7 +279,8 @@ def check_trajectory(rec: Record, workers: int = 0):
 
 def summary(rec: Record, reports) -> str:
     tot = lambda k: sum(getattr(r, k) for r in reports)
-    s = (f"{rec.wl.name} B={rec.wl.budget} batch={rec.wl.batch} ({rec.launch}): "
+    s = (f"{rec.wl.name} {rec.mode} capacity={rec.capacity} batch={rec.wl.batch} "
+         f"{rec.wl.num_q_heads}/{rec.wl.num_kv_heads} heads ({rec.launch}, max splits {rec.max_splits}): "
          f"{len(reports)} pairs x {rec.steps} steps, evictions {tot('evictions')}, "
          f"appends {tot('appends')}, near-ties {tot('near_ties')}, exact ties "
          f"{tot('exact_ties')} (lowest index {tot('tie_lowest_index')}), max rel err "
