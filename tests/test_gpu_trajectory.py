@@ -9,9 +9,10 @@ slot, and the pairs' cache regions every 1024 steps.
     the interleaved loop to the phased one when the cache passes 1024 slots.
   * Qwen3-0.6B layer: batch 32, 16/8 heads, B = 1024, full prompt, all 4,096
     evicting steps.
-  * Qwen3-8B layer at batch 256 with 10% duplicated tokens, B = 2048 and 4096
-    (the suite's one-workgroup-per-pair launches): prompt 512, then filling
-    and 512 evicting steps. Duplicates make exact score ties; each must go to
+  * Qwen3-8B layer at batch 256 with 10% duplicated tokens at every budget of
+    the sweep, B = 512, 1024, 2048 and 4096 (the suite's one-workgroup-per-pair
+    launches): prompt 512, then all 16,384 steps, filling up to the budget and
+    evicting from then on. Duplicates make exact score ties; each must go to
     the lowest slot.
   * Split-K over the Llama-8B layer's whole trajectory: one GPU's share under
     8-way tensor parallelism (64 pairs of one KV head) and batch 1 (8 pairs,
@@ -63,13 +64,12 @@ def test_qwen3_0p6b_layer_whole_trajectory():
         assert r.evictions == wl.steps and r.appends == 0
 
 
-@pytest.mark.parametrize("budget", [2048, 4096])
+@pytest.mark.parametrize("budget", [512, 1024, 2048, 4096])
 def test_qwen3_8b_layer_budget_with_ties(budget):
     wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=budget)
-    steps = budget - wl.prefill + 512
-    reports = _run(wl, steps, wl.prefill, seed=5)
+    reports = _run(wl, wl.steps, wl.prefill, check_every=2048, seed=5)
     for r in reports:
-        assert r.appends == budget - wl.prefill and r.evictions == 512
+        assert r.appends == budget - wl.prefill and r.evictions == wl.steps - r.appends
     exact = sum(r.exact_ties for r in reports)
     assert exact > 0
     assert sum(r.tie_lowest_index for r in reports) == exact
