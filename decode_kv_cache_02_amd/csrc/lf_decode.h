@@ -319,6 +319,7 @@ struct DecodeParams {
   float* ws_nnorm;      // [batch][num_kv_heads]: every head's ||v_new||
   int32_t* seq_arrive;  // [batch]: KV heads done, back to 0 after every launch
   uint64_t* wg_clock;   // optional: per-workgroup timing records (null: none)
+  const int32_t* order; // FULL mode: sequences in launch order, longest first
 };
 
 // hwreg encodings for s_getreg: XCC_ID (the accelerator complex die a
@@ -458,10 +459,17 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
                               P.wg_clock ? __builtin_amdgcn_s_memrealtime() : 0};
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
-  const int pair = SPLIT ? static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.pairs)) : blockIdx.x;
+  // Workgroup -> (sequence b, KV head h). FULL mode dispatches the sequences
+  // longest first (P.order); the evicting cache keeps index order.
+  const int slot_in_launch =
+      SPLIT ? static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.pairs)) : blockIdx.x;
   const int split = SPLIT ? static_cast<int>(blockIdx.x / static_cast<uint32_t>(P.pairs)) : 0;
-  const int b = pair / P.num_kv_heads;
-  const int h = pair - b * P.num_kv_heads;
+  const int h = slot_in_launch % P.num_kv_heads;
+  int b = slot_in_launch / P.num_kv_heads;
+  if constexpr (!EVICT) {
+    if (P.order) b = min(max(P.order[b], 0), P.pairs / P.num_kv_heads - 1);
+  }
+  const int pair = b * P.num_kv_heads + h;
   const int64_t slots_pad = P.pair_elems / D;
 
   const T* K = static_cast<const T*>(P.kc) + pair * P.pair_elems;
@@ -1530,6 +1538,7 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   P.ws_logit = W.logit;
   P.arrive = W.arrive;
   P.wg_clock = W.wg_clock;
+  P.order = EVICT ? nullptr : L.order;
   const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits, ILV) : decode_lds_bytes(geo, ILV);
   if (lds == 0) return hipErrorInvalidValue;
   // Phased loop, one workgroup per pair with one victim per sequence: the

@@ -34,6 +34,9 @@ struct LayerPtrs {
   float* vnorm;
   int32_t* fill;
   int32_t* victim;    // deferred order: next victim per pair, -1 = none
+  // FULL mode: the sequences of the layer in launch order (longest first),
+  // [batch]; the decode launch maps its workgroups through it.
+  int32_t* order;
 };
 
 // Split-K workspace of one layer launch: per (pair, split) the partial
@@ -112,6 +115,12 @@ hipError_t launch_seq_reset(const Geometry& g, int32_t num_layers, int32_t* fill
                             const int32_t* seqs_host, int32_t count, hipStream_t stream);
 
 constexpr int kFillSeqPerLaunch = 256;
+
+// Writes the launch order of `count` sequences, order[first + i] = seq[i]
+// (host array), into one layer's order array.
+constexpr int kOrderPerLaunch = 512;
+hipError_t launch_set_order(int32_t* order, const int32_t* seq_host, int32_t first, int32_t count,
+                            hipStream_t stream);
 
 // Static scratch of lf_decode_step_noalloc (lf_scratch.hip): one device array
 // per GPU. The first kScratchCounterBytes hold arrival counters only (zero

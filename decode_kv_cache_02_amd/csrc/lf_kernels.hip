@@ -89,6 +89,21 @@ __global__ __launch_bounds__(64) void seq_reset_kernel(ResetParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Launch order of a layer's sequences (FULL mode): the values travel in the
+// kernel arguments, so the write is stream-ordered and capturable.
+// ---------------------------------------------------------------------------
+struct OrderParams {
+  int32_t* order;
+  int32_t first;
+  int32_t count;
+  int32_t seq[kOrderPerLaunch];
+};
+
+__global__ __launch_bounds__(256) void set_order_kernel(OrderParams P) {
+  for (int i = threadIdx.x; i < P.count; i += blockDim.x) P.order[P.first + i] = P.seq[i];
+}
+
 template <typename T, int D>
 hipError_t launch_fill_t(const Geometry& geo, const LayerPtrs& L, const void* k, const void* v,
                          const int32_t* seq_host, const int32_t* n_host, int32_t count,
@@ -200,6 +215,18 @@ hipError_t launch_seq_reset(const Geometry& g, int32_t num_layers, int32_t* fill
   P.count = count;
   for (int i = 0; i < kFillSeqPerLaunch; ++i) P.seqs[i] = i < count ? seqs_host[i] : -1;
   hipLaunchKernelGGL(seq_reset_kernel, dim3(count, num_layers), dim3(64), 0, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_order(int32_t* order, const int32_t* seq_host, int32_t first, int32_t count,
+                            hipStream_t stream) {
+  if (count <= 0 || count > kOrderPerLaunch || first < 0) return hipErrorInvalidValue;
+  OrderParams P;
+  P.order = order;
+  P.first = first;
+  P.count = count;
+  for (int i = 0; i < kOrderPerLaunch; ++i) P.seq[i] = i < count ? seq_host[i] : 0;
+  hipLaunchKernelGGL(set_order_kernel, dim3(1), dim3(256), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <numeric>
 #include <vector>
 
 #include "../../include/longflow.h"
@@ -38,6 +39,7 @@ struct lf_cache {
   float* vnorm;
   int32_t* fill;
   int32_t* victim;
+  int32_t* order;        // [num_layers][batch]: FULL mode launch order of the sequences
   int64_t layer_pairs;   // batch * num_kv_heads
   size_t elem_bytes;
   std::vector<int32_t> fill_host;  // [num_layers][batch]
@@ -56,8 +58,8 @@ constexpr size_t kAlign = 256;
 constexpr int kSlotAlign = 64;
 
 struct Layout {
-  size_t k_off, v_off, vn_off, fill_off, victim_off, part_off, logit_off, arrive_off, score_off,
-      seq_arrive_off, new_norm_off, total;
+  size_t k_off, v_off, vn_off, fill_off, victim_off, order_off, part_off, logit_off, arrive_off,
+      score_off, seq_arrive_off, new_norm_off, total;
   int32_t slots_pad;
   int64_t pair_elems;
 };
@@ -145,6 +147,11 @@ lf_status layout(const lf_config* c, int32_t max_splits, Layout* L) {
   if (!add_ok(L->fill_off, align_up(fl), &t)) return LF_ERR_UNSUPPORTED;
   L->victim_off = t;
   if (!add_ok(L->victim_off, align_up(fl), &t)) return LF_ERR_UNSUPPORTED;
+  // FULL mode: each layer's launch order of its sequences.
+  L->order_off = t;
+  if (!add_ok(L->order_off, align_up(c->mode == LF_MODE_FULL
+                                          ? static_cast<size_t>(c->num_layers) * c->batch * 4 : 0), &t))
+    return LF_ERR_UNSUPPORTED;
   // Split-K workspace for one layer (the layers run one after another).
   size_t layer_pairs = static_cast<size_t>(c->batch) * c->num_kv_heads;
   size_t ws = max_splits > 1 ? layer_pairs * max_splits : 0;
@@ -189,7 +196,29 @@ lf::LayerPtrs layer_ptrs(const lf_cache* c, int32_t layer) {
   p.vnorm = c->vnorm + pair0 * c->geo.slots_pad;
   p.fill = c->fill + pair0;
   p.victim = c->victim + pair0;
+  p.order = c->order ? c->order + static_cast<int64_t>(layer) * c->cfg.batch : nullptr;
   return p;
+}
+
+// FULL mode: one layer's sequences in launch order, longest first (ties by
+// index), written to the device. Workgroups are dispatched in index order, so
+// the longest pairs start first and the short ones fill the last round.
+// Decode steps add one token to every sequence, which keeps the order; only
+// prefill and recycling change it.
+hipError_t write_order(const lf_cache* c, int32_t layer, hipStream_t st) {
+  if (!c->order) return hipSuccess;
+  const int32_t batch = c->cfg.batch;
+  const int32_t* fh = c->fill_host.data() + static_cast<size_t>(layer) * batch;
+  std::vector<int32_t> seq(batch);
+  std::iota(seq.begin(), seq.end(), 0);
+  std::stable_sort(seq.begin(), seq.end(), [fh](int32_t a, int32_t b) { return fh[a] > fh[b]; });
+  int32_t* dst = c->order + static_cast<int64_t>(layer) * batch;
+  for (int32_t first = 0; first < batch; first += lf::kOrderPerLaunch) {
+    const int32_t n = std::min<int32_t>(lf::kOrderPerLaunch, batch - first);
+    const hipError_t e = lf::launch_set_order(dst, seq.data() + first, first, n, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Makes the cache's device current for the length of one call and gives the
@@ -418,6 +447,12 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
     return e == hipErrorOutOfMemory ? LF_ERR_OOM : LF_ERR_HIP;
   }
   e = hipMemsetAsync(base, 0, L.total, nullptr);
+  if (e == hipSuccess && cfg->mode == LF_MODE_FULL) {
+    // every sequence starts empty: the launch order is the identity
+    c->order = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.order_off);
+    for (int32_t l = 0; l < cfg->num_layers && e == hipSuccess; ++l)
+      e = write_order(c, l, nullptr);
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
   // The device's static scratch (lf_decode_step_noalloc) is set up here,
   // outside any stream capture, once per device.
@@ -434,6 +469,9 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->vnorm = reinterpret_cast<float*>(static_cast<char*>(base) + L.vn_off);
   c->fill = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.fill_off);
   c->victim = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.victim_off);
+  c->order = cfg->mode == LF_MODE_FULL
+                 ? reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.order_off)
+                 : nullptr;
   c->work.part = reinterpret_cast<float*>(static_cast<char*>(base) + L.part_off);
   c->work.logit = reinterpret_cast<float*>(static_cast<char*>(base) + L.logit_off);
   c->work.arrive = reinterpret_cast<int32_t*>(static_cast<char*>(base) + L.arrive_off);
@@ -560,6 +598,7 @@ lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void*
   }
   for (int32_t b = 0; b < c->cfg.batch; ++b)
     if (n_per_seq[b] >= 0) fh[b] = n_per_seq[b];
+  if (write_order(c, layer, st) != hipSuccess) return LF_ERR_HIP;
   return LF_OK;
 }
 
@@ -580,6 +619,8 @@ lf_status lf_seq_reset(lf_cache* c, const int32_t* seqs, int32_t count, void* st
   for (int32_t l = 0; l < c->cfg.num_layers; ++l)
     for (int32_t i = 0; i < count; ++i)
       c->fill_host[static_cast<size_t>(l) * c->cfg.batch + seqs[i]] = 0;
+  for (int32_t l = 0; l < c->cfg.num_layers; ++l)
+    if (write_order(c, l, st) != hipSuccess) return LF_ERR_HIP;
   return LF_OK;
 }
 

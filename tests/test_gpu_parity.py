@@ -147,6 +147,23 @@ def test_ragged_fill_levels():
     assert rep.appends > 0 and rep.evictions > 0
 
 
+@pytest.mark.parametrize("batch", [40, 12])
+def test_full_mode_ragged_fill_levels_longest_first(batch):
+    """FULL mode dispatches a layer's sequences longest first. Ragged fills,
+    every pair checked (one workgroup per pair at 320 pairs, split-K at 96);
+    at step 4 three sequences are recycled with short prompts, which reorders
+    the launch."""
+    wl = WORKLOADS["llama8b_layer"].with_(batch=batch, budget=300)
+    rng = np.random.default_rng(batch)
+    n = rng.integers(0, 290, size=batch).astype(np.int32)
+    n[:3] = (0, 289, 1)
+    _say(f"bf16 FULL mode, batch {batch}, ragged fills {n.tolist()}, capacity 320, 8 steps, "
+         f"recycle 3 sequences at step 4")
+    rep = run_lockstep(wl, 8, prefill_n=n, mode="full", capacity=320, check_cache_every=2,
+                       recycle={4: ([1, batch - 1, batch // 2], 5)})
+    assert rep.appends == 8 * batch * wl.num_kv_heads and rep.recycled == 3
+
+
 @pytest.mark.parametrize("budget,loop", [(512, "auto"), (4096, "auto"), (512, "phased"),
                                          (4096, "interleaved")])
 def test_qwen3_8b_duplicate_ties(budget, loop):
