@@ -198,10 +198,20 @@ def cpu_baseline(wl, seconds: float):
              for w in range(workers)]
     for p in procs:
         p.start()
-    start.wait()
-    got = [results.get() for _ in procs]
-    for p in procs:
-        p.join()
+    # Every wait is bounded: a worker that dies (and so never reaches the
+    # barrier or never reports) ends the baseline with an error, not a hang.
+    limit = 4 * seconds + 300
+    try:
+        start.wait(timeout=limit)
+        got = [results.get(timeout=limit) for _ in procs]
+    except Exception as exc:
+        for p in procs:
+            if p.is_alive():
+                p.terminate()
+        raise RuntimeError(f"CPU baseline worker failed: {exc!r}") from exc
+    finally:
+        for p in procs:
+            p.join(timeout=60)
     pair_steps_per_s = sum(n * st / el for n, st, el in got)
     tokens_per_s = pair_steps_per_s / wl.num_kv_heads
     pair_steps = sum(n * st for n, st, _ in got)

@@ -168,6 +168,9 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out);
  * No victim is pending afterwards. Slots n_b..budget-1 keep what they held:
  * no step reads a slot before it has been written. Only the sequences being
  * filled are touched (and launched). k and v may be NULL when n_max = 0.
+ * In FULL mode the call also sets the layer's launch order (longest
+ * sequences first), which lf_seq_reset updates too; results do not depend
+ * on it.
  * Errors: LF_ERR_CAPACITY if some n_b > budget; LF_ERR_INVALID_ARG on null
  * pointers, a bad layer, n_b > n_max or n_b < -1. */
 lf_status lf_prefill_fill(lf_cache* c, int32_t layer, const void* k, const void* v,
