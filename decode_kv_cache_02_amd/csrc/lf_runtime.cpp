@@ -259,7 +259,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 //     the phased loop (K, then V).
 //   - A launch of at most one workgroup per CU uses 8 waves per workgroup,
 //     otherwise 4 (two workgroups per CU). This needs the 8-wave
-//     workgroup's LDS to fit.
+//     workgroup's LDS to fit, and at least 8 tiles per workgroup.
 // A forced split count (lf_cache_set_splits) wins within max_splits.
 struct LaunchShape {
   int32_t splits;
@@ -285,7 +285,9 @@ LaunchShape plan_launch(const lf_cache* c, int32_t n_max) {
   if (c->forced_loop > 0) ilv = c->forced_loop == 2;
   const size_t dyn = s > 1 ? lf::decode_split_lds_bytes(c->geo, s, ilv) : lf::decode_lds_bytes(c->geo, ilv);
   const bool fits8 = dyn + lf::decode_static_lds_bytes(c->geo, 8) <= c->lds_limit;
-  int32_t waves = pairs * s <= c->cus ? 8 : 4;
+  // 8 waves only when every wave has a 16-slot tile to stream (a 64-slot
+  // pair on 8 waves leaves half of them idle: 5.2 against 4.8 us per step).
+  int32_t waves = pairs * s <= c->cus && (per_wg + 15) / 16 >= 8 ? 8 : 4;
   if (c->forced_waves > 0) waves = c->forced_waves;
   if (waves == 8 && !fits8) waves = 4;
   return {s, waves, ilv};

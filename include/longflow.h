@@ -271,20 +271,23 @@ lf_status lf_cache_snapshot(const lf_cache* c, int32_t layer, void* k, void* v, 
 lf_status lf_cache_set_splits(lf_cache* c, int32_t splits);
 lf_status lf_cache_max_splits(const lf_cache* c, int32_t* max_splits);
 
-/* Launch-shape tuning (as above): workgroup size of the decode launches. By default a launch that holds at
- * most one workgroup per compute unit uses 8 waves (512 threads) per
- * workgroup, and any larger launch 4 waves, two workgroups per compute unit.
+/* Launch-shape tuning (as above): workgroup size of the decode launches. By
+ * default a launch that holds at most one workgroup per compute unit uses 8
+ * waves (512 threads) per workgroup when each workgroup streams at least 8
+ * tiles of 16 slots, and any other launch 4 waves (two workgroups per
+ * compute unit for large launches).
  * 4 or 8 forces that size (8 falls back to 4 where its LDS does not fit); 0
  * restores the automatic choice. Results do not depend on it except for
  * float32 rounding of the output. Errors: LF_ERR_INVALID_ARG for other
  * values. */
 lf_status lf_cache_set_waves(lf_cache* c, int32_t waves);
 
-/* Launch-shape tuning (as above): loop of the decode launches. By default a launch whose workgroups each
- * stream at most 1024 slots uses the interleaved loop (each wave streams the
- * K and the V of the same 16 slots together, with its own online softmax),
- * and longer streams the phased loop (all K, then all V). 1 forces the
- * phased loop, 2 the interleaved one, 0 restores the automatic choice.
+/* Launch-shape tuning (as above): loop of the decode launches. By default a
+ * launch whose workgroups each stream at most 1024 slots uses the
+ * interleaved loop (each wave streams the K and the V of the same 16 slots
+ * together, with its own online softmax), and longer streams the phased loop
+ * (all K, then all V). 1 forces the phased loop, 2 the interleaved one, 0
+ * restores the automatic choice.
  * Results do not depend on it except for float32 rounding of the output and
  * of the scores. Errors: LF_ERR_INVALID_ARG for other values. */
 lf_status lf_cache_set_loop(lf_cache* c, int32_t loop);

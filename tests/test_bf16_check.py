@@ -103,8 +103,8 @@ def test_dropped_new_token_fails(steps):
 def _oracle_record(wl, pairs, steps, prefill):
     """A Record as the GPU would write it, made by the oracle itself."""
     G, d = wl.group, wl.head_dim
-    out = np.zeros((steps, len(pairs), G, d), dtype=np.float32)
-    ev = np.zeros((steps, len(pairs)), dtype=np.int32)
+    out = np.zeros((1, steps, len(pairs), G, d), dtype=np.float32)
+    ev = np.zeros((1, steps, len(pairs)), dtype=np.int32)
     snaps = {}
     for i, (b, h) in enumerate(pairs):
         ps = PairTokenStream(wl, b, h)
@@ -113,14 +113,15 @@ def _oracle_record(wl, pairs, steps, prefill):
         q, kn, vn = ps.steps(steps)
         for t in range(steps):
             r = c.step(q[t], kn[t], vn[t])
-            out[t, i] = round_to_bf16(r.out.astype(np.float32))
-            ev[t, i] = r.evicted
+            out[0, t, i] = round_to_bf16(r.out.astype(np.float32))
+            ev[0, t, i] = r.evicted
             if (t + 1) % 8 == 0:
                 snaps.setdefault(t + 1, []).append((c.K.copy(), c.V.copy(), c.vnorm.copy(), c.n))
-    snapshots = [(t, np.stack([x[0] for x in v]), np.stack([x[1] for x in v]),
+    snapshots = [(t, 0, np.stack([x[0] for x in v]), np.stack([x[1] for x in v]),
                   np.stack([x[2] for x in v]), np.array([x[3] for x in v]))
                  for t, v in sorted(snaps.items())]
-    return trajectory.Record(wl, pairs, steps, prefill, 0, out, ev, snapshots, capacity=wl.budget)
+    return trajectory.Record(wl, pairs, steps, np.full(wl.batch, prefill), 0, out, ev, snapshots,
+                             capacity=wl.budget)
 
 
 def test_trajectory_checker_passes_the_oracle_and_fails_planted_mistakes():
@@ -135,7 +136,7 @@ def test_trajectory_checker_passes_the_oracle_and_fails_planted_mistakes():
 
     wrong = trajectory.Record(**{**rec.__dict__, "evicted": rec.evicted.copy()})
     t = 30
-    wrong.evicted[t, 1] = (wrong.evicted[t, 1] + 1) % wl.budget
+    wrong.evicted[0, t, 1] = (wrong.evicted[0, t, 1] + 1) % wl.budget
     with pytest.raises(AssertionError, match="evicted|near-tie"):
         trajectory.check_trajectory(wrong, workers=1)
 
@@ -147,6 +148,6 @@ def test_trajectory_checker_passes_the_oracle_and_fails_planted_mistakes():
         q, kn, vn = ps.steps(40)
         for t in range(40):
             r = c.step(q[t], kn[t], vn[t])
-            trunc.out[t, i] = _truncate_bf16(r.out.astype(np.float32))
+            trunc.out[0, t, i] = _truncate_bf16(r.out.astype(np.float32))
     with pytest.raises(AssertionError, match="RNE"):
         trajectory.check_trajectory(trunc, workers=1)

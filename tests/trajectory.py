@@ -56,27 +56,36 @@ class Record:
     wl: Workload
     pairs: list
     steps: int
-    prefill: int
+    prefill: np.ndarray                   # [batch] prompt tokens per sequence
     seed_offset: int
-    out: np.ndarray                       # [steps][pairs][G][d] float32 (dtype-exact)
-    evicted: np.ndarray                   # [steps][pairs] int32
-    snapshots: list = field(default_factory=list)   # (steps done, K, V, vnorm, fill) per pair axis
+    out: np.ndarray                       # [checked layers][steps][pairs][G][d] float32 (dtype-exact)
+    evicted: np.ndarray                   # [checked layers][steps][pairs] int32
+    snapshots: list = field(default_factory=list)   # (steps done, layer row, K, V, vnorm, fill)
     launch: str = ""
     mode: str = "evict"                   # "full": the full-KV baseline (no eviction)
     capacity: int = 0                     # slots per pair (the budget when evicting)
     max_splits: int = 1                   # split-K workgroups the cache allows per pair
+    layers: tuple = (0,)                  # the checked layers of the stack
+    num_layers: int = 1
 
 
-def record_trajectory(wl: Workload, steps: int, pairs, prefill: int, check_every: int = 0,
+def record_trajectory(wl: Workload, steps: int, pairs, prefill, check_every: int = 0,
                       seed_offset: int = 0, splits: int = 0, waves: int = 0,
-                      loop: str = "auto", mode: str = "evict") -> Record:
+                      loop: str = "auto", mode: str = "evict", num_layers: int = 1,
+                      layers=(0,)) -> Record:
+    """Run `steps` model steps (one lf_decode_step per layer of a
+    `num_layers` stack) and record the sampled pairs of the checked `layers`.
+    `prefill` is the prompt length of every sequence, or one per sequence."""
     import torch
     from decode_kv_cache_02_amd.native import LongFlowCache
 
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     G, d, P = wl.group, wl.head_dim, len(pairs)
-    capacity = wl.budget if mode == "evict" else prefill + steps
-    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, d, capacity,
+    layers = tuple(layers)
+    n_pf = np.broadcast_to(np.asarray(prefill, dtype=np.int64), (wl.batch,)).astype(np.int32)
+    n_max = int(n_pf.max(initial=0))
+    capacity = wl.budget if mode == "evict" else n_max + steps
+    cache = LongFlowCache(num_layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, d, capacity,
                           sink_size=wl.sink_size, dtype=wl.dtype, mode=mode)
     try:
         if splits:
@@ -90,59 +99,72 @@ def record_trajectory(wl: Workload, steps: int, pairs, prefill: int, check_every
         hq = torch.tensor([h * G + g for b, h in pairs for g in range(G)], device=cuda)
         bk = torch.tensor([b for b, _ in pairs], device=cuda)
         hk = torch.tensor([h for _, h in pairs], device=cuda)
-        streams = [PairTokenStream(wl, b, h, seed_offset=seed_offset) for b, h in pairs]
+        streams = {l: [PairTokenStream(wl, b, h, layer=l, seed_offset=seed_offset) for b, h in pairs]
+                   for l in layers}
         seed = 1000 * wl.cfg_id + seed_offset
-        if prefill > 0:
-            kp, vp = device_prefill(wl, prefill, seed=seed)
-            for s, (b, h) in zip(streams, pairs):
-                K, V = s.prefill(prefill)
-                kp[b, :, h] = torch.from_numpy(K).to(cuda, dt)
-                vp[b, :, h] = torch.from_numpy(V).to(cuda, dt)
-            cache.prefill(0, kp, vp, np.full(wl.batch, prefill, dtype=np.int32))
-            del kp, vp
-        else:
-            cache.prefill(0, None, None, np.zeros(wl.batch, dtype=np.int32))
+        for l in range(num_layers):
+            if n_max > 0:
+                kp, vp = device_prefill(wl, n_max, seed=seed + 7 * l)
+                for s, (b, h) in zip(streams.get(l, []), pairs):
+                    K, V = s.prefill(int(n_pf[b]))
+                    kp[b, :n_pf[b], h] = torch.from_numpy(K).to(cuda, dt)
+                    vp[b, :n_pf[b], h] = torch.from_numpy(V).to(cuda, dt)
+                cache.prefill(l, kp, vp, n_pf)
+                del kp, vp
+            else:
+                cache.prefill(l, None, None, n_pf)
         ring_q, ring_k, ring_v = device_steps(wl, RING, seed=seed + 1)
         q_buf, k_buf, v_buf = torch.empty_like(ring_q[0]), torch.empty_like(ring_k[0]), \
             torch.empty_like(ring_v[0])
         out = torch.empty_like(q_buf)
         ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device=cuda)
-        rec_out = torch.empty((steps, P * G, d), dtype=dt, device=cuda)
-        rec_ev = torch.empty((steps, P), dtype=torch.int32, device=cuda)
+        rec_out = torch.empty((len(layers), steps, P * G, d), dtype=dt, device=cuda)
+        rec_ev = torch.empty((len(layers), steps, P), dtype=torch.int32, device=cuda)
         snaps = []
 
         def snapshot(done):
-            k, v, vn, fill = cache.snapshot(0)
-            snaps.append((done, k[bk, hk].float().cpu().numpy(), v[bk, hk].float().cpu().numpy(),
-                          vn[bk, hk].cpu().numpy(), fill[bk, hk].cpu().numpy()))
+            for row, l in enumerate(layers):
+                k, v, vn, fill = cache.snapshot(l)
+                snaps.append((done, row, k[bk, hk].float().cpu().numpy(),
+                              v[bk, hk].float().cpu().numpy(), vn[bk, hk].cpu().numpy(),
+                              fill[bk, hk].cpu().numpy()))
 
         for t0 in range(0, steps, BLOCK):
             cnt = min(BLOCK, steps - t0)
-            host = [s.steps(cnt) for s in streams]
-            hq_blk = torch.from_numpy(np.stack([x[0] for x in host], axis=1).reshape(cnt, P * G, d))
-            hk_blk = torch.from_numpy(np.stack([x[1] for x in host], axis=1))
-            hv_blk = torch.from_numpy(np.stack([x[2] for x in host], axis=1))
-            hq_blk, hk_blk, hv_blk = (x.to(cuda, dt) for x in (hq_blk, hk_blk, hv_blk))
+            blk = {}
+            for l in layers:
+                host = [s.steps(cnt) for s in streams[l]]
+                blk[l] = tuple(torch.from_numpy(x).to(cuda, dt) for x in (
+                    np.stack([x[0] for x in host], axis=1).reshape(cnt, P * G, d),
+                    np.stack([x[1] for x in host], axis=1),
+                    np.stack([x[2] for x in host], axis=1)))
             for j in range(cnt):
                 t = t0 + j
-                q_buf.copy_(ring_q[t % RING])
-                k_buf.copy_(ring_k[t % RING])
-                v_buf.copy_(ring_v[t % RING])
-                q_buf[bq, hq] = hq_blk[j]
-                k_buf[bk, hk] = hk_blk[j]
-                v_buf[bk, hk] = hv_blk[j]
-                cache.decode_step(0, q_buf, k_buf, v_buf, out, ev)
-                rec_out[t] = out[bq, hq]
-                rec_ev[t] = ev[bk, hk]
+                for l in range(num_layers):
+                    r = (t + 5 * l) % RING
+                    if l not in blk:     # load only: device-drawn inputs
+                        cache.decode_step(l, ring_q[r], ring_k[r], ring_v[r], out, ev)
+                        continue
+                    row = layers.index(l)
+                    q_buf.copy_(ring_q[r])
+                    k_buf.copy_(ring_k[r])
+                    v_buf.copy_(ring_v[r])
+                    q_buf[bq, hq] = blk[l][0][j]
+                    k_buf[bk, hk] = blk[l][1][j]
+                    v_buf[bk, hk] = blk[l][2][j]
+                    cache.decode_step(l, q_buf, k_buf, v_buf, out, ev)
+                    rec_out[row, t] = out[bq, hq]
+                    rec_ev[row, t] = ev[bk, hk]
                 if check_every and (t + 1) % check_every == 0 and t + 1 < steps:
                     snapshot(t + 1)
         snapshot(steps)
         torch.cuda.synchronize()
-        return Record(wl, list(pairs), steps, prefill, seed_offset,
-                      rec_out.float().cpu().numpy().reshape(steps, P, G, d),
+        return Record(wl, list(pairs), steps, n_pf, seed_offset,
+                      rec_out.float().cpu().numpy().reshape(len(layers), steps, P, G, d),
                       rec_ev.cpu().numpy(), snaps,
                       launch=f"splits={splits or 'auto'} waves={waves or 'auto'} loop={loop}",
-                      mode=mode, capacity=capacity, max_splits=cache.max_splits)
+                      mode=mode, capacity=capacity, max_splits=cache.max_splits,
+                      layers=layers, num_layers=num_layers)
     finally:
         cache.close()
 
@@ -176,22 +198,22 @@ def _fail(rep: PairReport, msg: str) -> bool:
     return len(rep.failures) >= 5     # stop after a few
 
 
-def _check_pair(index: int) -> PairReport:
+def _check_pair(job: int) -> PairReport:
     from threadpoolctl import threadpool_limits
     from oracle.longflow_oracle import PairCache
 
     rec = _RECORD
     wl = rec.wl
+    row, index = divmod(job, len(rec.pairs))
+    layer = rec.layers[row]
     b, h = rec.pairs[index]
-    rep = PairReport((b, h))
+    rep = PairReport((layer, b, h) if rec.num_layers > 1 else (b, h))
     with threadpool_limits(1):
-        ps = PairTokenStream(wl, b, h, seed_offset=rec.seed_offset)
+        ps = PairTokenStream(wl, b, h, layer=layer, seed_offset=rec.seed_offset)
         oc = PairCache(rec.capacity or wl.budget, wl.head_dim, sink_size=wl.sink_size,
                        evict=rec.mode == "evict")
-        if rec.prefill > 0:
-            K, V = ps.prefill(rec.prefill)
-            oc.prefill(K, V)
-        snaps = {s[0]: s for s in rec.snapshots}
+        oc.prefill(*ps.prefill(int(rec.prefill[b])))
+        snaps = {s[0]: s for s in rec.snapshots if s[1] == row}
         tol = TOL[wl.dtype]
         for t0 in range(0, rec.steps, BLOCK):
             cnt = min(BLOCK, rec.steps - t0)
@@ -199,7 +221,7 @@ def _check_pair(index: int) -> PairReport:
             for j in range(cnt):
                 t = t0 + j
                 res = oc.attend(q[j], kn[j], vn[j])
-                gout = rec.out[t, index]
+                gout = rec.out[row, t, index]
                 err = row_rel_err(gout, res.out)
                 rep.max_rel_err = max(rep.max_rel_err, err)
                 if err > tol and _fail(rep, f"step {t}: out rel err {err:.3g} > {tol}"):
@@ -210,7 +232,7 @@ def _check_pair(index: int) -> PairReport:
                     rep.bf16_elements += n
                     if bad and _fail(rep, f"step {t}: {bad} bf16 outputs differ from RNE(oracle)"):
                         return rep
-                e = int(rec.evicted[t, index])
+                e = int(rec.evicted[row, t, index])
                 chosen = None
                 if res.evicted < 0:
                     rep.appends += 1
@@ -237,7 +259,7 @@ def _check_pair(index: int) -> PairReport:
                 oc.commit(res, kn[j], vn[j], chosen)
                 rep.steps += 1
                 if t + 1 in snaps:
-                    _, Ks, Vs, VNs, Fs = snaps[t + 1]
+                    _, _, Ks, Vs, VNs, Fs = snaps[t + 1]
                     n = oc.n
                     rep.snapshots += 1
                     if int(Fs[index]) != n:
@@ -256,17 +278,18 @@ def check_trajectory(rec: Record, workers: int = 0):
     """Replay every sampled pair in the oracle; returns the per-pair reports.
     Fails (AssertionError) with the first failures of each failing pair."""
     global _RECORD
+    jobs = len(rec.layers) * len(rec.pairs)
     if workers <= 0:
-        workers = min(len(rec.pairs), len(os.sched_getaffinity(0)), 8)
+        workers = min(jobs, len(os.sched_getaffinity(0)), 8)
     _RECORD = rec
     try:
         if workers == 1:
-            reports = [_check_pair(i) for i in range(len(rec.pairs))]
+            reports = [_check_pair(i) for i in range(jobs)]
         else:
             # fork: the workers inherit the record and run NumPy only (they
             # never touch the GPU), and no program is exec'd.
             with multiprocessing.get_context("fork").Pool(workers) as pool:
-                reports = pool.map(_check_pair, range(len(rec.pairs)), chunksize=1)
+                reports = pool.map(_check_pair, range(jobs), chunksize=1)
     finally:
         _RECORD = None
     bad = [r for r in reports if r.failures]
@@ -281,6 +304,7 @@ def summary(rec: Record, reports) -> str:
     tot = lambda k: sum(getattr(r, k) for r in reports)
     s = (f"{rec.wl.name} {rec.mode} capacity={rec.capacity} batch={rec.wl.batch} "
          f"{rec.wl.num_q_heads}/{rec.wl.num_kv_heads} heads ({rec.launch}, max splits {rec.max_splits}): "
+         f"layers {list(rec.layers)} of {rec.num_layers}, "
          f"{len(reports)} pairs x {rec.steps} steps, evictions {tot('evictions')}, "
          f"appends {tot('appends')}, near-ties {tot('near_ties')}, exact ties "
          f"{tot('exact_ties')} (lowest index {tot('tie_lowest_index')}), max rel err "
