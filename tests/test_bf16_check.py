@@ -151,3 +151,54 @@ def test_trajectory_checker_passes_the_oracle_and_fails_planted_mistakes():
             trunc.out[0, t, i] = _truncate_bf16(r.out.astype(np.float32))
     with pytest.raises(AssertionError, match="RNE"):
         trajectory.check_trajectory(trunc, workers=1)
+
+
+def _oracle_variant_record(wl, seqs, steps, prefill, order, scope, norm):
+    """A Record of every KV head of the given sequences under a cache variant,
+    made by the oracle's LayerCache (one per sequence)."""
+    from oracle.longflow_oracle import LayerCache
+    G, d, H = wl.group, wl.head_dim, wl.num_kv_heads
+    pairs = [(b, h) for b in seqs for h in range(H)]
+    out = np.zeros((1, steps, len(pairs), G, d), dtype=np.float32)
+    ev = np.zeros((1, steps, len(pairs)), dtype=np.int32)
+    for s, b in enumerate(seqs):
+        streams = [PairTokenStream(wl, b, h) for h in range(H)]
+        lc = LayerCache(1, H * G, H, d, wl.budget, norm=norm, order=order, scope=scope)
+        pf = [x.prefill(prefill) for x in streams]
+        lc.prefill(np.stack([x[0] for x in pf], axis=1)[None],
+                   np.stack([x[1] for x in pf], axis=1)[None], [prefill])
+        blk = [x.steps(steps) for x in streams]
+        for t in range(steps):
+            q = np.concatenate([x[0][t] for x in blk])[None]
+            kn = np.stack([x[1][t] for x in blk])[None]
+            vn = np.stack([x[2][t] for x in blk])[None]
+            res = lc.step(q, kn, vn)
+            for h in range(H):
+                out[0, t, s * H + h] = round_to_bf16(res[(0, h)].out.astype(np.float32))
+                ev[0, t, s * H + h] = res[(0, h)].evicted
+    return trajectory.Record(wl, pairs, steps, np.full(wl.batch, prefill), 0, out, ev, [],
+                             capacity=wl.budget, order=order, scope=scope, norm=norm)
+
+
+@pytest.mark.parametrize("order,scope,norm", [("deferred", "kv_head", "l1"),
+                                              ("same_step", "sequence", "l1"),
+                                              ("deferred", "sequence", "l1"),
+                                              ("same_step", "kv_head", "l2")])
+def test_variant_trajectory_checker(order, scope, norm):
+    """The checker replays the cache variants (deferred order: the slot
+    replaced at a step is the one chosen at the step before; one victim per
+    sequence: every KV head of a sequence replaces the same slot; the l2
+    score) and fails a planted wrong slot."""
+    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=96, batch=4)
+    rec = _oracle_variant_record(wl, [1, 3], 40, 80, order, scope, norm)
+    reports = trajectory.check_trajectory(rec, workers=2)
+    assert len(reports) == (2 if scope == "sequence" else 16)
+    heads = wl.num_kv_heads if scope == "sequence" else 1    # counts are per pair-step
+    assert all(r.appends == 16 * heads and r.steps == 40 for r in reports)
+    assert all(r.tie_lowest_index == r.exact_ties for r in reports)
+
+    wrong = trajectory.Record(**{**rec.__dict__, "evicted": rec.evicted.copy()})
+    i = 5 if scope == "kv_head" else slice(0, 8)
+    wrong.evicted[0, 30, i] = (rec.evicted[0, 30, 5] + 1) % wl.budget
+    with pytest.raises(AssertionError, match="evicted|near-tie|replaced|victim"):
+        trajectory.check_trajectory(wrong, workers=1)

@@ -22,6 +22,10 @@ slot, and the pairs' cache regions every 1024 steps.
   * The full-KV baseline growing past 16k tokens (14,976 -> 16,896, the
     Llama-8B layer at batch 8: split-K, each split streaming its ~4k slots
     in 2048-slot LDS chunks).
+  * The variants of the cache over whole trajectories: the deferred order
+    and the l2 score on the Llama-8B layer (8 pairs), and one victim per
+    sequence on the Qwen3-0.6B layer (two sequences, every KV head), in
+    either order.
 Each test prints its near-tie and exact-tie counts.
 """
 import pytest
@@ -32,15 +36,18 @@ import trajectory
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, steps, prefill, check_every=1024, pairs=8, seed=0, mode="evict"):
+def _run(wl, steps, prefill, check_every=1024, pairs=8, seed=0, mode="evict",
+         sampled=None, **variant):
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    sampled = trajectory.sample_pairs(wl, pairs, seed=seed)
-    print(f"\n[case] {wl.name} {mode} B={wl.budget} batch={wl.batch} {wl.num_q_heads}/"
-          f"{wl.num_kv_heads}: prompt {prefill}, {steps} steps, pairs {sampled}", flush=True)
+    if sampled is None:
+        sampled = trajectory.sample_pairs(wl, pairs, seed=seed)
+    print(f"\n[case] {wl.name} {mode} {variant or ''} B={wl.budget} batch={wl.batch} "
+          f"{wl.num_q_heads}/{wl.num_kv_heads}: prompt {prefill}, {steps} steps, "
+          f"pairs {sampled}", flush=True)
     rec = trajectory.record_trajectory(wl, steps, sampled, prefill, check_every=check_every,
-                                       mode=mode)
+                                       mode=mode, **variant)
     print(f"[case] recorded; checking {len(sampled)} pairs in the oracle", flush=True)
     reports = trajectory.check_trajectory(rec)
     print(trajectory.summary(rec, reports), flush=True)
@@ -133,3 +140,40 @@ def test_llama8b_stack32_ragged_window():
         b = r.pair[1]
         assert r.appends == max(0, min(wl.steps, wl.budget - int(fills[b])))
         assert r.appends + r.evictions == wl.steps
+
+
+def test_llama8b_layer_deferred_order_whole_trajectory():
+    """The Guide engine's order: the new token takes the slot chosen at the
+    step before (the last slot when none was chosen), then the next victim is
+    picked (LongFlow Guide, §End-to-End Implementation, the cache's step)."""
+    wl = WORKLOADS["llama8b_layer"]
+    reports = _run(wl, wl.steps, wl.prefill, seed=11, order="deferred")
+    fill_steps = wl.budget - wl.prefill
+    for r in reports:
+        assert r.appends == fill_steps and r.evictions == wl.steps - fill_steps + 1
+        assert r.tie_lowest_index == r.exact_ties
+
+
+def test_llama8b_layer_l2_score_whole_trajectory():
+    """The score with the l2 norm of the value rows (LongFlow Guide,
+    §Mathematical Derivation of the LongFlow Score: the score may take the l1
+    or the l2 norm of the contribution vector)."""
+    wl = WORKLOADS["llama8b_layer"]
+    _check_fill_then_evict(wl, _run(wl, wl.steps, wl.prefill, seed=12, norm="l2"))
+
+
+@pytest.mark.parametrize("order", ["same_step", "deferred"])
+def test_qwen3_0p6b_layer_one_victim_per_sequence_whole_trajectory(order):
+    """One victim per sequence, the argmin of the scores summed over every
+    KV head (the sum over all heads in the LongFlow Guide, §End-to-End
+    Implementation), with the same-step and the deferred order: two sequences, all 8 KV heads of each, from a
+    512-token prompt through 512 filling steps and 3,584 evicting ones."""
+    wl = WORKLOADS["qwen3_0p6b_layer"]
+    sampled = [(b, h) for b in (5, 26) for h in range(wl.num_kv_heads)]
+    reports = _run(wl, wl.steps, 512, sampled=sampled, scope="sequence", order=order)
+    assert len(reports) == 2
+    H = wl.num_kv_heads
+    for r in reports:
+        assert r.appends == (wl.budget - 512) * H
+        assert r.evictions == (wl.steps - (wl.budget - 512) + (order == "deferred")) * H
+        assert r.tie_lowest_index == r.exact_ties

@@ -67,12 +67,16 @@ class Record:
     max_splits: int = 1                   # split-K workgroups the cache allows per pair
     layers: tuple = (0,)                  # the checked layers of the stack
     num_layers: int = 1
+    order: str = "same_step"              # variants of the cache (lf_config.order / scope / norm)
+    scope: str = "kv_head"
+    norm: str = "l1"
 
 
 def record_trajectory(wl: Workload, steps: int, pairs, prefill, check_every: int = 0,
                       seed_offset: int = 0, splits: int = 0, waves: int = 0,
                       loop: str = "auto", mode: str = "evict", num_layers: int = 1,
-                      layers=(0,)) -> Record:
+                      layers=(0,), order: str = "same_step", scope: str = "kv_head",
+                      norm: str = "l1") -> Record:
     """Run `steps` model steps (one lf_decode_step per layer of a
     `num_layers` stack) and record the sampled pairs of the checked `layers`.
     `prefill` is the prompt length of every sequence, or one per sequence."""
@@ -86,7 +90,8 @@ def record_trajectory(wl: Workload, steps: int, pairs, prefill, check_every: int
     n_max = int(n_pf.max(initial=0))
     capacity = wl.budget if mode == "evict" else n_max + steps
     cache = LongFlowCache(num_layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, d, capacity,
-                          sink_size=wl.sink_size, dtype=wl.dtype, mode=mode)
+                          sink_size=wl.sink_size, dtype=wl.dtype, mode=mode, order=order,
+                          scope=scope, norm=norm)
     try:
         if splits:
             cache.set_splits(splits)
@@ -164,7 +169,7 @@ def record_trajectory(wl: Workload, steps: int, pairs, prefill, check_every: int
                       rec_ev.cpu().numpy(), snaps,
                       launch=f"splits={splits or 'auto'} waves={waves or 'auto'} loop={loop}",
                       mode=mode, capacity=capacity, max_splits=cache.max_splits,
-                      layers=layers, num_layers=num_layers)
+                      layers=layers, num_layers=num_layers, order=order, scope=scope, norm=norm)
     finally:
         cache.close()
 
@@ -198,77 +203,151 @@ def _fail(rep: PairReport, msg: str) -> bool:
     return len(rep.failures) >= 5     # stop after a few
 
 
-def _check_pair(job: int) -> PairReport:
+def _units(rec: Record):
+    """The checked units: one pair, or (one victim per sequence) all the
+    sampled pairs of one sequence, which must be all of its KV heads."""
+    if rec.scope != "sequence":
+        return [[i] for i in range(len(rec.pairs))]
+    by_seq = {}
+    for i, (b, _) in enumerate(rec.pairs):
+        by_seq.setdefault(b, []).append(i)
+    for b, idx in by_seq.items():
+        assert sorted(rec.pairs[i][1] for i in idx) == list(range(rec.wl.num_kv_heads)), (
+            f"sequence {b}: one victim per sequence needs every KV head sampled")
+    return list(by_seq.values())
+
+
+def _check_unit(job: int) -> PairReport:
+    """Replay one unit (a pair, or a whole sequence under one victim per
+    sequence) of one checked layer in the oracle against the record."""
     from threadpoolctl import threadpool_limits
-    from oracle.longflow_oracle import PairCache
+    from oracle.longflow_oracle import LayerCache
 
     rec = _RECORD
     wl = rec.wl
-    row, index = divmod(job, len(rec.pairs))
+    units = _units(rec)
+    row, u = divmod(job, len(units))
+    idx = units[u]
     layer = rec.layers[row]
-    b, h = rec.pairs[index]
-    rep = PairReport((layer, b, h) if rec.num_layers > 1 else (b, h))
+    b = rec.pairs[idx[0]][0]
+    heads = [rec.pairs[i][1] for i in idx]
+    G, hu = wl.group, len(idx)
+    rep = PairReport((layer, b, tuple(heads)) if rec.num_layers > 1 else
+                     ((b, heads[0]) if hu == 1 else (b, tuple(heads))))
+    deferred = rec.order == "deferred" and rec.mode == "evict"
+    budget = rec.capacity or wl.budget
     with threadpool_limits(1):
-        ps = PairTokenStream(wl, b, h, layer=layer, seed_offset=rec.seed_offset)
-        oc = PairCache(rec.capacity or wl.budget, wl.head_dim, sink_size=wl.sink_size,
-                       evict=rec.mode == "evict")
-        oc.prefill(*ps.prefill(int(rec.prefill[b])))
+        streams = [PairTokenStream(wl, b, h, layer=layer, seed_offset=rec.seed_offset)
+                   for h in heads]
+        oc = LayerCache(1, hu * G, hu, wl.head_dim, budget, sink_size=wl.sink_size,
+                        evict=rec.mode == "evict", norm=rec.norm, order=rec.order,
+                        scope=rec.scope)
+        pf = [s.prefill(int(rec.prefill[b])) for s in streams]
+        n0 = int(rec.prefill[b])
+        oc.prefill(np.stack([x[0] for x in pf], axis=1)[None], np.stack([x[1] for x in pf], axis=1)[None],
+                   [n0])
         snaps = {s[0]: s for s in rec.snapshots if s[1] == row}
         tol = TOL[wl.dtype]
+        pending = {}          # deferred: head -> result whose chosen victim is observed next step
         for t0 in range(0, rec.steps, BLOCK):
             cnt = min(BLOCK, rec.steps - t0)
-            q, kn, vn = ps.steps(cnt)
+            blk = [s.steps(cnt) for s in streams]
             for j in range(cnt):
                 t = t0 + j
-                res = oc.attend(q[j], kn[j], vn[j])
-                gout = rec.out[row, t, index]
-                err = row_rel_err(gout, res.out)
-                rep.max_rel_err = max(rep.max_rel_err, err)
-                if err > tol and _fail(rep, f"step {t}: out rel err {err:.3g} > {tol}"):
-                    return rep
-                if wl.dtype == "bf16":
-                    exc, bad, n = bf16_rounding_check(gout, res.out)
-                    rep.bf16_mid_exceptions += exc
-                    rep.bf16_elements += n
-                    if bad and _fail(rep, f"step {t}: {bad} bf16 outputs differ from RNE(oracle)"):
+                q = np.concatenate([x[0][j] for x in blk])[None]          # [1][hu*G][d]
+                kn = np.stack([x[1][j] for x in blk])[None]               # [1][hu][d]
+                vn = np.stack([x[2][j] for x in blk])[None]
+                e_all = [int(rec.evicted[row, t, i]) for i in idx]
+                if rec.scope == "sequence" and len(set(e_all)) != 1:
+                    if _fail(rep, f"step {t}: heads disagree on the victim {e_all}"):
                         return rep
-                e = int(rec.evicted[row, t, index])
-                chosen = None
-                if res.evicted < 0:
-                    rep.appends += 1
-                    if e != -1 and _fail(rep, f"step {t}: expected an append, GPU evicted {e}"):
+                if deferred:
+                    # the slot replaced now is the victim chosen one step ago
+                    for hh, prev in list(pending.items()):
+                        c = oc.cache[(0, hh)]
+                        if c.n < c.budget:
+                            continue
+                        e = e_all[hh]
+                        expect = prev.next_victim if prev.next_victim >= 0 else budget - 1
+                        if prev.near_tie:
+                            legal = [x if x >= 0 else budget - 1 for x in prev.legal]
+                            if e not in legal and _fail(
+                                    rep, f"step {t}: victim {e} outside near-tie set {legal}"):
+                                return rep
+                            finite = np.sort(prev.scores[np.isfinite(prev.scores)])
+                            if finite.size >= 2 and finite[0] == finite[1]:
+                                rep.exact_ties += 1
+                                rep.tie_lowest_index += int(e == expect)
+                            if e != expect:
+                                c.victim = e
+                        elif e != expect and _fail(rep, f"step {t}: GPU victim {e}, oracle {expect}"):
+                            return rep
+                        del pending[hh]
+                res = oc.attend(q, kn, vn)
+                chosen = {}
+                for hh in range(hu):
+                    r = res[(0, hh)]
+                    gout = rec.out[row, t, idx[hh]]
+                    err = row_rel_err(gout, r.out)
+                    rep.max_rel_err = max(rep.max_rel_err, err)
+                    if err > tol and _fail(rep, f"step {t} head {heads[hh]}: rel err {err:.3g} > {tol}"):
                         return rep
-                else:
+                    if wl.dtype == "bf16":
+                        exc, bad, n = bf16_rounding_check(gout, r.out)
+                        rep.bf16_mid_exceptions += exc
+                        rep.bf16_elements += n
+                        if bad and _fail(rep, f"step {t} head {heads[hh]}: {bad} bf16 outputs "
+                                              f"differ from RNE(oracle)"):
+                            return rep
+                    e = e_all[hh]
+                    if deferred:
+                        if e != r.evicted and _fail(
+                                rep, f"step {t} head {heads[hh]}: GPU replaced {e}, oracle {r.evicted}"):
+                            return rep
+                        rep.appends += int(e < 0)
+                        if r.scores is not None:
+                            rep.evictions += 1
+                            rep.near_ties += int(r.near_tie)
+                            if rep.fill_to_evict_step < 0:
+                                rep.fill_to_evict_step = t
+                            pending[hh] = r
+                        continue
+                    if r.evicted < 0:
+                        rep.appends += 1
+                        if e != -1 and _fail(rep, f"step {t}: expected an append, GPU evicted {e}"):
+                            return rep
+                        continue
                     rep.evictions += 1
                     if rep.fill_to_evict_step < 0:
                         rep.fill_to_evict_step = t
-                    if res.near_tie:
+                    if r.near_tie:
                         rep.near_ties += 1
-                        finite = np.sort(res.scores[np.isfinite(res.scores)])
+                        finite = np.sort(r.scores[np.isfinite(r.scores)])
                         if finite.size >= 2 and finite[0] == finite[1]:
                             rep.exact_ties += 1
-                            rep.tie_lowest_index += int(e == res.evicted)
-                        if e not in res.legal:
-                            if _fail(rep, f"step {t}: GPU slot {e} outside near-tie set {res.legal}"):
+                            rep.tie_lowest_index += int(e == r.evicted)
+                        if e not in r.legal:
+                            if _fail(rep, f"step {t}: GPU slot {e} outside near-tie set {r.legal}"):
                                 return rep
                         else:
-                            chosen = e
-                    elif e != res.evicted:
-                        if _fail(rep, f"step {t}: GPU evicted {e}, oracle {res.evicted}"):
+                            chosen[(0, hh)] = e
+                    elif e != r.evicted:
+                        if _fail(rep, f"step {t}: GPU evicted {e}, oracle {r.evicted}"):
                             return rep
-                oc.commit(res, kn[j], vn[j], chosen)
+                oc.commit(res, kn, vn, chosen)
                 rep.steps += 1
                 if t + 1 in snaps:
                     _, _, Ks, Vs, VNs, Fs = snaps[t + 1]
-                    n = oc.n
                     rep.snapshots += 1
-                    if int(Fs[index]) != n:
-                        _fail(rep, f"after step {t + 1}: fill {int(Fs[index])} != {n}")
-                    elif not (np.array_equal(Ks[index, :n], oc.K[:n])
-                              and np.array_equal(Vs[index, :n], oc.V[:n])):
-                        _fail(rep, f"after step {t + 1}: cached K/V rows differ")
-                    elif not np.allclose(VNs[index, :n], oc.vnorm[:n], rtol=2e-6, atol=0):
-                        _fail(rep, f"after step {t + 1}: sidecar differs")
+                    for hh in range(hu):
+                        c, i = oc.cache[(0, hh)], idx[hh]
+                        n = c.n
+                        if int(Fs[i]) != n:
+                            _fail(rep, f"after step {t + 1}: fill {int(Fs[i])} != {n}")
+                        elif not (np.array_equal(Ks[i, :n], c.K[:n]) and np.array_equal(Vs[i, :n], c.V[:n])):
+                            _fail(rep, f"after step {t + 1}: cached K/V rows differ")
+                        elif not np.allclose(VNs[i, :n], c.vnorm[:n], rtol=2e-6, atol=0):
+                            _fail(rep, f"after step {t + 1}: sidecar differs")
                     if rep.failures:
                         return rep
     return rep
@@ -278,18 +357,18 @@ def check_trajectory(rec: Record, workers: int = 0):
     """Replay every sampled pair in the oracle; returns the per-pair reports.
     Fails (AssertionError) with the first failures of each failing pair."""
     global _RECORD
-    jobs = len(rec.layers) * len(rec.pairs)
+    jobs = len(rec.layers) * len(_units(rec))
     if workers <= 0:
         workers = min(jobs, len(os.sched_getaffinity(0)), 8)
     _RECORD = rec
     try:
         if workers == 1:
-            reports = [_check_pair(i) for i in range(jobs)]
+            reports = [_check_unit(i) for i in range(jobs)]
         else:
             # fork: the workers inherit the record and run NumPy only (they
             # never touch the GPU), and no program is exec'd.
             with multiprocessing.get_context("fork").Pool(workers) as pool:
-                reports = pool.map(_check_pair, range(jobs), chunksize=1)
+                reports = pool.map(_check_unit, range(jobs), chunksize=1)
     finally:
         _RECORD = None
     bad = [r for r in reports if r.failures]
@@ -302,10 +381,12 @@ def check_trajectory(rec: Record, workers: int = 0):
 
 def summary(rec: Record, reports) -> str:
     tot = lambda k: sum(getattr(r, k) for r in reports)
-    s = (f"{rec.wl.name} {rec.mode} capacity={rec.capacity} batch={rec.wl.batch} "
+    variant = "" if (rec.order, rec.scope, rec.norm) == ("same_step", "kv_head", "l1") else \
+        f" [{rec.order}, {rec.scope}, {rec.norm}]"
+    s = (f"{rec.wl.name}{variant} {rec.mode} capacity={rec.capacity} batch={rec.wl.batch} "
          f"{rec.wl.num_q_heads}/{rec.wl.num_kv_heads} heads ({rec.launch}, max splits {rec.max_splits}): "
          f"layers {list(rec.layers)} of {rec.num_layers}, "
-         f"{len(reports)} pairs x {rec.steps} steps, evictions {tot('evictions')}, "
+         f"{len(reports)} units x {rec.steps} steps, evictions {tot('evictions')}, "
          f"appends {tot('appends')}, near-ties {tot('near_ties')}, exact ties "
          f"{tot('exact_ties')} (lowest index {tot('tie_lowest_index')}), max rel err "
          f"{max(r.max_rel_err for r in reports):.3g}, snapshots {tot('snapshots')}")
