@@ -61,7 +61,11 @@
  *     Calls are stream-ordered and asynchronous; the library never
  *     synchronises the device and never copies device -> host.
  *   - Arguments are validated on the host before anything is queued. A call
- *     that returns an error has changed nothing.
+ *     that returns any error other than LF_ERR_HIP has changed nothing.
+ *     LF_ERR_HIP means the HIP runtime refused a launch or copy; calls that
+ *     queue several (lf_prefill_fill, lf_seq_reset, lf_cache_snapshot) may
+ *     have queued some before it, so the layer's contents are then
+ *     undefined until it is filled again.
  *   - Inputs must be finite; NaN or Inf make the results undefined.
  *   - A handle is not thread-safe; serialise its calls on one stream.
  */
