@@ -151,10 +151,12 @@ def make_ring(wl, dtype):
     return [(dev(q[i]), dev(k[i]), dev(v[i])) for i in range(RING)]
 
 
-def _cpu_worker(wl, pairs, seconds, start, results):
-    """One host core: step its share of the pairs through the oracle, every
-    pair full, for about `seconds` after the common start. Inputs are drawn
-    before the start (they are resident, as on the GPU)."""
+def _cpu_worker(wl, pairs, fills, seconds, start, results):
+    """One host core: step its share of the pairs through the oracle for
+    about `seconds` after the common start, each pair from its fill level
+    (`fills[b]` tokens of sequence b; full pairs evict at every step, the
+    others append until they reach the budget). Inputs are drawn before the
+    start (they are resident, as on the GPU)."""
     from threadpoolctl import threadpool_limits
     from decode_kv_cache_02_amd.synth import PairTokenStream
     from oracle.longflow_oracle import PairCache
@@ -163,7 +165,7 @@ def _cpu_worker(wl, pairs, seconds, start, results):
         for b, h in pairs:
             ps = PairTokenStream(wl, b, h, seed_offset=99)
             c = PairCache(wl.budget, wl.head_dim)
-            c.prefill(*ps.prefill(wl.budget))
+            c.prefill(*ps.prefill(int(fills[b])))
             caches.append(c)
             inputs.append(ps.steps(RING))
         start.wait()
@@ -180,21 +182,29 @@ def _cpu_worker(wl, pairs, seconds, start, results):
     results.put((len(pairs), steps, el))
 
 
-def cpu_baseline(wl, seconds: float):
+def cpu_baseline(wl, seconds: float, sample: int = 0, fills=None):
     """The float64 oracle on every host core, on a bounded sample of the same
     workload: one process per core (one BLAS thread each), the pairs dealt out
-    round robin, every pair full. Each process steps all of its pairs once per
-    round, for about `seconds`. Must run before the process touches the GPU
-    (the workers are forked)."""
+    round robin, each pair from its fill level (every pair full unless
+    `fills`, one level per sequence, is given). Each process steps all of its
+    pairs once per round, for about `seconds`. `sample` > 0 times that many
+    pairs spread evenly over the layer instead of all of them; the rates are
+    per pair-step, so they scale to the layer. Must run before the process
+    touches the GPU (the workers are forked)."""
     import multiprocessing as mp
     cores = len(os.sched_getaffinity(0))
     all_pairs = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
-    workers = max(1, min(cores, len(all_pairs)))
+    timed = all_pairs
+    if 0 < sample < len(all_pairs):
+        timed = [all_pairs[i * len(all_pairs) // sample] for i in range(sample)]
+    if fills is None:
+        fills = np.full(wl.batch, wl.budget, dtype=np.int64)
+    workers = max(1, min(cores, len(timed)))
     ctx = mp.get_context("fork")
     start = ctx.Barrier(workers + 1)
     results = ctx.Queue()
     procs = [ctx.Process(target=_cpu_worker,
-                         args=(wl, all_pairs[w::workers], seconds, start, results))
+                         args=(wl, timed[w::workers], fills, seconds, start, results))
              for w in range(workers)]
     for p in procs:
         p.start()
@@ -213,16 +223,55 @@ def cpu_baseline(wl, seconds: float):
         for p in procs:
             p.join(timeout=60)
     pair_steps_per_s = sum(n * st / el for n, st, el in got)
-    tokens_per_s = pair_steps_per_s / wl.num_kv_heads
+    steps_per_s = pair_steps_per_s / len(all_pairs)     # layer steps
     pair_steps = sum(n * st for n, st, _ in got)
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "steps_per_s": tokens_per_s / wl.batch, "pair_steps_per_s": pair_steps_per_s,
+    full = bool(np.all(np.asarray(fills) >= wl.budget))
+    return {"value": steps_per_s * wl.batch, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "steps_per_s": steps_per_s, "pair_steps_per_s": pair_steps_per_s,
             "host_cores_available": cores,
-            "sample": f"{wl.name} with every pair full ({len(all_pairs)} pairs x {wl.budget} "
-                      f"slots): {workers} processes, one per host core, each stepping its "
+            "sample": f"{wl.name} with {'every pair full' if full else 'its ragged fill levels'} "
+                      f"({len(all_pairs)} pairs x {wl.budget} slots; "
+                      f"{'all' if len(timed) == len(all_pairs) else len(timed)} of the pairs "
+                      f"timed): {workers} processes, one per host core, each stepping its "
                       f"share of the pairs through the float64 NumPy oracle (one BLAS thread) "
                       f"for {seconds:.0f} s; {pair_steps} pair-steps in all. tokens/s = "
-                      f"pair-steps/s / {wl.num_kv_heads} KV heads"}
+                      f"pair-steps/s / {len(all_pairs)} pairs per layer step x batch {wl.batch}"}
+
+
+def cpu_suite(seconds: float):
+    """The oracle on every host core for each workload configuration, one JSON
+    line each (before any GPU work: the workers are forked). Stacks are timed
+    on one layer with the stack's per-layer shape and fill levels; their
+    model-step rate is that layer rate divided by the layer count
+    (extrapolated)."""
+    from decode_kv_cache_02_amd.native import lf_cache_bytes, make_config
+    from decode_kv_cache_02_amd.synth import WORKLOADS, TokenStream
+
+    def line(name, wl, layers, cpu):
+        cpu = dict(cpu)
+        per_layer = cpu["steps_per_s"]
+        cpu["model_steps_per_s"] = per_layer / layers
+        cpu["value"] = per_layer / layers * wl.batch
+        if layers > 1:
+            cpu["extrapolated"] = f"one layer timed; model steps/s = layer steps/s / {layers}"
+        print(json.dumps({"workload": name, "batch": wl.batch, "budget": wl.budget, "layers": layers,
+                          "cpu_oracle": cpu}), flush=True)
+
+    sample = 64
+    line("tiny_f32", WORKLOADS["tiny_f32"], 1, cpu_baseline(WORKLOADS["tiny_f32"], seconds))
+    for name in ("qwen3_0p6b_layer", "llama8b_layer"):
+        wl = WORKLOADS[name]
+        line(name, wl, 1, cpu_baseline(wl, seconds, sample=sample))
+    wl4 = WORKLOADS["llama8b_stack32_ragged"]
+    per_seq = (lf_cache_bytes(make_config(32, 1, 32, 8, 128, wl4.budget))
+               + lf_cache_bytes(make_config(32, 1, 32, 8, 128, 16384 + 512 + 64, mode="full")))
+    wl4 = wl4.with_(batch=int(0.95 * 288e9 // per_seq))
+    fills = np.minimum(TokenStream(wl4).start_offsets(), wl4.budget)
+    line("llama8b_stack32_ragged LongFlow", wl4, 32, cpu_baseline(wl4, seconds, sample=sample, fills=fills))
+    wl5 = WORKLOADS["qwen3_8b_stack36_ties"]
+    for budget in (512, 1024, 2048, 4096):
+        w = wl5.with_(budget=budget)
+        line(f"qwen3_8b_stack36 B={budget}", w, 36, cpu_baseline(w, seconds, sample=sample))
 
 
 def full_kv_baseline(wl, steps, warmup, fills=(8704, 16384)):
@@ -760,6 +809,9 @@ def main():
         wg_timing(args)
         return
     if args.suite:
+        # the oracle lines first: their workers are forked before any GPU use
+        if not args.no_cpu_baseline:
+            cpu_suite(min(args.cpu_seconds, 6.0))
         import torch
         torch.cuda.set_device(0)
         suite(args)
