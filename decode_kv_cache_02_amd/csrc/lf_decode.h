@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "lf_internal.h"
 
 namespace lf {
@@ -400,10 +402,11 @@ __device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 /*
- * One decode step.
- *   SPLIT = false: one workgroup per pair (blockIdx.x = pair).
- *   SPLIT = true : `splits` workgroups per pair (blockIdx.x = split * pairs +
- *                  pair), each over a contiguous range of 16-slot tiles. Each
+ * One decode step of one unit of work, by the whole workgroup (thread `tid`).
+ *   SPLIT = false: a unit is a pair (unit = pair, in launch order).
+ *   SPLIT = true : a unit is one of the `splits` parts of a pair (unit =
+ *                  split * pairs + pair), a contiguous range of 16-slot
+ *                  tiles. Each
  *                  publishes its partial softmax state (m, l, output) and,
  *                  when the cache is full, its raw logits; the last split to
  *                  arrive combines the partials, scores every slot against
@@ -418,7 +421,7 @@ __device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off
  */
 template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT,
           bool VAR, bool ILV>
-__global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel(DecodeParams P) {
+__device__ __forceinline__ void decode_unit(const DecodeParams& P, const int unit, const int tid) {
   constexpr int kBytes = Elem<T>::kBytes;
   constexpr int NT = WAVES * kWave;
   constexpr int kChunks = D * kBytes / 64;  // 16-byte K loads per lane per 16-slot tile
@@ -453,17 +456,13 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   (void)sh_fac;
   (void)sh_ticket;
 
-  const int tid = threadIdx.x;
-  const ClockRecord clock_rec{P.wg_clock && tid == 0 ? P.wg_clock + 4 * static_cast<size_t>(blockIdx.x)
-                                                     : nullptr,
-                              P.wg_clock ? __builtin_amdgcn_s_memrealtime() : 0};
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
-  // Workgroup -> (sequence b, KV head h). FULL mode dispatches the sequences
+  // Unit -> (sequence b, KV head h). FULL mode dispatches the sequences
   // longest first (P.order); the evicting cache keeps index order.
   const int slot_in_launch =
-      SPLIT ? static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.pairs)) : blockIdx.x;
-  const int split = SPLIT ? static_cast<int>(blockIdx.x / static_cast<uint32_t>(P.pairs)) : 0;
+      SPLIT ? static_cast<int>(static_cast<uint32_t>(unit) % static_cast<uint32_t>(P.pairs)) : unit;
+  const int split = SPLIT ? static_cast<int>(static_cast<uint32_t>(unit) / static_cast<uint32_t>(P.pairs)) : 0;
   const int h = slot_in_launch % P.num_kv_heads;
   int b = slot_in_launch / P.num_kv_heads;
   if constexpr (!EVICT) {
@@ -1501,11 +1500,82 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kern
   if (tid == 0) P.vnorm[static_cast<int64_t>(pair) * slots_pad + slot] = sh_vn_new;
 }
 
+// One workgroup per unit: the hardware hands the units out as workgroups
+// finish.
+template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT,
+          bool VAR, bool ILV>
+__global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel(DecodeParams P) {
+  const ClockRecord clock_rec{P.wg_clock && threadIdx.x == 0 ? P.wg_clock + 4 * static_cast<size_t>(blockIdx.x)
+                                                             : nullptr,
+                              P.wg_clock ? __builtin_amdgcn_s_memrealtime() : 0};
+  decode_unit<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR, ILV>(P, blockIdx.x, threadIdx.x);
+}
+
+// Units in turn: workgroup w takes pairs w, w + grid, w + 2 grid, ... (the
+// evicting main path only: no split, no variant). Used where one workgroup
+// per pair would leave the last round of resident workgroups part-full
+// (units_grid); a grid of pairs / rounds keeps every round full. The thread index is made
+// opaque to the compiler at the top of each unit, so the lane roles and
+// addresses are recomputed per unit rather than held in registers across
+// the loop.
+template <typename T, int D, int G, int WAVES, int UA, int UB, int POLICY, bool ILV>
+__global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel_units(DecodeParams P) {
+  const ClockRecord clock_rec{P.wg_clock && threadIdx.x == 0 ? P.wg_clock + 4 * static_cast<size_t>(blockIdx.x)
+                                                             : nullptr,
+                              P.wg_clock ? __builtin_amdgcn_s_memrealtime() : 0};
+  for (int unit = blockIdx.x; unit < P.pairs; unit += gridDim.x) {
+    // every wave is done with the previous unit's LDS before this one writes it
+    if (unit != static_cast<int>(blockIdx.x)) __syncthreads();
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    decode_unit<T, D, G, true, WAVES, UA, UB, POLICY, false, false, ILV>(P, unit, tid);
+  }
+}
+
+// Resident workgroups of one kernel per compute unit at a dynamic LDS size,
+// from the occupancy query. `memo` belongs to the kernel and keeps the last
+// answer as (lds + 1) << 32 | workgroups, so the query runs once per size.
+inline int resident_per_cu(std::atomic<uint64_t>& memo, const void* kern, int threads, size_t lds) {
+  const uint64_t m = memo.load(std::memory_order_relaxed);
+  if ((m >> 32) == lds + 1) return static_cast<int>(m & 0xffffffffu);
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, threads, lds) != hipSuccess || blocks < 1) {
+    (void)hipGetLastError();
+    blocks = 1;
+  }
+  memo.store(((static_cast<uint64_t>(lds) + 1) << 32) | static_cast<uint32_t>(blocks), std::memory_order_relaxed);
+  return blocks;
+}
+
+// Grid of the units-in-turn kernel for `units` pairs, or 0 for one workgroup
+// per pair. forced > 0 caps the grid at that (tests, tuning); forced < 0
+// always gives one workgroup per pair. Automatically: half the pairs,
+// rounded up, when one workgroup per pair would take two rounds of resident
+// workgroups with the second 40-85% full; 0 otherwise. Measured on the
+// Llama-8B layer (4-wave workgroups, 512 resident): 768 and 816 pairs
+// (second round 50% and 59% full) gain 1.4-2.3%, and the 32-layer ragged
+// stack's 816-pair layers 1.5%; 576 and 640 pairs (13% and 25%) lose
+// 1.5-2%, since most compute units then hold a single workgroup; at 960 and
+// 1016 pairs (88%, 98%) it makes no difference. Over many rounds it gains
+// nothing with equal pairs (4968 pairs: 1252 us either way) and loses with
+// ragged ones (the ragged stack at batch 621: 38.0 -> 38.9 ms per model
+// step), where workgroups handed out by the hardware as others finish
+// balance unequal pairs better than a fixed turn does.
+inline int units_grid(int units, int resident, int cus, int forced) {
+  if (forced < 0) return 0;
+  if (forced > 0) return forced < units ? forced : 0;
+  const int cap = resident * cus;
+  if (cap <= 0 || units <= cap || units >= 2 * cap) return 0;
+  const int last = units - cap;  // pairs of the second round
+  if (last * 10 < cap * 4 || last * 20 > cap * 17) return 0;
+  return (units + 1) / 2;
+}
+
 template <typename T, int D, int G, bool EVICT, bool SPLIT, bool VAR, int WAVES, bool ILV,
           int UA = 1, int UB = 4, int POLICY = kStream>
 hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitWork& W, int splits,
-                           const void* q, const void* k_new, const void* v_new, void* out,
-                           int32_t* evicted, hipStream_t stream) {
+                           const GridPlan& plan, const void* q, const void* k_new, const void* v_new,
+                           void* out, int32_t* evicted, hipStream_t stream) {
   DecodeParams P;
   P.q = q;
   P.k_new = k_new;
@@ -1545,16 +1615,33 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   // pair's scores follow the logits in LDS.
   const size_t score_lds = !ILV && !SPLIT ? decode_score_lds_bytes(geo) : 0;
   P.chunk = static_cast<int32_t>((lds - score_lds) / (sizeof(float) * G));
-  auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR, ILV>;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  const dim3 grid(SPLIT ? pairs * splits : pairs);
   const dim3 block(WAVES * kWave);
-  hipLaunchKernelGGL(kern, grid, block, lds, stream, P);
+  auto prepare = [lds](const void* k) {
+    return lds > 65536 ? hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds))
+                       : hipSuccess;
+  };
+  if constexpr (EVICT && !SPLIT && !VAR && WAVES == 4) {
+    auto kern_u = &decode_kernel_units<T, D, G, WAVES, UA, UB, POLICY, ILV>;
+    static std::atomic<uint64_t> memo{0};
+    const int resident = plan.forced == 0 && plan.cus > 0
+        ? resident_per_cu(memo, reinterpret_cast<const void*>(kern_u), WAVES * kWave, lds)
+        : 0;
+    const int grid_u = units_grid(pairs, resident, plan.cus, plan.forced);
+    if (grid_u > 0) {
+      const hipError_t e = prepare(reinterpret_cast<const void*>(kern_u));
+      if (e != hipSuccess) return e;
+      if (plan.workgroups) *plan.workgroups = grid_u;
+      hipLaunchKernelGGL(kern_u, dim3(grid_u), block, lds, stream, P);
+      return hipGetLastError();
+    }
+  }
+  auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR, ILV>;
+  const hipError_t e = prepare(reinterpret_cast<const void*>(kern));
+  if (e != hipSuccess) return e;
+  const int grid = SPLIT ? pairs * splits : pairs;
+  if (plan.workgroups) *plan.workgroups = grid;
+  hipLaunchKernelGGL(kern, dim3(grid), block, lds, stream, P);
   return hipGetLastError();
 }
 
@@ -1562,11 +1649,11 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
 // one workgroup size and loop kind.
 template <int WAVES, bool ILV>
 hipError_t launch_decode_waves(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
-                               const void* q, const void* k_new, const void* v_new, void* out,
-                               int32_t* evicted, hipStream_t stream) {
+                               const GridPlan& plan, const void* q, const void* k_new,
+                               const void* v_new, void* out, int32_t* evicted, hipStream_t stream) {
   const bool var = g.order != 0 || g.scope != 0;
 #define LF_LAUNCH(T, D, G, EVICT, SPLIT, VAR) \
-  launch_decode_t<T, D, G, EVICT, SPLIT, VAR, WAVES, ILV>(g, L, W, SPLIT ? splits : 1, q, k_new, v_new, out, evicted, stream)
+  launch_decode_t<T, D, G, EVICT, SPLIT, VAR, WAVES, ILV>(g, L, W, SPLIT ? splits : 1, plan, q, k_new, v_new, out, evicted, stream)
 #define LF_CASE(T, D, G)                                                                      \
   if (g.head_dim == D && g.group == G) {                                                     \
     if (g.mode != 0)                                                                         \

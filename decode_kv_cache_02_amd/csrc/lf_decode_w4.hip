@@ -4,9 +4,9 @@
 namespace lf {
 
 hipError_t launch_decode_w4(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,
-                             const void* q, const void* k_new, const void* v_new, void* out,
-                             int32_t* evicted, hipStream_t stream) {
-  return launch_decode_waves<4, false>(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
+                             const GridPlan& plan, const void* q, const void* k_new,
+                             const void* v_new, void* out, int32_t* evicted, hipStream_t stream) {
+  return launch_decode_waves<4, false>(g, L, W, splits, plan, q, k_new, v_new, out, evicted, stream);
 }
 
 }  // namespace lf

@@ -81,17 +81,31 @@ size_t split_part_floats(const Geometry& g);
 // LDS bytes one workgroup may use on the current device.
 size_t device_lds_limit();
 
-// splits == 1: one workgroup per pair. splits > 1: split-K over `splits`
-// workgroups per pair (W must then hold room for that many). waves: 4 or 8
-// waves of 64 lanes per workgroup (8 when one workgroup per CU is all the
-// launch has). ilv: the interleaved loop instead of the phased one.
+// How many workgroups a one-workgroup-per-pair launch may use instead (the
+// evicting main path with 4 waves: no split, no variant). cus > 0 lets the
+// launch halve its grid where the pairs would take two rounds of resident
+// workgroups with the second 40-85% full, each workgroup then taking two
+// pairs in turn; forced > 0 caps the grid at that many, forced < 0 keeps
+// one workgroup per pair. `workgroups` (may be null) receives the grid
+// launched.
+struct GridPlan {
+  int cus = 0;
+  int forced = 0;
+  int* workgroups = nullptr;
+};
+
+// splits == 1: one workgroup per pair, or fewer taking pairs in turn (plan).
+// splits > 1: split-K over `splits` workgroups per pair (W must then hold
+// room for that many). waves: 4 or 8 waves of 64 lanes per workgroup (8 when
+// one workgroup per CU is all the launch has). ilv: the interleaved loop
+// instead of the phased one.
 hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits, int waves,
-                         bool ilv, const void* q, const void* k_new, const void* v_new, void* out,
-                         int32_t* evicted, hipStream_t stream);
+                         bool ilv, const GridPlan& plan, const void* q, const void* k_new,
+                         const void* v_new, void* out, int32_t* evicted, hipStream_t stream);
 #define LF_DECLARE_DECODE_UNIT(NAME)                                                          \
   hipError_t NAME(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits,    \
-                  const void* q, const void* k_new, const void* v_new, void* out,           \
-                  int32_t* evicted, hipStream_t stream);
+                  const GridPlan& plan, const void* q, const void* k_new, const void* v_new, \
+                  void* out, int32_t* evicted, hipStream_t stream);
 LF_DECLARE_DECODE_UNIT(launch_decode_w4)   // lf_decode_w4.hip: 4 waves, phased
 LF_DECLARE_DECODE_UNIT(launch_decode_w8)   // lf_decode_w8.hip: 8 waves, phased
 LF_DECLARE_DECODE_UNIT(launch_decode_w4i)  // lf_decode_w4i.hip: 4 waves, interleaved

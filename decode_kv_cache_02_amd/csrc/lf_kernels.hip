@@ -193,14 +193,14 @@ size_t split_part_floats(const Geometry& g) {
 }
 
 hipError_t launch_decode(const Geometry& g, const LayerPtrs& L, const SplitWork& W, int splits, int waves,
-                         bool ilv, const void* q, const void* k_new, const void* v_new, void* out,
-                         int32_t* evicted, hipStream_t stream) {
+                         bool ilv, const GridPlan& plan, const void* q, const void* k_new,
+                         const void* v_new, void* out, int32_t* evicted, hipStream_t stream) {
   if (waves == 8)
-    return ilv ? launch_decode_w8i(g, L, W, splits, q, k_new, v_new, out, evicted, stream)
-               : launch_decode_w8(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
+    return ilv ? launch_decode_w8i(g, L, W, splits, plan, q, k_new, v_new, out, evicted, stream)
+               : launch_decode_w8(g, L, W, splits, plan, q, k_new, v_new, out, evicted, stream);
   if (waves == 4)
-    return ilv ? launch_decode_w4i(g, L, W, splits, q, k_new, v_new, out, evicted, stream)
-               : launch_decode_w4(g, L, W, splits, q, k_new, v_new, out, evicted, stream);
+    return ilv ? launch_decode_w4i(g, L, W, splits, plan, q, k_new, v_new, out, evicted, stream)
+               : launch_decode_w4(g, L, W, splits, plan, q, k_new, v_new, out, evicted, stream);
   return hipErrorInvalidValue;
 }
 

@@ -48,6 +48,7 @@ struct lf_cache {
   int32_t forced_splits;           // 0: plan automatically
   int32_t forced_waves;            // 0: plan automatically
   int32_t forced_loop;             // 0: plan automatically, 1: phased, 2: interleaved
+  int32_t forced_grid;             // 0: plan automatically, -1: one workgroup per pair, > 0: cap
   int32_t cus;                     // compute units of the device
   size_t lds_limit;                // LDS bytes one workgroup may use
 };
@@ -260,6 +261,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 //   - A launch of at most one workgroup per CU uses 8 waves per workgroup,
 //     otherwise 4 (two workgroups per CU). This needs the 8-wave
 //     workgroup's LDS to fit, and at least 8 tiles per workgroup.
+//   - A one-workgroup-per-pair launch of the evicting main path (4 waves,
+//     no variant) that would take two rounds of resident workgroups, the
+//     second 40-85% full, runs half as many workgroups, each taking two
+//     pairs in turn (decided at launch from the occupancy query).
 // A forced split count (lf_cache_set_splits) wins within max_splits.
 struct LaunchShape {
   int32_t splits;
@@ -352,11 +357,16 @@ lf_status decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_n
   for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
   const LaunchShape shape = plan_launch(c, n_max);
   lf::SplitWork work = c->work;
+  lf::GridPlan grid;
+  grid.cus = c->cus;
+  grid.forced = c->forced_grid;
+  int launched = 0;
   if (timing) {
+    // at most one workgroup per unit, whichever grid the launch takes
     const int64_t wgs = c->layer_pairs * shape.splits;
     if (!timing->records || !timing->workgroups || timing->capacity < wgs) return LF_ERR_INVALID_ARG;
-    *timing->workgroups = static_cast<int32_t>(wgs);
     work.wg_clock = timing->records;
+    grid.workgroups = &launched;
   }
   if (static_scratch) {
     char* base = static_cast<char*>(lf::scratch_ptr(c->device));
@@ -366,11 +376,12 @@ lf_status decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_n
   DeviceScope dev(c->device);
   if (!dev.ok()) return LF_ERR_HIP;
   const lf::LayerPtrs p = layer_ptrs(c, layer);
-  if (lf::launch_decode(c->geo, p, work, shape.splits, shape.waves, shape.ilv, q, k_new, v_new, out,
-                        evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {
+  if (lf::launch_decode(c->geo, p, work, shape.splits, shape.waves, shape.ilv, grid, q, k_new, v_new,
+                        out, evicted_slot, static_cast<hipStream_t>(stream)) != hipSuccess) {
     (void)hipGetLastError();
     return LF_ERR_HIP;
   }
+  if (timing) *timing->workgroups = launched;
   for (int32_t b = 0; b < c->cfg.batch; ++b)
     if (fh[b] < c->cfg.budget) ++fh[b];
   return LF_OK;
@@ -484,6 +495,7 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->forced_splits = 0;
   c->forced_waves = 0;
   c->forced_loop = 0;
+  c->forced_grid = 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
     cus = 256;
@@ -552,6 +564,12 @@ lf_status lf_cache_set_waves(lf_cache* c, int32_t waves) {
 lf_status lf_cache_set_loop(lf_cache* c, int32_t loop) {
   if (!c || loop < 0 || loop > 2) return LF_ERR_INVALID_ARG;
   c->forced_loop = loop;
+  return LF_OK;
+}
+
+lf_status lf_cache_set_grid(lf_cache* c, int32_t workgroups) {
+  if (!c || workgroups < -1) return LF_ERR_INVALID_ARG;
+  c->forced_grid = workgroups;
   return LF_OK;
 }
 

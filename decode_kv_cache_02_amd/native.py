@@ -95,6 +95,7 @@ SIGNATURES = [
     ("lf_cache_set_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_set_waves", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_set_loop", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    ("lf_cache_set_grid", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_max_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_fill_levels", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_cache_destroy", None, [ctypes.c_void_p]),
@@ -263,6 +264,11 @@ def lf_cache_set_loop(handle: int, loop) -> None:
     _check(load_library().lf_cache_set_loop(ctypes.c_void_p(handle), value), "lf_cache_set_loop")
 
 
+def lf_cache_set_grid(handle: int, workgroups: int) -> None:
+    _check(load_library().lf_cache_set_grid(ctypes.c_void_p(handle), int(workgroups)),
+           "lf_cache_set_grid")
+
+
 def lf_cache_max_splits(handle: int) -> int:
     v = ctypes.c_int32(0)
     _check(load_library().lf_cache_max_splits(ctypes.c_void_p(handle), ctypes.byref(v)),
@@ -424,6 +430,11 @@ class LongFlowCache:
     def set_loop(self, loop) -> None:
         """'auto' (or 0), 'phased' (1) or 'interleaved' (2)."""
         lf_cache_set_loop(self.handle, loop)
+
+    def set_grid(self, workgroups: int) -> None:
+        """0 automatic, -1 one workgroup per pair, n > 0 at most n workgroups
+        taking the pairs in turn (evicting main path with 4 waves)."""
+        lf_cache_set_grid(self.handle, workgroups)
 
     @property
     def max_splits(self) -> int:

@@ -296,6 +296,20 @@ lf_status lf_cache_set_waves(lf_cache* c, int32_t waves);
  * of the scores. Errors: LF_ERR_INVALID_ARG for other values. */
 lf_status lf_cache_set_loop(lf_cache* c, int32_t loop);
 
+/* Launch-shape tuning (as above): workgroups of a one-workgroup-per-pair
+ * launch of the evicting main path (4 waves per workgroup, same-step order,
+ * one victim per KV head). By default such a launch runs one workgroup per
+ * pair. The exception is a launch whose pairs would take two rounds of the
+ * workgroups resident on the device at once, the second 40-85% full; it
+ * runs ceil(pairs / 2) workgroups, each taking pairs w and w + grid in turn,
+ * so that no round runs on part of the device. A positive
+ * `workgroups` caps every such launch at that many workgroups. -1 always
+ * keeps one workgroup per pair, and 0 restores the automatic choice. Other
+ * launches (split-K, 8 waves, the variants, FULL mode) ignore it. Every
+ * pair is computed exactly as with one workgroup per pair, so results are
+ * bit-identical. Errors: LF_ERR_INVALID_ARG for values below -1. */
+lf_status lf_cache_set_grid(lf_cache* c, int32_t workgroups);
+
 /* Host-side copy of the fill levels of one layer (tokens held per pair: the
  * initial fill of LongFlow Guide, §Static Memory Pre-Allocation and In-Place
  * Eviction, item 1, grows to the budget), [batch] int32 into the
