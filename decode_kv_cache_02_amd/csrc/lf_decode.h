@@ -47,8 +47,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "lf_internal.h"
 
 namespace lf {
@@ -322,6 +320,27 @@ struct DecodeParams {
   int32_t* seq_arrive;  // [batch]: KV heads done, back to 0 after every launch
   uint64_t* wg_clock;   // optional: per-workgroup timing records (null: none)
   const int32_t* order; // FULL mode: sequences in launch order, longest first
+  // Stream launch (decode_kernel_stream): pairs [0, sk_first) whole, taken in
+  // turn; pairs [sk_first, sk_first + sk_pairs) as one run of sk_pairs *
+  // sk_tiles tiles dealt out sk_q at a time to workgroups 0 .. sk_wgs - 1.
+  int32_t sk_first;
+  int32_t sk_pairs;
+  int32_t sk_tiles;     // tiles per pair (of the longest pair)
+  int32_t sk_q;         // tiles per workgroup
+  int32_t sk_wgs;
+  int32_t sk_stride;    // partials per workspace row
+};
+
+// One part of a pair in a split launch: which pair, which of its parts, the
+// tiles it streams, and the row of the split workspace (partials, raw
+// logits, arrival counter) that the pair's parts share.
+struct Part {
+  int pair;    // the pair, in launch order
+  int index;   // 0 .. count - 1
+  int count;   // parts of the pair
+  int row;     // workspace row
+  int stride;  // partials per workspace row
+  int t0, t1;  // tiles [t0, t1) of the pair; t0 < 0: part `index` of `count` equal ones
 };
 
 // hwreg encodings for s_getreg: XCC_ID (the accelerator complex die a
@@ -404,9 +423,8 @@ __device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off
 /*
  * One decode step of one unit of work, by the whole workgroup (thread `tid`).
  *   SPLIT = false: a unit is a pair (unit = pair, in launch order).
- *   SPLIT = true : a unit is one of the `splits` parts of a pair (unit =
- *                  split * pairs + pair), a contiguous range of 16-slot
- *                  tiles. Each
+ *   SPLIT = true : a unit is one part of a pair (`seg`), a contiguous range
+ *                  of 16-slot tiles. Each
  *                  publishes its partial softmax state (m, l, output) and,
  *                  when the cache is full, its raw logits; the last split to
  *                  arrive combines the partials, scores every slot against
@@ -421,7 +439,8 @@ __device__ __forceinline__ void ws_load_g(__amdgpu_buffer_rsrc_t r, uint32_t off
  */
 template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT,
           bool VAR, bool ILV>
-__device__ __forceinline__ void decode_unit(const DecodeParams& P, const int unit, const int tid) {
+__device__ __forceinline__ void decode_unit(const DecodeParams& P, const int unit, const int tid,
+                                            const Part& seg) {
   constexpr int kBytes = Elem<T>::kBytes;
   constexpr int NT = WAVES * kWave;
   constexpr int kChunks = D * kBytes / 64;  // 16-byte K loads per lane per 16-slot tile
@@ -460,9 +479,8 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
   const int wave = tid >> 6;
   // Unit -> (sequence b, KV head h). FULL mode dispatches the sequences
   // longest first (P.order); the evicting cache keeps index order.
-  const int slot_in_launch =
-      SPLIT ? static_cast<int>(static_cast<uint32_t>(unit) % static_cast<uint32_t>(P.pairs)) : unit;
-  const int split = SPLIT ? static_cast<int>(static_cast<uint32_t>(unit) / static_cast<uint32_t>(P.pairs)) : 0;
+  const int slot_in_launch = SPLIT ? seg.pair : unit;
+  const int split = SPLIT ? seg.index : 0;
   const int h = slot_in_launch % P.num_kv_heads;
   int b = slot_in_launch / P.num_kv_heads;
   if constexpr (!EVICT) {
@@ -485,10 +503,17 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
   int lo = 0, hi = n;
   if (SPLIT) {
     const int tiles = (n + 15) >> 4;
-    const int per = (tiles + P.splits - 1) / P.splits;
-    const int tb = min(split * per, tiles);
+    int tb, te;
+    if (seg.t0 >= 0) {
+      tb = min(seg.t0, tiles);
+      te = min(seg.t1, tiles);
+    } else {
+      const int per = (tiles + seg.count - 1) / seg.count;
+      tb = min(split * per, tiles);
+      te = min(tb + per, tiles);
+    }
     lo = tb * 16;
-    hi = min(min(tb + per, tiles) * 16, n);
+    hi = min(te * 16, n);
   }
 
   // Lane roles. K: r16 = slot within a 16-slot tile, grp = 16-byte chunk
@@ -565,8 +590,13 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
   float best = INFINITY;  // this thread's (score, slot) minimum
   int best_i = 0x7fffffff;
   constexpr int kPart = 2 * G + G * D;  // split partial: m[G], l[G], o[G][D]
-  const int S = SPLIT ? P.splits : 1;
+  const int S = SPLIT ? seg.count : 1;  // parts of this pair
+  // This pair's row of the split workspace: partials, raw logits, counter.
+  const int64_t wsr = SPLIT ? seg.row : pair;
+  const int64_t wstride = SPLIT ? seg.stride : 1;
   (void)S;
+  (void)wsr;
+  (void)wstride;
 
   if constexpr (ILV) {
     // ======== Interleaved loop: K and V of each tile together ========
@@ -839,11 +869,11 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       }
     } else {
       // ---------------- Split: publish this split's partial state ----------------
-      float* mine = P.ws_part + (static_cast<int64_t>(pair) * S + split) * kPart;
+      float* mine = P.ws_part + (wsr * wstride + split) * kPart;
       if (scoring) {
         // Raw logits of this split's slots for the last split's score.
         const __amdgpu_buffer_rsrc_t rW = make_rsrc(
-            P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(hi) * G * 4u);
+            P.ws_logit + wsr * slots_pad * G, static_cast<uint32_t>(hi) * G * 4u);
         for (int i = tid; i < hi - lo; i += NT) {
           float x[G];
           lds_get<G>(lds, i, x);
@@ -869,7 +899,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       drain_stores();
       __syncthreads();
       if (tid == 0)
-        sh_ticket = __hip_atomic_fetch_add(P.arrive + pair, 1, __ATOMIC_RELAXED,
+        sh_ticket = __hip_atomic_fetch_add(P.arrive + wsr, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
     }
@@ -1031,7 +1061,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
       // Split with a full cache: this pair's raw-logit area (no records otherwise).
       const __amdgpu_buffer_rsrc_t rW =
-          make_rsrc(SPLIT && scoring ? P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G : nullptr,
+          make_rsrc(SPLIT && scoring ? P.ws_logit + wsr * slots_pad * G : nullptr,
                     SPLIT && scoring ? static_cast<uint32_t>(slots_pad) * G * 4u : 0u);
       for (int i = tid; i < ntiles * 16; i += NT) {  // masked slots hold -inf -> p = 0
         float x[G];
@@ -1182,7 +1212,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       }
     } else {
       // ---------------- Split: publish this split's partial state ----------------
-      float* mine = P.ws_part + (static_cast<int64_t>(pair) * S + split) * kPart;
+      float* mine = P.ws_part + (wsr * wstride + split) * kPart;
       for (int idx = tid; idx < G * D; idx += NT) {
         const int g = idx / D;
         const int d = idx - g * D;
@@ -1198,7 +1228,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       drain_stores();
       __syncthreads();
       if (tid == 0)
-        sh_ticket = __hip_atomic_fetch_add(P.arrive + pair, 1, __ATOMIC_RELAXED,
+        sh_ticket = __hip_atomic_fetch_add(P.arrive + wsr, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
     }
@@ -1212,7 +1242,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
     // before any of it is used, in the order it is needed: every split's
     // (m, l) for this thread's query head, its partial outputs, then raw
     // logits and norms. The tail costs one memory round trip, not four.
-    const float* part = P.ws_part + static_cast<int64_t>(pair) * S * kPart;
+    const float* part = P.ws_part + wsr * wstride * kPart;
     float ml[kMaxSplits][2];
     {
       const int g = tid & (G - 1);
@@ -1231,7 +1261,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
         op[j][s2] = s2 < S ? ws_load(part + s2 * kPart + 2 * G + idx) : 0.0f;
     }
     const __amdgpu_buffer_rsrc_t rL = make_rsrc(
-        P.ws_logit + static_cast<int64_t>(pair) * slots_pad * G, static_cast<uint32_t>(n) * G * 4u);
+        P.ws_logit + wsr * slots_pad * G, static_cast<uint32_t>(n) * G * 4u);
     const __amdgpu_buffer_rsrc_t rNa =
         make_rsrc(P.vnorm + static_cast<int64_t>(pair) * slots_pad, static_cast<uint32_t>(n) * 4u);
     constexpr int kLastBatch = 8;  // slots per thread with loads in flight together
@@ -1328,7 +1358,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       if (idx < G * D) from_f32(ofin[j], out_rows() + idx);
     }
     if (shared && scoring && tid == 0) ws_store(P.ws_nnorm + pair, sh_vn_new);
-    if (tid == 0) __hip_atomic_store(P.arrive + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(P.arrive + wsr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // ---------------- Choice of the victim ----------------
   // One victim per pair: the cross-wave argmin of this workgroup, lowest slot
@@ -1501,74 +1531,72 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
 }
 
 // One workgroup per unit: the hardware hands the units out as workgroups
-// finish.
+// finish. Split launches: unit = split * pairs + pair, equal parts.
 template <typename T, int D, int G, bool EVICT, int WAVES, int UA, int UB, int POLICY, bool SPLIT,
           bool VAR, bool ILV>
 __global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel(DecodeParams P) {
   const ClockRecord clock_rec{P.wg_clock && threadIdx.x == 0 ? P.wg_clock + 4 * static_cast<size_t>(blockIdx.x)
                                                              : nullptr,
                               P.wg_clock ? __builtin_amdgcn_s_memrealtime() : 0};
-  decode_unit<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR, ILV>(P, blockIdx.x, threadIdx.x);
+  Part seg{0, 0, 1, 0, 1, -1, -1};
+  if constexpr (SPLIT) {
+    const int pair = static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.pairs));
+    seg = Part{pair, static_cast<int>(blockIdx.x / static_cast<uint32_t>(P.pairs)), P.splits, pair,
+               P.splits, -1, -1};
+  }
+  decode_unit<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR, ILV>(P, blockIdx.x, threadIdx.x, seg);
 }
 
-// Units in turn: workgroup w takes pairs w, w + grid, w + 2 grid, ... (the
-// evicting main path only: no split, no variant). Used where one workgroup
-// per pair would leave the last round of resident workgroups part-full
-// (units_grid); a grid of pairs / rounds keeps every round full. The thread index is made
-// opaque to the compiler at the top of each unit, so the lane roles and
-// addresses are recomputed per unit rather than held in registers across
-// the loop.
+// Stream launch of the evicting main path (no variant): workgroup w first
+// takes its sk_q tiles of the run of pairs [sk_first, sk_first + sk_pairs)
+// (a pair cut between workgroups becomes a split pair, combined by the last
+// of its parts to finish; a pair held whole by w runs as usual), then the
+// whole pairs w, w + grid, ... below sk_first. With sk_pairs = 0 this is
+// whole pairs in turn. Every workgroup then does the same share of the
+// layer's tiles, where one workgroup per pair would leave a round of
+// resident workgroups part-full. A barrier separates the units, and the
+// thread index is made opaque to the compiler at the top of each unit, so
+// the lane roles and addresses are recomputed per unit rather than held in
+// registers across the loop.
 template <typename T, int D, int G, int WAVES, int UA, int UB, int POLICY, bool ILV>
-__global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel_units(DecodeParams P) {
+__global__ __launch_bounds__(WAVES * kWave, WAVES >= 8 ? 1 : 2) void decode_kernel_stream(DecodeParams P) {
   const ClockRecord clock_rec{P.wg_clock && threadIdx.x == 0 ? P.wg_clock + 4 * static_cast<size_t>(blockIdx.x)
                                                              : nullptr,
                               P.wg_clock ? __builtin_amdgcn_s_memrealtime() : 0};
-  for (int unit = blockIdx.x; unit < P.pairs; unit += gridDim.x) {
-    // every wave is done with the previous unit's LDS before this one writes it
-    if (unit != static_cast<int>(blockIdx.x)) __syncthreads();
+  const int w = blockIdx.x;
+  bool first = true;
+  if (w < P.sk_wgs) {
+    const int64_t tn = P.sk_tiles;
+    const int64_t total = static_cast<int64_t>(P.sk_pairs) * tn;
+    const int64_t end = min(static_cast<int64_t>(w) * P.sk_q + P.sk_q, total);
+    for (int64_t t = static_cast<int64_t>(w) * P.sk_q; t < end;) {
+      const int row = static_cast<int>(t / tn);
+      const int64_t base = row * tn;
+      const int fw = static_cast<int>(base / P.sk_q);              // the pair's first workgroup
+      const int lw = static_cast<int>((base + tn - 1) / P.sk_q);   // and its last
+      if (!first) __syncthreads();  // every wave is done with the previous unit's LDS
+      first = false;
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      if (fw == lw) {
+        decode_unit<T, D, G, true, WAVES, UA, UB, POLICY, false, false, ILV>(
+            P, P.sk_first + row, tid, Part{0, 0, 1, 0, 1, -1, -1});
+      } else {
+        const Part seg{P.sk_first + row, w - fw, lw - fw + 1, row, P.sk_stride,
+                       static_cast<int>(t - base), static_cast<int>(min(end - base, tn))};
+        decode_unit<T, D, G, true, WAVES, UA, UB, POLICY, true, false, ILV>(P, 0, tid, seg);
+      }
+      t = base + tn;
+    }
+  }
+  for (int unit = w; unit < P.sk_first; unit += gridDim.x) {
+    if (!first) __syncthreads();
+    first = false;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_unit<T, D, G, true, WAVES, UA, UB, POLICY, false, false, ILV>(P, unit, tid);
+    decode_unit<T, D, G, true, WAVES, UA, UB, POLICY, false, false, ILV>(P, unit, tid,
+                                                                      Part{0, 0, 1, 0, 1, -1, -1});
   }
-}
-
-// Resident workgroups of one kernel per compute unit at a dynamic LDS size,
-// from the occupancy query. `memo` belongs to the kernel and keeps the last
-// answer as (lds + 1) << 32 | workgroups, so the query runs once per size.
-inline int resident_per_cu(std::atomic<uint64_t>& memo, const void* kern, int threads, size_t lds) {
-  const uint64_t m = memo.load(std::memory_order_relaxed);
-  if ((m >> 32) == lds + 1) return static_cast<int>(m & 0xffffffffu);
-  int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, threads, lds) != hipSuccess || blocks < 1) {
-    (void)hipGetLastError();
-    blocks = 1;
-  }
-  memo.store(((static_cast<uint64_t>(lds) + 1) << 32) | static_cast<uint32_t>(blocks), std::memory_order_relaxed);
-  return blocks;
-}
-
-// Grid of the units-in-turn kernel for `units` pairs, or 0 for one workgroup
-// per pair. forced > 0 caps the grid at that (tests, tuning); forced < 0
-// always gives one workgroup per pair. Automatically: half the pairs,
-// rounded up, when one workgroup per pair would take two rounds of resident
-// workgroups with the second 40-85% full; 0 otherwise. Measured on the
-// Llama-8B layer (4-wave workgroups, 512 resident): 768 and 816 pairs
-// (second round 50% and 59% full) gain 1.4-2.3%, and the 32-layer ragged
-// stack's 816-pair layers 1.5%; 576 and 640 pairs (13% and 25%) lose
-// 1.5-2%, since most compute units then hold a single workgroup; at 960 and
-// 1016 pairs (88%, 98%) it makes no difference. Over many rounds it gains
-// nothing with equal pairs (4968 pairs: 1252 us either way) and loses with
-// ragged ones (the ragged stack at batch 621: 38.0 -> 38.9 ms per model
-// step), where workgroups handed out by the hardware as others finish
-// balance unequal pairs better than a fixed turn does.
-inline int units_grid(int units, int resident, int cus, int forced) {
-  if (forced < 0) return 0;
-  if (forced > 0) return forced < units ? forced : 0;
-  const int cap = resident * cus;
-  if (cap <= 0 || units <= cap || units >= 2 * cap) return 0;
-  const int last = units - cap;  // pairs of the second round
-  if (last * 10 < cap * 4 || last * 20 > cap * 17) return 0;
-  return (units + 1) / 2;
 }
 
 template <typename T, int D, int G, bool EVICT, bool SPLIT, bool VAR, int WAVES, bool ILV,
@@ -1609,6 +1637,7 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   P.arrive = W.arrive;
   P.wg_clock = W.wg_clock;
   P.order = EVICT ? nullptr : L.order;
+  P.sk_first = P.sk_pairs = P.sk_tiles = P.sk_q = P.sk_wgs = P.sk_stride = 0;
   const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits, ILV) : decode_lds_bytes(geo, ILV);
   if (lds == 0) return hipErrorInvalidValue;
   // Phased loop, one workgroup per pair with one victim per sequence: the
@@ -1621,27 +1650,25 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
                                              static_cast<int>(lds))
                        : hipSuccess;
   };
-  if constexpr (EVICT && !SPLIT && !VAR && WAVES == 4) {
-    auto kern_u = &decode_kernel_units<T, D, G, WAVES, UA, UB, POLICY, ILV>;
-    static std::atomic<uint64_t> memo{0};
-    const int resident = plan.forced == 0 && plan.cus > 0
-        ? resident_per_cu(memo, reinterpret_cast<const void*>(kern_u), WAVES * kWave, lds)
-        : 0;
-    const int grid_u = units_grid(pairs, resident, plan.cus, plan.forced);
-    if (grid_u > 0) {
-      const hipError_t e = prepare(reinterpret_cast<const void*>(kern_u));
+  if constexpr (EVICT && !SPLIT && !VAR) {
+    if (plan.grid > 0) {
+      P.sk_first = plan.sk_first;
+      P.sk_pairs = plan.sk_pairs;
+      P.sk_tiles = plan.sk_tiles;
+      P.sk_q = plan.sk_q;
+      P.sk_wgs = plan.sk_wgs;
+      P.sk_stride = plan.sk_stride;
+      auto kern_s = &decode_kernel_stream<T, D, G, WAVES, UA, UB, POLICY, ILV>;
+      const hipError_t e = prepare(reinterpret_cast<const void*>(kern_s));
       if (e != hipSuccess) return e;
-      if (plan.workgroups) *plan.workgroups = grid_u;
-      hipLaunchKernelGGL(kern_u, dim3(grid_u), block, lds, stream, P);
+      hipLaunchKernelGGL(kern_s, dim3(plan.grid), block, lds, stream, P);
       return hipGetLastError();
     }
   }
   auto kern = &decode_kernel<T, D, G, EVICT, WAVES, UA, UB, POLICY, SPLIT, VAR, ILV>;
   const hipError_t e = prepare(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
-  const int grid = SPLIT ? pairs * splits : pairs;
-  if (plan.workgroups) *plan.workgroups = grid;
-  hipLaunchKernelGGL(kern, dim3(grid), block, lds, stream, P);
+  hipLaunchKernelGGL(kern, dim3(SPLIT ? pairs * splits : pairs), block, lds, stream, P);
   return hipGetLastError();
 }
 

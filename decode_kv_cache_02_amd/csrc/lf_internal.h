@@ -64,6 +64,16 @@ constexpr int kMaxSplits = 16;
 constexpr int kSplitGridTarget = 512;
 constexpr int kSplitPairsBelow = 256;
 constexpr int kMinSplitSlots = 256;   // fewer slots per split are not worth a split
+// Stream launches (GridPlan): the evicting main path gets workspace rows
+// (kMaxSplits parts each, at most kStreamRows) for the pairs a stream launch
+// would cut on a device of kStreamCusRef compute units (MI355X) with one or
+// two resident 4-wave workgroups per compute unit, decided from the
+// configuration alone so that lf_cache_bytes needs no device; on another
+// device a launch streams only if its cut pairs fit. A workgroup's share is
+// at least kStreamMinTiles tiles.
+constexpr int kStreamRows = 512;
+constexpr int kStreamCusRef = 256;
+constexpr int kStreamMinTiles = 16;
 // Launches whose workgroups stream at most this many slots use the
 // interleaved loop (K and V of each tile together, both streams in flight
 // from the start); longer streams use the phased loop (K, then V).
@@ -81,20 +91,24 @@ size_t split_part_floats(const Geometry& g);
 // LDS bytes one workgroup may use on the current device.
 size_t device_lds_limit();
 
-// How many workgroups a one-workgroup-per-pair launch may use instead (the
-// evicting main path with 4 waves: no split, no variant). cus > 0 lets the
-// launch halve its grid where the pairs would take two rounds of resident
-// workgroups with the second 40-85% full, each workgroup then taking two
-// pairs in turn; forced > 0 caps the grid at that many, forced < 0 keeps
-// one workgroup per pair. `workgroups` (may be null) receives the grid
-// launched.
+// How a launch of the evicting main path (4 waves, no split, no variant)
+// spreads its pairs over workgroups; the runtime plans it. grid = 0: one
+// workgroup per pair. grid > 0: decode_kernel_stream with `grid` workgroups:
+// whole pairs [0, sk_first) taken in turn, then pairs [sk_first, sk_first +
+// sk_pairs) as one run of sk_pairs * sk_tiles tiles dealt out sk_q at a time
+// to workgroups 0 .. sk_wgs - 1, a pair cut between workgroups combining its
+// parts through workspace rows of sk_stride partials (row = pair - sk_first).
 struct GridPlan {
-  int cus = 0;
-  int forced = 0;
-  int* workgroups = nullptr;
+  int grid = 0;
+  int sk_first = 0;
+  int sk_pairs = 0;
+  int sk_tiles = 0;
+  int sk_q = 0;
+  int sk_wgs = 0;
+  int sk_stride = 0;
 };
 
-// splits == 1: one workgroup per pair, or fewer taking pairs in turn (plan).
+// splits == 1: one workgroup per pair, or the stream launch of `plan`.
 // splits > 1: split-K over `splits` workgroups per pair (W must then hold
 // room for that many). waves: 4 or 8 waves of 64 lanes per workgroup (8 when
 // one workgroup per CU is all the launch has). ilv: the interleaved loop
@@ -141,7 +155,7 @@ hipError_t launch_set_order(int32_t* order, const int32_t* seq_host, int32_t fir
 // between launches): split-K counters at word 0 + pair, per-sequence counters
 // at word kScratchSeqCounterWord + sequence. The rest holds the workspace
 // of one launch.
-constexpr size_t kScratchBytes = size_t{16} << 20;
+constexpr size_t kScratchBytes = size_t{64} << 20;
 constexpr size_t kScratchCounterBytes = size_t{64} << 10;
 constexpr int32_t kScratchSeqCounterWord = 8192;
 // Looks up the array's device address on `device` (which must be current)

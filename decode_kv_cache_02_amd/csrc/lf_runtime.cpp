@@ -49,8 +49,12 @@ struct lf_cache {
   int32_t forced_waves;            // 0: plan automatically
   int32_t forced_loop;             // 0: plan automatically, 1: phased, 2: interleaved
   int32_t forced_grid;             // 0: plan automatically, -1: one workgroup per pair, > 0: cap
+  int32_t forced_stream;           // 0: plan automatically, > 0: stream launch of that many tiles
+  int32_t sk_rows;                 // workspace rows for the cut pairs of a stream launch
+  int32_t sk_stride;               // partials per workspace row
   int32_t cus;                     // compute units of the device
   size_t lds_limit;                // LDS bytes one workgroup may use
+  size_t lds_per_cu;               // LDS bytes of one compute unit
 };
 
 namespace {
@@ -124,6 +128,23 @@ lf::Geometry geometry(const lf_config* c) {
   return g;
 }
 
+// Workspace rows for the cut pairs of stream launches on the evicting main
+// path (same-step order, one victim per KV head): the most pairs the stream
+// rule of plan_stream cuts on a device of kStreamCusRef compute units, at
+// most kStreamRows.
+// Layers with a split-K workspace (max_splits > 1) use that one instead.
+int32_t stream_rows(const lf_config* c, int32_t max_splits) {
+  const int64_t pairs = static_cast<int64_t>(c->batch) * c->num_kv_heads;
+  if (max_splits > 1 || c->mode != LF_MODE_EVICT || c->order != LF_ORDER_SAME_STEP ||
+      c->scope != LF_SCOPE_KV_HEAD || pairs <= lf::kStreamCusRef)
+    return 0;
+  // just past one round of 8-wave (room = CUs) or 4-wave (2 CUs) workgroups
+  int64_t rows = 0;
+  for (const int64_t room : {int64_t{lf::kStreamCusRef}, 2 * int64_t{lf::kStreamCusRef}})
+    if (pairs > room && pairs * 10 <= room * 13) rows = std::max(rows, pairs - room);
+  return static_cast<int32_t>(std::min<int64_t>(rows, lf::kStreamRows));
+}
+
 lf_status layout(const lf_config* c, int32_t max_splits, Layout* L) {
   const lf::Geometry g = geometry(c);
   const size_t elem = c->dtype == LF_DTYPE_F32 ? 4 : 2;
@@ -153,17 +174,22 @@ lf_status layout(const lf_config* c, int32_t max_splits, Layout* L) {
   if (!add_ok(L->order_off, align_up(c->mode == LF_MODE_FULL
                                           ? static_cast<size_t>(c->num_layers) * c->batch * 4 : 0), &t))
     return LF_ERR_UNSUPPORTED;
-  // Split-K workspace for one layer (the layers run one after another).
+  // Split-K workspace for one layer (the layers run one after another):
+  // split launches (rows = pairs, max_splits partials each), or the cut
+  // pairs of stream launches (stream_rows rows of kMaxSplits partials).
   size_t layer_pairs = static_cast<size_t>(c->batch) * c->num_kv_heads;
-  size_t ws = max_splits > 1 ? layer_pairs * max_splits : 0;
-  const size_t logits = max_splits > 1 && c->mode == LF_MODE_EVICT
-      ? layer_pairs * static_cast<size_t>(g.slots_pad) * g.group * 4 : 0;
+  const size_t srows = static_cast<size_t>(stream_rows(c, max_splits));
+  size_t ws = max_splits > 1 ? layer_pairs * max_splits : srows * lf::kMaxSplits;
+  const size_t logit_rows = max_splits > 1 ? layer_pairs : srows;
+  const size_t logits = (max_splits > 1 || srows > 0) && c->mode == LF_MODE_EVICT
+      ? logit_rows * static_cast<size_t>(g.slots_pad) * g.group * 4 : 0;
   L->part_off = t;
   if (!add_ok(L->part_off, align_up(ws * lf::split_part_floats(g) * 4), &t)) return LF_ERR_UNSUPPORTED;
   L->logit_off = t;
   if (!add_ok(L->logit_off, align_up(logits), &t)) return LF_ERR_UNSUPPORTED;
   L->arrive_off = t;
-  if (!add_ok(L->arrive_off, align_up(max_splits > 1 ? layer_pairs * 4 : 0), &t)) return LF_ERR_UNSUPPORTED;
+  if (!add_ok(L->arrive_off, align_up(max_splits > 1 ? layer_pairs * 4 : srows * 4), &t))
+    return LF_ERR_UNSUPPORTED;
   // One victim per sequence: each pair's score vector for one layer launch.
   const bool shared = c->scope == LF_SCOPE_SEQUENCE;
   L->score_off = t;
@@ -262,9 +288,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 //     otherwise 4 (two workgroups per CU). This needs the 8-wave
 //     workgroup's LDS to fit, and at least 8 tiles per workgroup.
 //   - A one-workgroup-per-pair launch of the evicting main path (4 waves,
-//     no variant) that would take two rounds of resident workgroups, the
-//     second 40-85% full, runs half as many workgroups, each taking two
-//     pairs in turn (decided at launch from the occupancy query).
+//     no variant) may run as a stream launch instead (plan_stream).
 // A forced split count (lf_cache_set_splits) wins within max_splits.
 struct LaunchShape {
   int32_t splits;
@@ -298,15 +322,106 @@ LaunchShape plan_launch(const lf_cache* c, int32_t n_max) {
   return {s, waves, ilv};
 }
 
+// Resident 4-wave decode workgroups per compute unit: two (the kernels'
+// launch bounds) when their LDS fits the compute unit twice, else one.
+int32_t resident_4wave(const lf_cache* c, bool ilv) {
+  const size_t per_wg = lf::decode_lds_bytes(c->geo, ilv) + lf::decode_static_lds_bytes(c->geo, 4);
+  return 2 * per_wg <= c->lds_per_cu ? 2 : 1;
+}
+
+// Stream launch of the evicting main path (no split, no variant), or grid = 0
+// for one workgroup per pair. With R workgroups resident at once, P pairs
+// take ceil(P / R) rounds of whole pairs, and a part-full last round leaves
+// the device partly idle.
+//   - Just past one round (R < P <= 1.3 R): every workgroup takes its whole
+//     pair of the first round, then an equal run (at least kStreamMinTiles
+//     tiles) of the remaining pairs' tiles; pairs cut between workgroups
+//     combine their parts as split-K does. Just past one round of 8-wave
+//     workgroups (one per compute unit: cus < P <= 1.3 cus) the launch
+//     switches to 8 waves for this; past one round of 4-wave workgroups
+//     (2 cus < P <= 2.6 cus with two resident per compute unit) it keeps 4.
+//     Needs workspace rows for the cut pairs.
+//   - Two rounds of 4-wave workgroups with the second 40-85% full:
+//     ceil(P / 2) workgroups taking two whole pairs each.
+//   - Otherwise one workgroup per pair.
+// No pair is cut into more than `stride` parts. Overrides: forced_stream > 0
+// streams every pair with that many tiles per workgroup (no whole pairs
+// first); forced_grid > 0 takes whole pairs in turn on that many
+// workgroups; forced_grid < 0 keeps one workgroup per pair.
+lf::GridPlan plan_stream(const lf_cache* c, LaunchShape* shape, int32_t n_max) {
+  lf::GridPlan g;
+  const lf::Geometry& geo = c->geo;
+  if (shape->splits != 1 || geo.mode != LF_MODE_EVICT || geo.order != 0 || geo.scope != 0 ||
+      c->forced_grid < 0)
+    return g;
+  const int64_t pairs = c->layer_pairs;
+  const int64_t tn = std::max<int64_t>(1, (static_cast<int64_t>(n_max) + 15) / 16);
+  const int64_t stride = c->sk_stride;
+  // tiles per share so that no pair is cut into more than `stride` parts
+  const int64_t q_min = stride > 1 ? (tn + stride - 2) / (stride - 1) : tn;
+  auto stream = [&](int64_t first, int64_t q, int64_t grid_min) {
+    const int64_t run = (pairs - first) * tn;
+    q = std::max(q, q_min);
+    g.sk_first = static_cast<int>(first);
+    g.sk_pairs = static_cast<int>(pairs - first);
+    g.sk_tiles = static_cast<int>(tn);
+    g.sk_q = static_cast<int>(q);
+    g.sk_wgs = static_cast<int>((run + q - 1) / q);
+    g.sk_stride = static_cast<int>(stride);
+    g.grid = static_cast<int>(std::max<int64_t>(grid_min, g.sk_wgs));
+  };
+  if (c->forced_stream > 0) {
+    if (pairs <= c->sk_rows && stride > 1) stream(0, c->forced_stream, 1);
+    return g;
+  }
+  if (shape->waves != 4) return g;
+  if (c->forced_grid > 0) {
+    if (c->forced_grid < pairs) {
+      g.grid = c->forced_grid;
+      g.sk_first = static_cast<int>(pairs);
+    }
+    return g;
+  }
+  // whole pairs for the first `room` workgroups, the rest cut into runs
+  auto past_one_round = [&](int64_t room) {
+    const int64_t cut = pairs - room;
+    if (cut <= 0 || cut > c->sk_rows || stride <= 1 || pairs * 10 > room * 13) return false;
+    const int64_t run = cut * tn;
+    const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(room, run / lf::kStreamMinTiles));
+    stream(room, std::max<int64_t>((run + wgs - 1) / wgs, lf::kStreamMinTiles), room);
+    return true;
+  };
+  const size_t dyn = lf::decode_lds_bytes(geo, shape->ilv);
+  if (c->forced_waves == 0 && dyn + lf::decode_static_lds_bytes(geo, 8) <= c->lds_limit &&
+      past_one_round(c->cus)) {
+    shape->waves = 8;
+    return g;
+  }
+  const int64_t room = static_cast<int64_t>(resident_4wave(c, shape->ilv)) * c->cus;
+  if (room <= c->cus || pairs <= c->cus) return g;
+  if (past_one_round(room)) return g;
+  const int64_t last = pairs - room;  // pairs of a second round
+  if (last > 0 && last <= room && last * 10 >= room * 4 && last * 20 <= room * 17) {
+    g.grid = static_cast<int>((pairs + 1) / 2);
+    g.sk_first = static_cast<int>(pairs);
+  }
+  return g;
+}
+
 // Workspace of one decode launch carved out of the device's static scratch:
 // counters at fixed words of the counter area, the rest after it. Returns
 // false if the launch needs more than the array holds.
-bool scratch_work(const lf_cache* c, char* base, int32_t splits, lf::SplitWork* w) {
+bool scratch_work(const lf_cache* c, char* base, int32_t splits, const lf::GridPlan& plan,
+                  lf::SplitWork* w) {
   const lf::Geometry& g = c->geo;
-  const size_t pairs = static_cast<size_t>(c->layer_pairs);
   const bool split = splits > 1;
+  const bool cut = plan.grid > 0 && plan.sk_pairs > 0;  // stream launch with cut pairs
+  // workspace rows: every pair (split-K) or the stream launch's cut pairs
+  const size_t pairs = static_cast<size_t>(c->layer_pairs);
+  const size_t rows = split ? pairs : cut ? static_cast<size_t>(plan.sk_pairs) : 0;
+  const size_t per_row = split ? static_cast<size_t>(splits) : static_cast<size_t>(plan.sk_stride);
   const bool shared = g.scope == LF_SCOPE_SEQUENCE;
-  if (split && pairs > static_cast<size_t>(lf::kScratchSeqCounterWord)) return false;
+  if (rows > static_cast<size_t>(lf::kScratchSeqCounterWord)) return false;
   if (shared && (static_cast<size_t>(lf::kScratchSeqCounterWord) + g.batch) * 4 > lf::kScratchCounterBytes)
     return false;
   size_t off = lf::kScratchCounterBytes;
@@ -316,8 +431,8 @@ bool scratch_work(const lf_cache* c, char* base, int32_t splits, lf::SplitWork* 
     return base + at;
   };
   // Each size is at most the cache's own K region, so none overflows.
-  const size_t part = split ? pairs * splits * lf::split_part_floats(g) * 4 : 0;
-  const size_t logit = split && g.mode == LF_MODE_EVICT ? pairs * g.slots_pad * g.group * 4 : 0;
+  const size_t part = rows * per_row * lf::split_part_floats(g) * 4;
+  const size_t logit = g.mode == LF_MODE_EVICT ? rows * g.slots_pad * g.group * 4 : 0;
   const size_t score = shared ? pairs * g.slots_pad * 4 : 0;
   const size_t nnorm = shared ? pairs * 4 : 0;
   if (part > lf::kScratchBytes || logit > lf::kScratchBytes || score > lf::kScratchBytes) return false;
@@ -355,23 +470,18 @@ lf_status decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_n
   }
   int32_t n_max = 0;
   for (int32_t b = 0; b < c->cfg.batch; ++b) n_max = std::max(n_max, fh[b]);
-  const LaunchShape shape = plan_launch(c, n_max);
+  LaunchShape shape = plan_launch(c, n_max);
+  const lf::GridPlan grid = plan_stream(c, &shape, n_max);
   lf::SplitWork work = c->work;
-  lf::GridPlan grid;
-  grid.cus = c->cus;
-  grid.forced = c->forced_grid;
-  int launched = 0;
+  const int64_t wgs = grid.grid > 0 ? grid.grid : c->layer_pairs * shape.splits;
   if (timing) {
-    // at most one workgroup per unit, whichever grid the launch takes
-    const int64_t wgs = c->layer_pairs * shape.splits;
     if (!timing->records || !timing->workgroups || timing->capacity < wgs) return LF_ERR_INVALID_ARG;
     work.wg_clock = timing->records;
-    grid.workgroups = &launched;
   }
   if (static_scratch) {
     char* base = static_cast<char*>(lf::scratch_ptr(c->device));
     if (!base) return LF_ERR_HIP;  // set up by lf_cache_create on this device
-    if (!scratch_work(c, base, shape.splits, &work)) return LF_ERR_SCRATCH;
+    if (!scratch_work(c, base, shape.splits, grid, &work)) return LF_ERR_SCRATCH;
   }
   DeviceScope dev(c->device);
   if (!dev.ok()) return LF_ERR_HIP;
@@ -381,7 +491,7 @@ lf_status decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_n
     (void)hipGetLastError();
     return LF_ERR_HIP;
   }
-  if (timing) *timing->workgroups = launched;
+  if (timing) *timing->workgroups = static_cast<int32_t>(wgs);
   for (int32_t b = 0; b < c->cfg.batch; ++b)
     if (fh[b] < c->cfg.budget) ++fh[b];
   return LF_OK;
@@ -496,11 +606,22 @@ lf_status lf_cache_create(const lf_config* cfg, lf_cache** out) {
   c->forced_waves = 0;
   c->forced_loop = 0;
   c->forced_grid = 0;
+  c->forced_stream = 0;
+  c->sk_rows = max_splits > 1 ? static_cast<int32_t>(c->layer_pairs) : stream_rows(cfg, max_splits);
+  c->sk_stride = max_splits > 1 ? max_splits : lf::kMaxSplits;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
     cus = 256;
   c->cus = cus;
   c->lds_limit = lf::device_lds_limit();
+  int lds_cu = 0;
+  if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device) !=
+          hipSuccess ||
+      lds_cu < 1) {
+    (void)hipGetLastError();
+    lds_cu = 160 * 1024;
+  }
+  c->lds_per_cu = static_cast<size_t>(lds_cu);
   *out = c;
   return LF_OK;
 }
@@ -570,6 +691,12 @@ lf_status lf_cache_set_loop(lf_cache* c, int32_t loop) {
 lf_status lf_cache_set_grid(lf_cache* c, int32_t workgroups) {
   if (!c || workgroups < -1) return LF_ERR_INVALID_ARG;
   c->forced_grid = workgroups;
+  return LF_OK;
+}
+
+lf_status lf_cache_set_stream(lf_cache* c, int32_t tiles) {
+  if (!c || tiles < 0) return LF_ERR_INVALID_ARG;
+  c->forced_stream = tiles;
   return LF_OK;
 }
 

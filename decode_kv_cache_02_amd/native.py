@@ -96,6 +96,7 @@ SIGNATURES = [
     ("lf_cache_set_waves", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_set_loop", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_set_grid", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    ("lf_cache_set_stream", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("lf_cache_max_splits", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_fill_levels", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     ("lf_cache_destroy", None, [ctypes.c_void_p]),
@@ -269,6 +270,11 @@ def lf_cache_set_grid(handle: int, workgroups: int) -> None:
            "lf_cache_set_grid")
 
 
+def lf_cache_set_stream(handle: int, tiles: int) -> None:
+    _check(load_library().lf_cache_set_stream(ctypes.c_void_p(handle), int(tiles)),
+           "lf_cache_set_stream")
+
+
 def lf_cache_max_splits(handle: int) -> int:
     v = ctypes.c_int32(0)
     _check(load_library().lf_cache_max_splits(ctypes.c_void_p(handle), ctypes.byref(v)),
@@ -432,9 +438,14 @@ class LongFlowCache:
         lf_cache_set_loop(self.handle, loop)
 
     def set_grid(self, workgroups: int) -> None:
-        """0 automatic, -1 one workgroup per pair, n > 0 at most n workgroups
-        taking the pairs in turn (evicting main path with 4 waves)."""
+        """0 automatic, -1 one workgroup per pair, n > 0 n workgroups taking
+        whole pairs in turn (evicting main path with 4 waves)."""
         lf_cache_set_grid(self.handle, workgroups)
+
+    def set_stream(self, tiles: int) -> None:
+        """0 automatic, n > 0 a stream launch over every pair with n tiles
+        per workgroup (evicting main path with 4 waves, no split)."""
+        lf_cache_set_stream(self.handle, tiles)
 
     @property
     def max_splits(self) -> int:

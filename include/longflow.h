@@ -218,7 +218,7 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
  * where the launch's cross-workgroup workspace lives (split-K partial states,
  * raw logits and arrival counters; the score vectors, new-token norms and
  * counters of LF_SCOPE_SEQUENCE). Here it comes from one static device array
- * of the library, 16 MiB per GPU, held by every GPU the library runs on until
+ * of the library, 64 MiB per GPU, held by every GPU the library runs on until
  * the process ends, instead of the cache's own allocation. The array's
  * address is looked up, and its counters cleared, by the first
  * lf_cache_create on each device; the counters are back at zero after every
@@ -229,13 +229,17 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
  * undefined results. Serialise them on one stream.
  *
  * Errors: those of lf_decode_step, and LF_ERR_SCRATCH (nothing queued) when
- * the launch's workspace does not fit in the array: split-K launches need
- * pairs * splits * (2G + G*head_dim) * 4 bytes of partial states plus
- * pairs * slots_padded * G * 4 bytes of logits (EVICT mode); LF_SCOPE_SEQUENCE
- * needs pairs * (slots_padded + 1) * 4 bytes, with each region rounded up to
- * 256 bytes, in 16 MiB - 64 KiB; split-K launches also need pairs <= 8192 and
- * LF_SCOPE_SEQUENCE batch <= 8192. One-workgroup-per-pair launches of
- * LF_SCOPE_KV_HEAD use no workspace and always fit. */
+ * the launch's workspace does not fit in the array. The regions, each
+ * rounded up to 256 bytes, must fit in 64 MiB - 64 KiB:
+ *   - split-K launches need pairs * splits * (2G + G*head_dim) * 4 bytes of
+ *     partial states, plus pairs * slots_padded * G * 4 bytes of logits
+ *     (EVICT mode);
+ *   - stream launches (lf_cache_set_stream) need the same with the cut pairs
+ *     for `pairs` and 16 partial states per cut pair for `splits`;
+ *   - LF_SCOPE_SEQUENCE needs pairs * (slots_padded + 1) * 4 bytes.
+ * Split-K and stream launches also need at most 8192 pairs with a
+ * workspace row, and LF_SCOPE_SEQUENCE batch <= 8192. Launches of whole
+ * pairs with LF_SCOPE_KV_HEAD use no workspace and always fit. */
 lf_status lf_decode_step_noalloc(lf_cache* c, int32_t layer, const void* q, const void* k_new,
                                  const void* v_new, void* out, int32_t* evicted_slot,
                                  void* stream);
@@ -296,19 +300,42 @@ lf_status lf_cache_set_waves(lf_cache* c, int32_t waves);
  * of the scores. Errors: LF_ERR_INVALID_ARG for other values. */
 lf_status lf_cache_set_loop(lf_cache* c, int32_t loop);
 
-/* Launch-shape tuning (as above): workgroups of a one-workgroup-per-pair
- * launch of the evicting main path (4 waves per workgroup, same-step order,
- * one victim per KV head). By default such a launch runs one workgroup per
- * pair. The exception is a launch whose pairs would take two rounds of the
- * workgroups resident on the device at once, the second 40-85% full; it
- * runs ceil(pairs / 2) workgroups, each taking pairs w and w + grid in turn,
- * so that no round runs on part of the device. A positive
- * `workgroups` caps every such launch at that many workgroups. -1 always
- * keeps one workgroup per pair, and 0 restores the automatic choice. Other
- * launches (split-K, 8 waves, the variants, FULL mode) ignore it. Every
- * pair is computed exactly as with one workgroup per pair, so results are
- * bit-identical. Errors: LF_ERR_INVALID_ARG for values below -1. */
+/* Launch-shape tuning (as above): how a launch of the evicting main path
+ * with no split (same-step order, one victim per KV head) spreads its pairs
+ * over workgroups. With R workgroups resident on the device at once, the
+ * pairs take ceil(pairs / R) rounds of whole pairs, and a part-full last
+ * round leaves the device partly idle. R is the compute units for 8-wave
+ * workgroups, and twice that for 4-wave ones unless LDS allows only one. By
+ * default:
+ *   - just past one round (R < pairs <= 1.3 R): a stream launch of R
+ *     workgroups. Each takes its whole pair of the first round, then an
+ *     equal run (at least 16 tiles of 16 slots) of the remaining pairs'
+ *     tiles. A pair cut between workgroups is combined by the last of its
+ *     parts to finish, as in split-K. Just past the compute units this
+ *     uses 8-wave workgroups; just past two per compute unit, 4-wave ones.
+ *     The cache holds workspace for the cut pairs of these bands on a
+ *     256-CU device (up to 512 of them), and a launch is taken only if they
+ *     fit;
+ *   - two rounds of 4-wave workgroups with the second 40-85% full:
+ *     ceil(pairs / 2) workgroups, each taking two whole pairs in turn;
+ *   - otherwise one workgroup per pair.
+ * lf_cache_set_grid: a positive `workgroups` makes 4-wave launches take
+ * whole pairs in turn on that many workgroups; -1 always keeps one
+ * workgroup per pair (no stream launch either); 0 restores the automatic
+ * choice.
+ * lf_cache_set_stream: a positive `tiles` streams every pair with that many
+ * tiles per workgroup, raised where a pair would be cut into more parts than
+ * its workspace row holds; 0 restores the automatic choice. It takes effect
+ * only where the layer's workspace holds every pair: with a split-K
+ * workspace (below 256 pairs, then with lf_cache_set_splits 1), or where
+ * the stream rows cover the layer.
+ * Other launches (split-K, the variants, FULL mode) ignore both. Whole pairs
+ * in turn give the results of one workgroup per pair bit for bit; a stream
+ * launch differs only in float32 rounding of the cut pairs' outputs and
+ * scores, as split-K does. Errors: LF_ERR_INVALID_ARG for workgroups < -1
+ * or tiles < 0. */
 lf_status lf_cache_set_grid(lf_cache* c, int32_t workgroups);
+lf_status lf_cache_set_stream(lf_cache* c, int32_t tiles);
 
 /* Host-side copy of the fill levels of one layer (tokens held per pair: the
  * initial fill of LongFlow Guide, §Static Memory Pre-Allocation and In-Place

@@ -46,7 +46,9 @@ lf_status lf_probe_stream_read_timing(const void* buf, size_t bytes, int32_t wor
 /* One lf_decode_step (the same launch plan, kernels and results) that also
  * writes the timing record above for every workgroup of the launch.
  *   records      device [capacity][4] uint64
- *   workgroups   HOST out: the launch's workgroup count (pairs x splits)
+ *   workgroups   HOST out: the launch's workgroup count (pairs x splits;
+ *                fewer when workgroups take whole pairs in turn; up to twice
+ *                the compute units for a stream launch)
  * Errors: those of lf_decode_step, and LF_ERR_INVALID_ARG (nothing queued)
  * on NULL records or workgroups, or capacity below the workgroup count.
  * The records show how one launch spreads over the XCDs and CUs; they cost

@@ -115,7 +115,8 @@ def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
                  num_layers: int = 1, check_cache_every: int = 0,
                  splits: int = 0, order: str = "same_step", scope: str = "kv_head",
                  norm: str = "l1", recycle: Optional[dict] = None,
-                 waves: int = 0, loop: str = "auto", grid: int = 0) -> LockstepReport:
+                 waves: int = 0, loop: str = "auto", grid: int = 0,
+                 stream: int = 0) -> LockstepReport:
     """Run `steps` decode steps of one layer on the GPU and in the oracle."""
     import torch
     from decode_kv_cache_02_amd.native import LongFlowCache
@@ -132,6 +133,8 @@ def run_lockstep(wl: Workload, steps: int, pairs: Optional[Sequence] = None,
         cache.set_loop(loop)
     if grid:
         cache.set_grid(grid)
+    if stream:
+        cache.set_stream(stream)
     deferred = order == "deferred" and mode == "evict"
     try:
         ts = TokenStream(wl, layer=layer, seed_offset=seed_offset)

@@ -108,11 +108,11 @@ def test_noalloc_refuses_a_workspace_beyond_the_array():
     from decode_kv_cache_02_amd.native import LongFlowCache
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    # One victim per sequence over 256 sequences x 8 KV heads, B = 4096: the
-    # score vectors alone (2048 x 4096 x 4 bytes = 32 MiB) exceed the 16 MiB
+    # One victim per sequence over 640 sequences x 8 KV heads, B = 4096: the
+    # score vectors alone (5120 x 4160 x 4 bytes = 81 MiB) exceed the 64 MiB
     # array. The cache starts empty, so the step it refuses would append.
-    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=4096)
-    _say("noalloc refusal: 256 x 8 pairs, B = 4096, one victim per sequence")
+    wl = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=4096, batch=640)
+    _say("noalloc refusal: 640 x 8 pairs, B = 4096, one victim per sequence")
     cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
                           dtype=wl.dtype, scope="sequence")
     try:
