@@ -662,6 +662,12 @@ def suite(args):
         small = wl3.with_(batch=b)
         ms, nb, win = steady_state(small, steps, warmup)
         emit(f"llama8b_layer batch {b} (split-K)", small, ms, nb, windows=win, steps=steps)
+    # just past a round of resident workgroups: stream launches
+    for b, how in ((33, "256 workgroups of 8 waves, 8 pairs cut"),
+                   (65, "512 workgroups of 4 waves, 8 pairs cut")):
+        w = wl3.with_(batch=b)
+        ms, nb, win = steady_state(w, steps, warmup)
+        emit(f"llama8b_layer batch {b} (stream launch: {how})", w, ms, nb, windows=win, steps=steps)
     # 32-layer ragged stack at the batch where both caches fit 0.95 x 288 GB,
     # over the workload's 512-step window (fill levels advance through it)
     wl4 = WORKLOADS["llama8b_stack32_ragged"]
