@@ -138,10 +138,13 @@ int32_t stream_rows(const lf_config* c, int32_t max_splits) {
   if (max_splits > 1 || c->mode != LF_MODE_EVICT || c->order != LF_ORDER_SAME_STEP ||
       c->scope != LF_SCOPE_KV_HEAD || pairs <= lf::kStreamCusRef)
     return 0;
-  // just past one round of 8-wave (room = CUs) or 4-wave (2 CUs) workgroups
+  // just past one round of 8-wave workgroups (room = CUs), or past whole
+  // rounds of 4-wave ones (room = 2 CUs)
   int64_t rows = 0;
-  for (const int64_t room : {int64_t{lf::kStreamCusRef}, 2 * int64_t{lf::kStreamCusRef}})
-    if (pairs > room && pairs * 10 <= room * 13) rows = std::max(rows, pairs - room);
+  const int64_t cus = lf::kStreamCusRef;
+  if (pairs > cus && (pairs - cus) * 4 <= cus) rows = pairs - cus;
+  const int64_t cut = pairs % (2 * cus);
+  if (pairs > 2 * cus && cut * 4 <= 2 * cus) rows = std::max(rows, cut);
   return static_cast<int32_t>(std::min<int64_t>(rows, lf::kStreamRows));
 }
 
@@ -333,14 +336,15 @@ int32_t resident_4wave(const lf_cache* c, bool ilv) {
 // for one workgroup per pair. With R workgroups resident at once, P pairs
 // take ceil(P / R) rounds of whole pairs, and a part-full last round leaves
 // the device partly idle.
-//   - Just past one round (R < P <= 1.3 R): every workgroup takes its whole
-//     pair of the first round, then an equal run (at least kStreamMinTiles
-//     tiles) of the remaining pairs' tiles; pairs cut between workgroups
-//     combine their parts as split-K does. Just past one round of 8-wave
-//     workgroups (one per compute unit: cus < P <= 1.3 cus) the launch
-//     switches to 8 waves for this; past one round of 4-wave workgroups
-//     (2 cus < P <= 2.6 cus with two resident per compute unit) it keeps 4.
-//     Needs workspace rows for the cut pairs.
+//   - Just past k whole rounds (k R < P <= (k + 0.25) R): every workgroup
+//     takes its k whole pairs of those rounds in turn, then an equal run
+//     (at least kStreamMinTiles tiles) of the remaining pairs' tiles; pairs
+//     cut between workgroups combine their parts as split-K does. Just past
+//     one round of 8-wave workgroups (one per compute unit: cus < P <= 1.25
+//     cus) the launch switches to 8 waves for this; past k rounds of 4-wave
+//     workgroups (two per compute unit) it keeps 4. Needs workspace rows for
+//     the cut pairs. Measured on the Llama-8B layer, the gain falls from
+//     10-19% with a few cut pairs to nothing at 0.3 R.
 //   - Two rounds of 4-wave workgroups with the second 40-85% full:
 //     ceil(P / 2) workgroups taking two whole pairs each.
 //   - Otherwise one workgroup per pair.
@@ -382,24 +386,27 @@ lf::GridPlan plan_stream(const lf_cache* c, LaunchShape* shape, int32_t n_max) {
     }
     return g;
   }
-  // whole pairs for the first `room` workgroups, the rest cut into runs
-  auto past_one_round = [&](int64_t room) {
-    const int64_t cut = pairs - room;
-    if (cut <= 0 || cut > c->sk_rows || stride <= 1 || pairs * 10 > room * 13) return false;
+  // k whole rounds of `room` workgroups (each workgroup takes k whole pairs
+  // in turn), the remaining pairs cut into runs
+  auto past_whole_rounds = [&](int64_t room, int64_t max_rounds) {
+    const int64_t k = pairs / room;
+    const int64_t cut = pairs - k * room;
+    if (k < 1 || k > max_rounds || cut <= 0 || cut > c->sk_rows || stride <= 1 || cut * 4 > room)
+      return false;
     const int64_t run = cut * tn;
     const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(room, run / lf::kStreamMinTiles));
-    stream(room, std::max<int64_t>((run + wgs - 1) / wgs, lf::kStreamMinTiles), room);
+    stream(k * room, std::max<int64_t>((run + wgs - 1) / wgs, lf::kStreamMinTiles), room);
     return true;
   };
   const size_t dyn = lf::decode_lds_bytes(geo, shape->ilv);
   if (c->forced_waves == 0 && dyn + lf::decode_static_lds_bytes(geo, 8) <= c->lds_limit &&
-      past_one_round(c->cus)) {
+      past_whole_rounds(c->cus, 1)) {
     shape->waves = 8;
     return g;
   }
   const int64_t room = static_cast<int64_t>(resident_4wave(c, shape->ilv)) * c->cus;
   if (room <= c->cus || pairs <= c->cus) return g;
-  if (past_one_round(room)) return g;
+  if (past_whole_rounds(room, pairs)) return g;
   const int64_t last = pairs - room;  // pairs of a second round
   if (last > 0 && last <= room && last * 10 >= room * 4 && last * 20 <= room * 17) {
     g.grid = static_cast<int>((pairs + 1) / 2);

@@ -307,15 +307,15 @@ lf_status lf_cache_set_loop(lf_cache* c, int32_t loop);
  * round leaves the device partly idle. R is the compute units for 8-wave
  * workgroups, and twice that for 4-wave ones unless LDS allows only one. By
  * default:
- *   - just past one round (R < pairs <= 1.3 R): a stream launch of R
- *     workgroups. Each takes its whole pair of the first round, then an
- *     equal run (at least 16 tiles of 16 slots) of the remaining pairs'
- *     tiles. A pair cut between workgroups is combined by the last of its
- *     parts to finish, as in split-K. Just past the compute units this
- *     uses 8-wave workgroups; just past two per compute unit, 4-wave ones.
- *     The cache holds workspace for the cut pairs of these bands on a
- *     256-CU device (up to 512 of them), and a launch is taken only if they
- *     fit;
+ *   - just past k whole rounds (k R < pairs <= (k + 0.25) R): a stream
+ *     launch of R workgroups. Each takes its k whole pairs of those rounds
+ *     in turn, then an equal run (at least 16 tiles of 16 slots) of the
+ *     remaining pairs' tiles. A pair cut between workgroups is combined by
+ *     the last of its parts to finish, as in split-K. Just past one round of
+ *     the compute units this uses 8-wave workgroups; past rounds of two per
+ *     compute unit, 4-wave ones. The cache holds workspace for the cut pairs
+ *     of these bands on a 256-CU device (up to 512 of them), and a launch
+ *     is taken only if they fit;
  *   - two rounds of 4-wave workgroups with the second 40-85% full:
  *     ceil(pairs / 2) workgroups, each taking two whole pairs in turn;
  *   - otherwise one workgroup per pair.
