@@ -352,15 +352,27 @@ int32_t resident_4wave(const lf_cache* c, bool ilv) {
 // streams every pair with that many tiles per workgroup (no whole pairs
 // first); forced_grid > 0 takes whole pairs in turn on that many
 // workgroups; forced_grid < 0 keeps one workgroup per pair.
-lf::GridPlan plan_stream(const lf_cache* c, LaunchShape* shape, int32_t n_max) {
+// What plan_stream decides from, apart from the cache: the device, the
+// layer's workspace and the overrides (also the input of
+// lf_probe_stream_plan).
+struct StreamInputs {
+  int64_t pairs;
+  int32_t n_max;
+  int32_t cus;
+  int32_t resident4;   // resident 4-wave workgroups per CU
+  bool fits8;          // an 8-wave workgroup's LDS fits
+  int32_t rows;        // workspace rows for cut pairs
+  int32_t stride;      // partials per row
+  int32_t forced_stream, forced_grid, forced_waves;
+};
+
+lf::GridPlan stream_plan(const StreamInputs& in, bool* eight_waves) {
   lf::GridPlan g;
-  const lf::Geometry& geo = c->geo;
-  if (shape->splits != 1 || geo.mode != LF_MODE_EVICT || geo.order != 0 || geo.scope != 0 ||
-      c->forced_grid < 0)
-    return g;
-  const int64_t pairs = c->layer_pairs;
-  const int64_t tn = std::max<int64_t>(1, (static_cast<int64_t>(n_max) + 15) / 16);
-  const int64_t stride = c->sk_stride;
+  *eight_waves = false;
+  if (in.forced_grid < 0) return g;
+  const int64_t pairs = in.pairs;
+  const int64_t tn = std::max<int64_t>(1, (static_cast<int64_t>(in.n_max) + 15) / 16);
+  const int64_t stride = in.stride;
   // tiles per share so that no pair is cut into more than `stride` parts
   const int64_t q_min = stride > 1 ? (tn + stride - 2) / (stride - 1) : tn;
   auto stream = [&](int64_t first, int64_t q, int64_t grid_min) {
@@ -374,14 +386,13 @@ lf::GridPlan plan_stream(const lf_cache* c, LaunchShape* shape, int32_t n_max) {
     g.sk_stride = static_cast<int>(stride);
     g.grid = static_cast<int>(std::max<int64_t>(grid_min, g.sk_wgs));
   };
-  if (c->forced_stream > 0) {
-    if (pairs <= c->sk_rows && stride > 1) stream(0, c->forced_stream, 1);
+  if (in.forced_stream > 0) {
+    if (pairs <= in.rows && stride > 1) stream(0, in.forced_stream, 1);
     return g;
   }
-  if (shape->waves != 4) return g;
-  if (c->forced_grid > 0) {
-    if (c->forced_grid < pairs) {
-      g.grid = c->forced_grid;
+  if (in.forced_grid > 0) {
+    if (in.forced_grid < pairs) {
+      g.grid = in.forced_grid;
       g.sk_first = static_cast<int>(pairs);
     }
     return g;
@@ -391,27 +402,49 @@ lf::GridPlan plan_stream(const lf_cache* c, LaunchShape* shape, int32_t n_max) {
   auto past_whole_rounds = [&](int64_t room, int64_t max_rounds) {
     const int64_t k = pairs / room;
     const int64_t cut = pairs - k * room;
-    if (k < 1 || k > max_rounds || cut <= 0 || cut > c->sk_rows || stride <= 1 || cut * 4 > room)
+    if (k < 1 || k > max_rounds || cut <= 0 || cut > in.rows || stride <= 1 || cut * 4 > room)
       return false;
     const int64_t run = cut * tn;
     const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(room, run / lf::kStreamMinTiles));
     stream(k * room, std::max<int64_t>((run + wgs - 1) / wgs, lf::kStreamMinTiles), room);
     return true;
   };
-  const size_t dyn = lf::decode_lds_bytes(geo, shape->ilv);
-  if (c->forced_waves == 0 && dyn + lf::decode_static_lds_bytes(geo, 8) <= c->lds_limit &&
-      past_whole_rounds(c->cus, 1)) {
-    shape->waves = 8;
+  if (in.forced_waves == 0 && in.fits8 && past_whole_rounds(in.cus, 1)) {
+    *eight_waves = true;
     return g;
   }
-  const int64_t room = static_cast<int64_t>(resident_4wave(c, shape->ilv)) * c->cus;
-  if (room <= c->cus || pairs <= c->cus) return g;
+  const int64_t room = static_cast<int64_t>(in.resident4) * in.cus;
+  if (room <= in.cus || pairs <= in.cus) return g;
   if (past_whole_rounds(room, pairs)) return g;
   const int64_t last = pairs - room;  // pairs of a second round
   if (last > 0 && last <= room && last * 10 >= room * 4 && last * 20 <= room * 17) {
     g.grid = static_cast<int>((pairs + 1) / 2);
     g.sk_first = static_cast<int>(pairs);
   }
+  return g;
+}
+
+lf::GridPlan plan_stream(const lf_cache* c, LaunchShape* shape, int32_t n_max) {
+  const lf::Geometry& geo = c->geo;
+  // one-workgroup-per-pair launches of 4 waves on the evicting main path
+  // (a forced stream launch also takes an 8-wave shape)
+  if (shape->splits != 1 || geo.mode != LF_MODE_EVICT || geo.order != 0 || geo.scope != 0 ||
+      (shape->waves != 4 && c->forced_stream == 0))
+    return lf::GridPlan{};
+  StreamInputs in;
+  in.pairs = c->layer_pairs;
+  in.n_max = n_max;
+  in.cus = c->cus;
+  in.resident4 = resident_4wave(c, shape->ilv);
+  in.fits8 = lf::decode_lds_bytes(geo, shape->ilv) + lf::decode_static_lds_bytes(geo, 8) <= c->lds_limit;
+  in.rows = c->sk_rows;
+  in.stride = c->sk_stride;
+  in.forced_stream = c->forced_stream;
+  in.forced_grid = c->forced_grid;
+  in.forced_waves = c->forced_waves;
+  bool eight = false;
+  const lf::GridPlan g = stream_plan(in, &eight);
+  if (eight) shape->waves = 8;
   return g;
 }
 
@@ -786,6 +819,21 @@ lf_status lf_decode_step(lf_cache* c, int32_t layer, const void* q, const void* 
 lf_status lf_decode_step_noalloc(lf_cache* c, int32_t layer, const void* q, const void* k_new,
                                  const void* v_new, void* out, int32_t* evicted_slot, void* stream) {
   return decode_step(c, layer, q, k_new, v_new, out, evicted_slot, stream, true);
+}
+
+lf_status lf_probe_stream_plan(int64_t pairs, int32_t n_max, int32_t cus, int32_t resident4,
+                               int32_t fits8, int32_t rows, int32_t stride, int32_t forced_stream,
+                               int32_t forced_grid, int32_t* plan) {
+  if (!plan || pairs < 1 || n_max < 0 || cus < 1 || resident4 < 1 || rows < 0 || stride < 0)
+    return LF_ERR_INVALID_ARG;
+  const StreamInputs in{pairs, n_max, cus, resident4, fits8 != 0, rows, stride, forced_stream,
+                        forced_grid, 0};
+  bool eight = false;
+  const lf::GridPlan g = stream_plan(in, &eight);
+  const int32_t out[8] = {g.grid, g.sk_first, g.sk_pairs, g.sk_tiles, g.sk_q, g.sk_wgs, g.sk_stride,
+                          eight ? 8 : 4};
+  std::memcpy(plan, out, sizeof(out));
+  return LF_OK;
 }
 
 lf_status lf_probe_decode_timing(lf_cache* c, int32_t layer, const void* q, const void* k_new,

@@ -106,6 +106,10 @@ SIGNATURES = [
                                              ctypes.c_void_p, ctypes.c_void_p]),
     ("lf_probe_hbm_attributes", ctypes.c_int, [ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_int32)]),
+    ("lf_probe_stream_plan", ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_int32)]),
     ("lf_probe_stream_read_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     ("lf_probe_decode_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
@@ -310,6 +314,20 @@ def lf_probe_stream_read_timing(buf, workgroups: int, sink, records, stream=None
         ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel() * buf.element_size()),
         int(workgroups), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(records.data_ptr()),
         ctypes.c_void_p(_stream_ptr(stream))), "lf_probe_stream_read_timing")
+
+
+PLAN_FIELDS = ("grid", "sk_first", "sk_pairs", "sk_tiles", "sk_q", "sk_wgs", "sk_stride", "waves")
+
+
+def lf_probe_stream_plan(pairs: int, n_max: int, cus: int, resident4: int, fits8: bool, rows: int,
+                         stride: int, forced_stream: int = 0, forced_grid: int = 0) -> dict:
+    """The library's launch plan for an evicting main-path layer (host only)."""
+    out = (ctypes.c_int32 * 8)()
+    _check(load_library().lf_probe_stream_plan(int(pairs), int(n_max), int(cus), int(resident4),
+                                               int(bool(fits8)), int(rows), int(stride),
+                                               int(forced_stream), int(forced_grid), out),
+           "lf_probe_stream_plan")
+    return dict(zip(PLAN_FIELDS, list(out)))
 
 
 def lf_probe_decode_timing(handle: int, layer: int, q, k_new, v_new, out, evicted_slot, records,

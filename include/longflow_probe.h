@@ -66,6 +66,26 @@ lf_status lf_probe_decode_timing(lf_cache* c, int32_t layer, const void* q, cons
  * pointer; LF_ERR_HIP if the runtime cannot report either attribute. */
 lf_status lf_probe_hbm_attributes(int32_t* mem_clock_khz, int32_t* bus_width_bits);
 
+/* The launch plan that lf_decode_step makes for a layer of the evicting
+ * main path with no split (lf_cache_set_grid and lf_cache_set_stream,
+ * longflow.h), from its inputs alone: host only, no device needed.
+ *   pairs          pairs of the layer
+ *   n_max          tokens of its longest pair
+ *   cus            compute units; resident4: 4-wave workgroups resident
+ *                  per compute unit; fits8: an 8-wave workgroup's LDS fits
+ *   rows, stride   the layer's workspace rows for cut pairs, and partial
+ *                  states per row
+ *   forced_stream, forced_grid   the overrides (0: automatic)
+ *   plan           HOST out int32[8]: workgroups (0: one per pair), whole
+ *                  pairs taken in turn first (pairs [0, sk_first)), cut
+ *                  pairs (sk_pairs), tiles per pair, tiles per workgroup
+ *                  run, workgroups with a run, partial states per row,
+ *                  and waves per workgroup (4 or 8)
+ * Errors: LF_ERR_INVALID_ARG on a NULL plan or a count out of range. */
+lf_status lf_probe_stream_plan(int64_t pairs, int32_t n_max, int32_t cus, int32_t resident4,
+                               int32_t fits8, int32_t rows, int32_t stride, int32_t forced_stream,
+                               int32_t forced_grid, int32_t* plan);
+
 #ifdef __cplusplus
 }
 #endif
