@@ -3,7 +3,10 @@ multi-layer model step) replays bit-identically to the same calls made
 eagerly on a twin cache, replay after replay, with eager work (input copies,
 snapshots, synchronisation) between the replays. The step queues only kernel
 launches (no memset, no host synchronisation), and its cross-workgroup
-counters are reset by the kernel itself, so it can be captured.
+counters are reset by the kernel itself, so it can be captured. The shapes
+cover one workgroup per pair (Llama-8B layer at batch 8), split-K (64 pairs
+of one KV head), a stream launch with cut pairs (520 pairs) and two whole
+pairs per workgroup (816 pairs).
 """
 import numpy as np
 import pytest
@@ -23,7 +26,7 @@ def _dev(x, dtype):
     return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
 
 
-@pytest.mark.parametrize("shape", ["llama_batch8", "tp8_split"])
+@pytest.mark.parametrize("shape", ["llama_batch8", "tp8_split", "stream_b65", "units_b102"])
 def test_graph_replay_matches_eager(shape):
     import torch
     if not torch.cuda.is_available():
@@ -32,9 +35,15 @@ def test_graph_replay_matches_eager(shape):
     if shape == "llama_batch8":
         wl = WORKLOADS["llama8b_layer"].with_(batch=8, prefill=3277)
         layers = 3
-    else:   # 64 pairs of one KV head: split-K launch with counters
+    elif shape == "tp8_split":   # 64 pairs of one KV head: split-K launch with counters
         wl = WORKLOADS["llama8b_layer"].with_(batch=64, num_q_heads=4, num_kv_heads=1,
                                               prefill=3277)
+        layers = 2
+    elif shape == "stream_b65":  # 520 pairs: stream launch, 8 cut pairs with counters
+        wl = WORKLOADS["llama8b_layer"].with_(batch=65, budget=512, prefill=512)
+        layers = 2
+    else:                        # 816 pairs: two whole pairs per workgroup
+        wl = WORKLOADS["llama8b_layer"].with_(batch=102, budget=512, prefill=512)
         layers = 2
     _say(f"graph capture, {shape}: {layers} layers, 12 replays")
     caches = [LongFlowCache(layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
