@@ -94,6 +94,7 @@ def parse_args():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--suite-part", default="", help=argparse.SUPPRESS)
     ap.add_argument("--suite", action="store_true",
                     help="measure every workload shape (one JSON line each) instead of the bench line")
     ap.add_argument("--wg-timing", action="store_true",
@@ -602,9 +603,28 @@ def batch_gain(wl, model_steps):
         yield w, ms, nb, win, extra
 
 
+SUITE_PARTS = ("tiny", "qwen06", "llama", "generation", "variants", "churn", "small", "ragged",
+               "gain", "qwen_b512", "qwen_b1024", "qwen_b2048", "qwen_b4096", "qwen_graph")
+
+
 def suite(args):
     """One JSON line per workload shape (steady state unless stated). Lines
-    timed in windows report the median of 5 windows and every window."""
+    timed in windows report the median of 5 windows and every window. Each
+    group of lines runs in a child process of its own, so no measurement
+    inherits another's allocations; this process never touches the GPU."""
+    import subprocess
+    for part in SUITE_PARTS:
+        cmd = [sys.executable, "-u", os.path.abspath(__file__), "--suite-part", part,
+               "--steps", str(args.steps)]
+        proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, text=True)
+        for line in proc.stdout:
+            print(line, end="", flush=True)
+        if proc.wait() != 0:
+            raise RuntimeError(f"suite part {part} failed with status {proc.returncode}")
+
+
+def suite_part(part, args):
+    """One group of suite lines (see suite)."""
     from decode_kv_cache_02_amd.native import lf_cache_bytes, make_config
     from decode_kv_cache_02_amd.synth import WORKLOADS, TokenStream
 
@@ -622,84 +642,100 @@ def suite(args):
         print(json.dumps(line), flush=True)
 
     steps, warmup = min(args.steps, 300), 20
-    wl1 = WORKLOADS["tiny_f32"]
-    e_ms, g_ms = tiny_latency(wl1)
-    nb1 = wl1.num_kv_heads * algorithmic_bytes_per_pair(wl1.budget, wl1.group, wl1.head_dim, 4, True)
-    emit("tiny_f32 (launch-latency bound), one call per step", wl1, e_ms, nb1)
-    emit("tiny_f32 (launch-latency bound), 64 steps per HIP graph replay", wl1, g_ms, nb1)
-    wl2 = WORKLOADS["qwen3_0p6b_layer"]
-    ms, nb, win = steady_state(wl2, steps, warmup)
-    emit("qwen3_0p6b_layer", wl2, ms, nb, windows=win, steps=steps)
     wl3 = WORKLOADS["llama8b_layer"]
-    for fill in (512, 1638, 3000):
-        ms, nb, win = steady_state(wl3, steps, warmup, fill=fill)
-        emit(f"llama8b_layer fill {fill} (appending)", wl3, ms, nb, windows=win, steps=steps)
-    ms, nb, win = steady_state(wl3, steps, warmup)
-    emit("llama8b_layer steady state", wl3, ms, nb, windows=win, steps=steps)
-    # a whole 16k-token generation from a 512-token prompt, LongFlow vs full-KV
-    ms_lf, nb_lf = trajectory(wl3, 16384, 512, "evict")
-    ms_fk, nb_fk = trajectory(wl3, 16384, 512, "full")
-    emit("llama8b_layer whole generation: prompt 512 + 16384 tokens, LongFlow", wl3, ms_lf, nb_lf,
-         extra={"fill_steps": wl3.budget - 512}, steps=16384)
-    emit("llama8b_layer whole generation: prompt 512 + 16384 tokens, full-KV", wl3, ms_fk, nb_fk,
-         extra={"speedup_of_longflow": ms_fk / ms_lf}, steps=16384)
-    for label, kw in (("deferred order (the blog engine's)", dict(order="deferred")),
-                      ("one victim per sequence", dict(scope="sequence")),
-                      ("one victim per sequence, deferred order", dict(scope="sequence", order="deferred")),
-                      ("l2 score", dict(norm="l2"))):
-        ms, nb, win = steady_state(wl3, steps, warmup, **kw)
-        emit(f"llama8b_layer steady state, {label}", wl3, ms, nb, extra={"variant": kw},
-             windows=win, steps=steps)
-    ms, nb = churn(wl3, min(steps, 256), warmup)
-    emit("llama8b_layer churn: 4 sequences recycled every 16 steps (512-token prompts)", wl3, ms, nb,
-         extra={"note": "reset + prefill inside the timed window; bytes include the prompts"},
-         steps=min(steps, 256))
-    shard = wl3.with_(num_q_heads=4, num_kv_heads=1)
-    ms, nb, win = steady_state(shard, steps, warmup)
-    emit("llama8b_layer tp8 shard (1 KV head per GPU)", shard, ms, nb, windows=win, steps=steps)
-    # small batches: fewer pairs than CUs, so every launch is split-K
-    for b in (1, 4, 16):
-        small = wl3.with_(batch=b)
-        ms, nb, win = steady_state(small, steps, warmup)
-        emit(f"llama8b_layer batch {b} (split-K)", small, ms, nb, windows=win, steps=steps)
-    # just past a round of resident workgroups: stream launches
-    for b, how in ((33, "256 workgroups of 8 waves, 8 pairs cut"),
-                   (65, "512 workgroups of 4 waves, 8 pairs cut")):
-        w = wl3.with_(batch=b)
-        ms, nb, win = steady_state(w, steps, warmup)
-        emit(f"llama8b_layer batch {b} (stream launch: {how})", w, ms, nb, windows=win, steps=steps)
-    # 32-layer ragged stack at the batch where both caches fit 0.95 x 288 GB,
-    # over the workload's 512-step window (fill levels advance through it)
-    wl4 = WORKLOADS["llama8b_stack32_ragged"]
-    cfg_c = make_config(32, 1, 32, 8, 128, wl4.budget)
-    cfg_f = make_config(32, 1, 32, 8, 128, 16384 + 512 + 64, mode="full")
-    per_seq = lf_cache_bytes(cfg_c) + lf_cache_bytes(cfg_f)
-    batch = int(0.95 * 288e9 // per_seq)
-    wl4 = wl4.with_(batch=batch)
-    offsets = TokenStream(wl4).start_offsets()
-    ms, nb, win = steady_state(wl4, wl4.steps, 5, layers=32,
-                               ragged=np.minimum(offsets, wl4.budget), seed=4)
-    emit("llama8b_stack32_ragged LongFlow", wl4, ms, nb, 32,
-         {"batch_rule": "largest batch with both caches in 0.95 x 288 GB",
-          "evicting_seqs": int(np.sum(offsets >= wl4.budget))}, windows=win, steps=wl4.steps)
-    ms, nb, win = steady_state(wl4, wl4.steps, 2, layers=32, mode="full",
-                               capacity=16384 + 512 + 64, ragged=offsets, seed=4)
-    emit("llama8b_stack32_ragged full-KV", wl4, ms, nb, 32, windows=win, steps=wl4.steps)
-    for w, ms, nb, win, extra in batch_gain(wl4, 50):
-        emit(f"llama8b_stack32_ragged {extra.pop('method')} at its own largest batch", w, ms, nb, 32,
-             extra, windows=win, steps=50)
-    # Qwen3-8B stack at every budget of the sweep, every pair full: 512 model
-    # steps each (of the workload's 16,384; the GPU time of a suite run bounds
-    # the window)
     wl5 = WORKLOADS["qwen3_8b_stack36_ties"]
-    for budget in (512, 1024, 2048, 4096):
+
+    def ragged_stack():
+        # 32-layer ragged stack at the batch where both caches fit 0.95 x 288 GB
+        wl4 = WORKLOADS["llama8b_stack32_ragged"]
+        cfg_c = make_config(32, 1, 32, 8, 128, wl4.budget)
+        cfg_f = make_config(32, 1, 32, 8, 128, 16384 + 512 + 64, mode="full")
+        per_seq = lf_cache_bytes(cfg_c) + lf_cache_bytes(cfg_f)
+        return wl4.with_(batch=int(0.95 * 288e9 // per_seq))
+
+    if part == "tiny":
+        wl1 = WORKLOADS["tiny_f32"]
+        e_ms, g_ms = tiny_latency(wl1)
+        nb1 = wl1.num_kv_heads * algorithmic_bytes_per_pair(wl1.budget, wl1.group, wl1.head_dim, 4, True)
+        emit("tiny_f32 (launch-latency bound), one call per step", wl1, e_ms, nb1)
+        emit("tiny_f32 (launch-latency bound), 64 steps per HIP graph replay", wl1, g_ms, nb1)
+    elif part == "qwen06":
+        wl2 = WORKLOADS["qwen3_0p6b_layer"]
+        ms, nb, win = steady_state(wl2, steps, warmup)
+        emit("qwen3_0p6b_layer", wl2, ms, nb, windows=win, steps=steps)
+    elif part == "llama":
+        for fill in (512, 1638, 3000):
+            ms, nb, win = steady_state(wl3, steps, warmup, fill=fill)
+            emit(f"llama8b_layer fill {fill} (appending)", wl3, ms, nb, windows=win, steps=steps)
+        ms, nb, win = steady_state(wl3, steps, warmup)
+        emit("llama8b_layer steady state", wl3, ms, nb, windows=win, steps=steps)
+    elif part == "generation":
+        # a whole 16k-token generation from a 512-token prompt, LongFlow vs full-KV
+        ms_lf, nb_lf = trajectory(wl3, 16384, 512, "evict")
+        ms_fk, nb_fk = trajectory(wl3, 16384, 512, "full")
+        emit("llama8b_layer whole generation: prompt 512 + 16384 tokens, LongFlow", wl3, ms_lf, nb_lf,
+             extra={"fill_steps": wl3.budget - 512}, steps=16384)
+        emit("llama8b_layer whole generation: prompt 512 + 16384 tokens, full-KV", wl3, ms_fk, nb_fk,
+             extra={"speedup_of_longflow": ms_fk / ms_lf}, steps=16384)
+    elif part == "variants":
+        for label, kw in (("deferred order (the blog engine's)", dict(order="deferred")),
+                          ("one victim per sequence", dict(scope="sequence")),
+                          ("one victim per sequence, deferred order", dict(scope="sequence", order="deferred")),
+                          ("l2 score", dict(norm="l2"))):
+            ms, nb, win = steady_state(wl3, steps, warmup, **kw)
+            emit(f"llama8b_layer steady state, {label}", wl3, ms, nb, extra={"variant": kw},
+                 windows=win, steps=steps)
+    elif part == "churn":
+        ms, nb = churn(wl3, min(steps, 256), warmup)
+        emit("llama8b_layer churn: 4 sequences recycled every 16 steps (512-token prompts)", wl3, ms, nb,
+             extra={"note": "reset + prefill inside the timed window; bytes include the prompts"},
+             steps=min(steps, 256))
+    elif part == "small":
+        shard = wl3.with_(num_q_heads=4, num_kv_heads=1)
+        ms, nb, win = steady_state(shard, steps, warmup)
+        emit("llama8b_layer tp8 shard (1 KV head per GPU)", shard, ms, nb, windows=win, steps=steps)
+        # small batches: fewer pairs than CUs, so every launch is split-K
+        for b in (1, 4, 16):
+            small = wl3.with_(batch=b)
+            ms, nb, win = steady_state(small, steps, warmup)
+            emit(f"llama8b_layer batch {b} (split-K)", small, ms, nb, windows=win, steps=steps)
+        # just past a round of resident workgroups: stream launches
+        for b, how in ((33, "256 workgroups of 8 waves, 8 pairs cut"),
+                       (65, "512 workgroups of 4 waves, 8 pairs cut")):
+            w = wl3.with_(batch=b)
+            ms, nb, win = steady_state(w, steps, warmup)
+            emit(f"llama8b_layer batch {b} (stream launch: {how})", w, ms, nb, windows=win, steps=steps)
+    elif part == "ragged":
+        # over the workload's 512-step window (fill levels advance through it)
+        wl4 = ragged_stack()
+        offsets = TokenStream(wl4).start_offsets()
+        ms, nb, win = steady_state(wl4, wl4.steps, 5, layers=32,
+                                   ragged=np.minimum(offsets, wl4.budget), seed=4)
+        emit("llama8b_stack32_ragged LongFlow", wl4, ms, nb, 32,
+             {"batch_rule": "largest batch with both caches in 0.95 x 288 GB",
+              "evicting_seqs": int(np.sum(offsets >= wl4.budget))}, windows=win, steps=wl4.steps)
+        ms, nb, win = steady_state(wl4, wl4.steps, 2, layers=32, mode="full",
+                                   capacity=16384 + 512 + 64, ragged=offsets, seed=4)
+        emit("llama8b_stack32_ragged full-KV", wl4, ms, nb, 32, windows=win, steps=wl4.steps)
+    elif part == "gain":
+        for w, ms, nb, win, extra in batch_gain(ragged_stack(), 50):
+            emit(f"llama8b_stack32_ragged {extra.pop('method')} at its own largest batch", w, ms, nb, 32,
+                 extra, windows=win, steps=50)
+    elif part.startswith("qwen_b"):
+        # Qwen3-8B stack at one budget of the sweep, every pair full: 512 model
+        # steps (of the workload's 16,384; the GPU time of a suite run bounds
+        # the window)
+        budget = int(part[len("qwen_b"):])
         w = wl5.with_(budget=budget)
         ms, nb, win = steady_state(w, 512, 3, layers=36, seed=5)
         emit(f"qwen3_8b_stack36 B={budget}", w, ms, nb, 36, windows=win, steps=512)
-    w = wl5.with_(budget=512)
-    ms, nb, win = stack_graph(w, 36, 512, seed=5)
-    emit("qwen3_8b_stack36 B=512, one HIP graph per model step", w, ms, nb, 36, windows=win,
-         steps=512)
+    elif part == "qwen_graph":
+        w = wl5.with_(budget=512)
+        ms, nb, win = stack_graph(w, 36, 512, seed=5)
+        emit("qwen3_8b_stack36 B=512, one HIP graph per model step", w, ms, nb, 36, windows=win,
+             steps=512)
+    else:
+        raise ValueError(f"unknown suite part {part}")
 
 
 TICK_US = 0.01          # the device's constant clock (s_memrealtime): 100 MHz
@@ -814,12 +850,16 @@ def main():
         torch.cuda.set_device(0)
         wg_timing(args)
         return
-    if args.suite:
-        # the oracle lines first: their workers are forked before any GPU use
-        if not args.no_cpu_baseline:
-            cpu_suite(min(args.cpu_seconds, 6.0))
+    if args.suite_part:
         import torch
         torch.cuda.set_device(0)
+        suite_part(args.suite_part, args)
+        return
+    if args.suite:
+        # the oracle lines first (their workers are forked); this process
+        # never touches the GPU, each group of GPU lines runs in a child
+        if not args.no_cpu_baseline:
+            cpu_suite(min(args.cpu_seconds, 6.0))
         suite(args)
         return
     if args.gpus != 1:
