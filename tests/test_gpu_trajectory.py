@@ -19,9 +19,10 @@ slot, and the pairs' cache regions every 1024 steps.
     all checked). The planned split count grows with the cache (2 splits at
     512 slots; 4 and 12 once it is full), so the trajectory crosses launch
     shapes as well as the fill -> evict boundary.
-  * A stream launch over the Llama-8B layer's whole trajectory: batch 65
-    (520 pairs, 8 of them cut between workgroups every step), four cut and
-    four whole pairs checked.
+  * Stream launches over the Llama-8B layer's whole trajectory: batch 65
+    (520 pairs, 4-wave workgroups) and batch 33 (264 pairs, 8-wave), 8 pairs
+    cut between workgroups every step; four cut and four whole pairs
+    checked.
   * The full-KV baseline growing past 16k tokens (14,976 -> 16,896, the
     Llama-8B layer at batch 8: split-K, each split streaming its ~4k slots
     in 2048-slot LDS chunks).
@@ -102,13 +103,16 @@ def test_llama8b_batch1_whole_trajectory():
     _check_fill_then_evict(wl, _run(wl, wl.steps, wl.prefill, seed=1))
 
 
-def test_llama8b_batch65_stream_whole_trajectory():
-    # 520 pairs, 8 past the 512 resident 4-wave workgroups: every step is a
-    # stream launch whose last 8 pairs (sequence 64) are cut into parts and
-    # combined like split-K, through the fill, the interleaved -> phased
-    # switch at 1024 slots and eviction. Four cut pairs, four whole ones.
-    wl = WORKLOADS["llama8b_layer"].with_(batch=65)
-    sampled = [(0, 0), (17, 3), (40, 6), (63, 7), (64, 0), (64, 3), (64, 5), (64, 7)]
+@pytest.mark.parametrize("batch", [65, 33])
+def test_llama8b_stream_launch_whole_trajectory(batch):
+    # Batch 65: 520 pairs, 8 past the 512 resident 4-wave workgroups. Batch
+    # 33: 264 pairs, 8 past one 8-wave workgroup per compute unit. Every step
+    # is a stream launch whose last 8 pairs (the last sequence) are cut into
+    # parts and combined like split-K, through the fill, the interleaved ->
+    # phased switch at 1024 slots and eviction. Four cut pairs, four whole.
+    wl = WORKLOADS["llama8b_layer"].with_(batch=batch)
+    last = batch - 1
+    sampled = [(0, 0), (11, 3), (last // 2, 6), (last - 1, 7), (last, 0), (last, 3), (last, 5), (last, 7)]
     _check_fill_then_evict(wl, _run(wl, wl.steps, wl.prefill, seed=9, sampled=sampled))
 
 
