@@ -20,9 +20,9 @@ slot, and the pairs' cache regions every 1024 steps.
     512 slots; 4 and 12 once it is full), so the trajectory crosses launch
     shapes as well as the fill -> evict boundary.
   * Stream launches over the Llama-8B layer's whole trajectory: batch 65
-    (520 pairs, 4-wave workgroups) and batch 33 (264 pairs, 8-wave), 8 pairs
-    cut between workgroups every step; four cut and four whole pairs
-    checked.
+    (520 pairs, 4-wave workgroups), batch 33 (264 pairs, 8-wave) and batch
+    129 (1032 pairs, two whole pairs per workgroup first), 8 pairs cut
+    between workgroups every step; four cut and four whole pairs checked.
   * The full-KV baseline growing past 16k tokens (14,976 -> 16,896, the
     Llama-8B layer at batch 8: split-K, each split streaming its ~4k slots
     in 2048-slot LDS chunks).
@@ -103,10 +103,11 @@ def test_llama8b_batch1_whole_trajectory():
     _check_fill_then_evict(wl, _run(wl, wl.steps, wl.prefill, seed=1))
 
 
-@pytest.mark.parametrize("batch", [65, 33])
+@pytest.mark.parametrize("batch", [65, 33, 129])
 def test_llama8b_stream_launch_whole_trajectory(batch):
     # Batch 65: 520 pairs, 8 past the 512 resident 4-wave workgroups. Batch
-    # 33: 264 pairs, 8 past one 8-wave workgroup per compute unit. Every step
+    # 33: 264 pairs, 8 past one 8-wave workgroup per compute unit. Batch 129:
+    # 1032 pairs, each workgroup takes two whole pairs first. Every step
     # is a stream launch whose last 8 pairs (the last sequence) are cut into
     # parts and combined like split-K, through the fill, the interleaved ->
     # phased switch at 1024 slots and eviction. Four cut pairs, four whole.
