@@ -99,6 +99,8 @@ def parse_args():
                     help="measure every workload shape (one JSON line each) instead of the bench line")
     ap.add_argument("--wg-timing", action="store_true",
                     help="per-workgroup timing records: how each launch spreads over the XCDs")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-workgroup phase records: where one launch's time goes")
     return ap.parse_args()
 
 
@@ -741,6 +743,80 @@ def suite_part(part, args):
 TICK_US = 0.01          # the device's constant clock (s_memrealtime): 100 MHz
 
 
+PHASES = ("first tile processed (interleaved) / K stream done (phased)", "stream done",
+          "split part published and drained", "split part's ticket back",
+          "last part: every part's max and sum in", "last part: score done", "in-place write reached")
+
+
+def summarize_phase_records(rec, ph):
+    """One launch's records ([wgs][4] and [wgs][8] int64,
+    lf_probe_decode_phases): per phase the median over the workgroups that
+    reached it, in us from the launch's first workgroup start; the last parts
+    of split pairs apart."""
+    rec = np.asarray(rec, dtype=np.int64)
+    ph = np.asarray(ph, dtype=np.int64)
+    t0 = rec[:, 0].min()
+    us = lambda x: float(np.median((x - t0) * TICK_US)) if len(x) else None
+    last = ph[:, 4] > 0                      # phase 5 reached: the last part of a pair
+    out = {"workgroups": int(len(rec)), "span_us": float((rec[:, 1].max() - t0) * TICK_US),
+           "last_start_us": float((rec[:, 0].max() - t0) * TICK_US), "phases": {}}
+    for k, name in enumerate(PHASES, start=1):
+        col = ph[:, k - 1]
+        if (col > 0).any():                  # phases 5-7 of a split launch: its last parts only
+            out["phases"][f"{k} {name}"] = us(col[col > 0])
+    out["end_us"] = us(rec[last, 1] if last.any() else rec[:, 1])
+    if last.any():
+        out["other_parts_end_us"] = us(rec[~last, 1])
+        out["last_parts"] = int(last.sum())
+    return out
+
+
+def phase_timing(args):
+    """Phase records (lf_probe_decode_phases, in the measurement build
+    liblongflow_phases.so) of the split-K shapes and two one-workgroup-per-pair
+    layers: where one launch's time goes. One JSON line per case, from the
+    launch with the median span of 7 (after warmup)."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache, lf_probe_decode_phases
+    from decode_kv_cache_02_amd.synth import WORKLOADS, device_prefill
+    w3 = WORKLOADS["llama8b_layer"]
+    cases = [("llama8b_layer tp8 shard (64 pairs, 4 splits x 8 waves)", w3.with_(num_q_heads=4, num_kv_heads=1)),
+             ("llama8b_layer batch 4 (32 pairs, 8 splits x 8 waves)", w3.with_(batch=4)),
+             ("llama8b_layer batch 1 (8 pairs, 12 splits x 8 waves)", w3.with_(batch=1)),
+             ("qwen3_0p6b_layer (256 pairs, one 8-wave workgroup each, interleaved)", WORKLOADS["qwen3_0p6b_layer"]),
+             ("llama8b_layer steady state (512 pairs, one 4-wave workgroup each, phased)", w3)]
+    for name, wl in cases:
+        cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                              dtype=wl.dtype)
+        try:
+            k, v = device_prefill(wl, wl.budget, seed=wl.cfg_id)
+            cache.prefill(0, k, v, np.full(wl.batch, wl.budget, dtype=np.int32))
+            del k, v
+            ring = make_ring(wl, wl.dtype)
+            out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=ring[0][0].dtype,
+                              device="cuda")
+            ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+            recs = torch.zeros((4096, 4), dtype=torch.int64, device="cuda")
+            phs = torch.zeros((4096, 8), dtype=torch.int64, device="cuda")
+            args_ = prepared_ring(cache, ring, out, ev)
+            for t in range(30):
+                cache.step_prepared(args_[t % RING][0])
+            runs = []
+            for t in range(7):
+                recs.zero_()
+                phs.zero_()
+                q, kn, vn = ring[t % RING]
+                n = lf_probe_decode_phases(cache.handle, 0, q, kn, vn, out, ev, recs, phs)
+                torch.cuda.synchronize()
+                runs.append(summarize_phase_records(recs[:n].cpu().numpy(), phs[:n].cpu().numpy()))
+            runs.sort(key=lambda r: r["span_us"])
+            r = runs[3]
+            r["case"] = name
+            print(json.dumps(r), flush=True)
+        finally:
+            cache.close()
+
+
 def summarize_wg_records(rec):
     """Per-XCD and per-CU view of one launch's timing records ([wgs][4]
     int64: start, end, XCC id | hardware id << 32, workgroup; 100 MHz)."""
@@ -849,6 +925,14 @@ def main():
         import torch
         torch.cuda.set_device(0)
         wg_timing(args)
+        return
+    if args.phases:
+        # the measurement build: the library with phase stamps compiled in
+        from decode_kv_cache_02_amd import native
+        native.load_library(native.PHASES_LIB_PATH)
+        import torch
+        torch.cuda.set_device(0)
+        phase_timing(args)
         return
     if args.suite_part:
         import torch

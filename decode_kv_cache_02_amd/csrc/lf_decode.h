@@ -319,6 +319,7 @@ struct DecodeParams {
   float* ws_nnorm;      // [batch][num_kv_heads]: every head's ||v_new||
   int32_t* seq_arrive;  // [batch]: KV heads done, back to 0 after every launch
   uint64_t* wg_clock;   // optional: per-workgroup timing records (null: none)
+  uint64_t* wg_phase;   // optional: per-workgroup phase stamps [workgroups][8] (null: none)
   const int32_t* order; // FULL mode: sequences in launch order, longest first
   // Stream launch (decode_kernel_stream): pairs [0, sk_first) whole, taken in
   // turn; pairs [sk_first, sk_first + sk_pairs) as one run of sk_pairs *
@@ -365,6 +366,22 @@ struct ClockRecord {
     }
   }
 };
+
+// Phase stamps: the constant clock at the end of phases 1..8 of the
+// workgroup's last unit (0: not reached), written by thread 0. 1: the
+// interleaved loop's first tile processed, or the phased loop's K stream
+// done; 2: the stream done; 3: a split's partial state published and
+// drained; 4: its ticket back; 5: the last split has every split's (m, l)
+// and the pair's max and sum; 6: the last split's score done; 7: the
+// in-place write reached. Only the measurement build (kPhaseStamps)
+// compiles the stamps in, and only into bfloat16 instances (the float32
+// ones have no registers to spare).
+template <typename T>
+__device__ __forceinline__ void phase_stamp(const DecodeParams& P, int tid, int k) {
+  if constexpr (kPhaseStamps && sizeof(T) == 2) {
+    if (P.wg_phase && tid == 0) P.wg_phase[8 * static_cast<size_t>(blockIdx.x) + k - 1] = __builtin_amdgcn_s_memrealtime();
+  }
+}
 
 // Cross-workgroup data of a split launch goes through relaxed agent-scope
 // atomic accesses: each is coherent across the XCDs on its own, so no
@@ -739,6 +756,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       load_set(kr2, vr2, t0 + kStep);
       process(kr, vr, t0);
       if (new_pending) {
+        phase_stamp<T>(P, tid, 1);
         new_token();
         new_pending = false;
       }
@@ -746,6 +764,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       process(kr2, vr2, t0 + kStep);
     }
     if (new_pending) new_token();
+    phase_stamp<T>(P, tid, 2);
 
     // ---------------- Combine the waves ----------------
     // Each wave's (m_w, sum, acc) goes to LDS; after one barrier every thread
@@ -897,11 +916,13 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
         }
       }
       drain_stores();
+      phase_stamp<T>(P, tid, 3);
       __syncthreads();
       if (tid == 0)
         sh_ticket = __hip_atomic_fetch_add(P.arrive + wsr, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
+      phase_stamp<T>(P, tid, 4);
     }
   } else {
     // ======== Phased loop: K stream, softmax and score, then V stream ========
@@ -1022,6 +1043,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
         qk_tiles(kr2, t0 + kStepA);
       }
 
+      phase_stamp<T>(P, tid, 1);
       // First V rows of the chunk go out before the softmax bookkeeping.
       const int nq = (cn + SPI - 1) / SPI;
       const uint32_t vbase = static_cast<uint32_t>(c0 + vsub) * kRowBytes + vcol * kBytes;
@@ -1165,6 +1187,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
     }
 
     if (lo >= hi) new_token();  // no slot for this workgroup: nothing streamed
+    phase_stamp<T>(P, tid, 2);
 
     // ---------------- Phase D: cross-wave output reduction ----------------
 #pragma unroll
@@ -1226,11 +1249,13 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
         ws_store(mine + G + tid, l_run[tid]);
       }
       drain_stores();
+      phase_stamp<T>(P, tid, 3);
       __syncthreads();
       if (tid == 0)
         sh_ticket = __hip_atomic_fetch_add(P.arrive + wsr, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
+      phase_stamp<T>(P, tid, 4);
     }
   }
 
@@ -1296,6 +1321,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       sh_gl[g] = L;
     }
     __syncthreads();
+    phase_stamp<T>(P, tid, 5);
     // Output values now, stores after the score: stores count in the same
     // counter as loads, so a store issued before the score's last loads
     // would have to be acknowledged before the score could finish.
@@ -1346,6 +1372,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
           }
         }
       }
+      phase_stamp<T>(P, tid, 6);
       wave_argmin(best, best_i);
       if (lane == 0) {
         sh_best_score[wave] = best;
@@ -1514,6 +1541,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       }
     }
   }
+  phase_stamp<T>(P, tid, 7);
   if (tid >= 2 * kRowLoads) return;
   if (slot >= P.budget) return;  // FULL cache already at capacity (the host prevents it)
   if (tid == 0) {
@@ -1636,6 +1664,7 @@ hipError_t launch_decode_t(const Geometry& geo, const LayerPtrs& L, const SplitW
   P.ws_logit = W.logit;
   P.arrive = W.arrive;
   P.wg_clock = W.wg_clock;
+  P.wg_phase = W.wg_phase;
   P.order = EVICT ? nullptr : L.order;
   P.sk_first = P.sk_pairs = P.sk_tiles = P.sk_q = P.sk_wgs = P.sk_stride = 0;
   const size_t lds = SPLIT ? decode_split_lds_bytes(geo, splits, ILV) : decode_lds_bytes(geo, ILV);

@@ -52,9 +52,19 @@ struct SplitWork {
   float* new_norm;    // [batch][num_kv_heads]: ||v_new|| of every head
   int32_t* seq_arrive;  // [batch]
   // Optional timing records, one per workgroup of the launch (null: none):
-  // [start, end, XCC id | hardware id << 32, workgroup index], uint64 each.
+  // [start, end, XCC id | hardware id << 32, workgroup index], uint64 each;
+  // optional phase stamps, eight uint64 per workgroup (lf_decode.h).
   uint64_t* wg_clock = nullptr;
+  uint64_t* wg_phase = nullptr;
 };
+
+// The measurement build (compiled with LF_PHASE_STAMPS=1, liblongflow_phases.so)
+// records when each phase of a decode step ends (lf_probe_decode_phases);
+// the library itself leaves those stamps out.
+#ifndef LF_PHASE_STAMPS
+#define LF_PHASE_STAMPS 0
+#endif
+constexpr bool kPhaseStamps = LF_PHASE_STAMPS != 0;
 
 constexpr int kMaxSplits = 16;
 // Split-K workspace sizing (no device query, so that lf_cache_bytes works

@@ -490,6 +490,7 @@ struct Timing {
   uint64_t* records;   // device [capacity][4]
   int64_t capacity;
   int32_t* workgroups; // host: the launch's workgroup count
+  uint64_t* phases;    // device [capacity][8], or null
 };
 
 // One decode step of one layer; `static_scratch` takes the launch's
@@ -517,6 +518,7 @@ lf_status decode_step(lf_cache* c, int32_t layer, const void* q, const void* k_n
   if (timing) {
     if (!timing->records || !timing->workgroups || timing->capacity < wgs) return LF_ERR_INVALID_ARG;
     work.wg_clock = timing->records;
+    work.wg_phase = timing->phases;
   }
   if (static_scratch) {
     char* base = static_cast<char*>(lf::scratch_ptr(c->device));
@@ -840,7 +842,17 @@ lf_status lf_probe_decode_timing(lf_cache* c, int32_t layer, const void* q, cons
                                  const void* v_new, void* out, int32_t* evicted_slot,
                                  uint64_t* records, int64_t capacity, int32_t* workgroups,
                                  void* stream) {
-  const Timing t{records, capacity, workgroups};
+  const Timing t{records, capacity, workgroups, nullptr};
+  return decode_step(c, layer, q, k_new, v_new, out, evicted_slot, stream, false, &t);
+}
+
+lf_status lf_probe_decode_phases(lf_cache* c, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, void* out, int32_t* evicted_slot,
+                                 uint64_t* records, uint64_t* phases, int64_t capacity,
+                                 int32_t* workgroups, void* stream) {
+  if (!lf::kPhaseStamps) return LF_ERR_UNSUPPORTED;  // the measurement build records phases
+  if (!phases) return LF_ERR_INVALID_ARG;
+  const Timing t{records, capacity, workgroups, phases};
   return decode_step(c, layer, q, k_new, v_new, out, evicted_slot, stream, false, &t);
 }
 

@@ -15,6 +15,9 @@ import numpy as np
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "liblongflow.so")
+# The measurement build (decode_kv_cache_02_amd/build.py --phases): the same
+# library with the phase stamps of lf_probe_decode_phases compiled in.
+PHASES_LIB_PATH = os.path.join(os.path.dirname(LIB_PATH), "liblongflow_phases.so")
 
 LF_OK = 0
 LF_ERR_INVALID_ARG = 1
@@ -116,6 +119,11 @@ SIGNATURES = [
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                                ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
+    ("lf_probe_decode_phases", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
+                                               ctypes.c_void_p]),
 ]
 
 _lib = None
@@ -330,10 +338,20 @@ def lf_probe_stream_plan(pairs: int, n_max: int, cus: int, resident4: int, fits8
     return dict(zip(PLAN_FIELDS, list(out)))
 
 
+def _check_records(records, width: int) -> None:
+    """The kernel writes `width` uint64 words per workgroup: the tensor must
+    be a contiguous int64 device tensor [capacity][width]."""
+    import torch
+    if (records.dtype != torch.int64 or records.dim() != 2 or records.shape[1] != width
+            or not records.is_contiguous() or not records.is_cuda):
+        raise ValueError(f"records must be a contiguous int64 device tensor [capacity][{width}]")
+
+
 def lf_probe_decode_timing(handle: int, layer: int, q, k_new, v_new, out, evicted_slot, records,
                            stream=None) -> int:
     """One lf_decode_step writing per-workgroup timing records (int64 device
     tensor [capacity][4]); returns the launch's workgroup count."""
+    _check_records(records, 4)
     wgs = ctypes.c_int32(0)
     _check(load_library().lf_probe_decode_timing(
         ctypes.c_void_p(handle), int(layer), ctypes.c_void_p(q.data_ptr()),
@@ -341,6 +359,27 @@ def lf_probe_decode_timing(handle: int, layer: int, q, k_new, v_new, out, evicte
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(evicted_slot.data_ptr()),
         ctypes.c_void_p(records.data_ptr()), int(records.shape[0]), ctypes.byref(wgs),
         ctypes.c_void_p(_stream_ptr(stream))), "lf_probe_decode_timing")
+    return int(wgs.value)
+
+
+def lf_probe_decode_phases(handle: int, layer: int, q, k_new, v_new, out, evicted_slot, records,
+                           phases, stream=None) -> int:
+    """lf_probe_decode_timing that also records when each phase of every
+    workgroup's step ended (int64 device tensors records [capacity][4] and
+    phases [capacity][8]; include/longflow_probe.h); returns the launch's
+    workgroup count."""
+    _check_records(records, 4)
+    _check_records(phases, 8)
+    if phases.shape[0] != records.shape[0]:
+        raise ValueError("records and phases must have the same capacity")
+    wgs = ctypes.c_int32(0)
+    _check(load_library().lf_probe_decode_phases(
+        ctypes.c_void_p(handle), int(layer), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(evicted_slot.data_ptr()),
+        ctypes.c_void_p(records.data_ptr()), ctypes.c_void_p(phases.data_ptr()),
+        int(records.shape[0]), ctypes.byref(wgs), ctypes.c_void_p(_stream_ptr(stream))),
+        "lf_probe_decode_phases")
     return int(wgs.value)
 
 

@@ -6,8 +6,10 @@
  * loads, non-temporal cache policy) and keeps an XOR of what it read, so a
  * benchmark can report the streaming-read bandwidth this GPU attains next to
  * the decode kernel's; the timing variants record when and where each
- * workgroup of a read or of a decode step ran; lf_probe_hbm_attributes
- * reports the device's own memory clock and bus width.
+ * workgroup of a read or of a decode step ran (and, with
+ * lf_probe_decode_phases, when each phase of its step ended);
+ * lf_probe_hbm_attributes reports the device's own memory clock and bus
+ * width.
  */
 #ifndef LONGFLOW_PROBE_H
 #define LONGFLOW_PROBE_H
@@ -57,6 +59,31 @@ lf_status lf_probe_decode_timing(lf_cache* c, int32_t layer, const void* q, cons
                                  const void* v_new, void* out, int32_t* evicted_slot,
                                  uint64_t* records, int64_t capacity, int32_t* workgroups,
                                  void* stream);
+
+/* lf_probe_decode_timing that also records when each phase of every
+ * workgroup's step ended: thread 0's constant clock at the end of phases 1
+ * to 8, eight uint64 values per workgroup (0 where the workgroup did not
+ * reach the phase). A workgroup that takes several pairs in turn records its
+ * last one.
+ *   1  interleaved loop: the first tile processed; phased loop: the K
+ *      stream done
+ *   2  the K and V stream done
+ *   3  split-K part: partial state (and raw logits) published, stores drained
+ *   4  split-K part: its arrival ticket back
+ *   5  last part of a pair: every part's max and sum in, the pair's formed
+ *   6  last part of a pair: the score of every slot done
+ *   7  the in-place write of the new token reached
+ *   8  unused (0)
+ *   records      device [capacity][4] uint64, as lf_probe_decode_timing
+ *   phases       device [capacity][8] uint64
+ * Caches of float32 leave the phase words 0 (their kernels record no
+ * phases). Other arguments and errors as lf_probe_decode_timing (a NULL
+ * phases is LF_ERR_INVALID_ARG). The stamps cost the decode kernel one
+ * uniform branch each when not requested. */
+lf_status lf_probe_decode_phases(lf_cache* c, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, void* out, int32_t* evicted_slot,
+                                 uint64_t* records, uint64_t* phases, int64_t capacity,
+                                 int32_t* workgroups, void* stream);
 
 /* The memory attributes the current device reports about itself
  * (hipDeviceAttributeMemoryClockRate in kHz, hipDeviceAttributeMemoryBusWidth

@@ -165,3 +165,22 @@ def test_variant_workspace_bytes(lib):
     shared = native.lf_cache_bytes(_cfg(scope="sequence"))
     extra = 64 * 8 * 3328 * 4 + 64 * 4 + 64 * 8 * 4   # scores, counters, new-token norms
     assert extra <= shared - base < extra + 3 * 256
+
+
+def test_timing_records_must_have_the_record_width():
+    """The timing probes write 4 uint64 words of record, and
+    lf_probe_decode_phases 8 words of phases, per workgroup: the binding
+    refuses any other tensor before the library is called."""
+    torch = pytest.importorskip("torch")
+    from decode_kv_cache_02_amd import native
+    for bad in (torch.zeros((8, 12), dtype=torch.int64), torch.zeros((8, 4), dtype=torch.int32),
+                torch.zeros((32,), dtype=torch.int64)):
+        with pytest.raises(ValueError):
+            native.lf_probe_decode_timing(0, 0, None, None, None, None, None, bad)
+        with pytest.raises(ValueError):
+            native.lf_probe_decode_phases(0, 0, None, None, None, None, None, bad,
+                                          torch.zeros((8, 8), dtype=torch.int64))
+    for bad in (torch.zeros((8, 4), dtype=torch.int64), torch.zeros((8, 8), dtype=torch.int32)):
+        with pytest.raises(ValueError):
+            native.lf_probe_decode_phases(0, 0, None, None, None, None, None,
+                                          torch.zeros((8, 4), dtype=torch.int64), bad)

@@ -106,3 +106,49 @@ def test_timing_records_of_a_read_and_of_a_decode_step():
     finally:
         for c in caches:
             c.close()
+
+
+def test_phase_probe_needs_the_measurement_build():
+    """The library leaves the phase stamps out: lf_probe_decode_phases says
+    LF_ERR_UNSUPPORTED and queues nothing."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_kv_cache_02_amd import native
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    cache = LongFlowCache(1, 2, 8, 2, 128, 64)
+    try:
+        q = torch.zeros((2, 8, 128), dtype=torch.bfloat16, device="cuda")
+        kv = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty_like(q)
+        ev = torch.empty((2, 2), dtype=torch.int32, device="cuda")
+        recs = torch.zeros((64, 4), dtype=torch.int64, device="cuda")
+        phs = torch.zeros((64, 8), dtype=torch.int64, device="cuda")
+        with pytest.raises(native.LongFlowError) as ei:
+            native.lf_probe_decode_phases(cache.handle, 0, q, kv, kv, out, ev, recs, phs)
+        assert ei.value.status == native.LF_ERR_UNSUPPORTED
+        torch.cuda.synchronize()
+        assert not recs.any() and not phs.any()
+        assert cache.fill_levels(0).tolist() == [0, 0]
+    finally:
+        cache.close()
+
+
+def test_phase_records_of_the_measurement_build():
+    """tests/phase_check.py, run in a process of its own on
+    liblongflow_phases.so: the probed step equals lf_decode_step on a twin
+    cache, and every workgroup's phase stamps are in order (a split launch,
+    and one workgroup per pair with either loop)."""
+    import subprocess
+    import sys
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_kv_cache_02_amd import native
+    import os
+    if not os.path.exists(native.PHASES_LIB_PATH):
+        pytest.fail(f"{native.PHASES_LIB_PATH} is missing: python -m decode_kv_cache_02_amd.build --phases")
+    script = os.path.join(os.path.dirname(os.path.abspath(__file__)), "phase_check.py")
+    res = subprocess.run([sys.executable, "-u", script], capture_output=True, text=True, timeout=240)
+    print(res.stdout[-4000:], res.stderr[-4000:], flush=True)
+    assert res.returncode == 0
