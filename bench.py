@@ -101,6 +101,9 @@ def parse_args():
                     help="per-workgroup timing records: how each launch spreads over the XCDs")
     ap.add_argument("--phases", action="store_true",
                     help="per-workgroup phase records: where one launch's time goes")
+    ap.add_argument("--stack-trajectory", type=int, default=0, metavar="B",
+                    help="time the 36-layer Qwen3-8B stack at budget B over its whole run "
+                         "(512-token prompt, 16,384 model steps)")
     return ap.parse_args()
 
 
@@ -490,6 +493,68 @@ def trajectory(wl, steps: int, prompt: int, mode: str):
                 n = min(n, wl.budget)
             nbytes += algorithmic_bytes_per_pair(n, wl.group, wl.head_dim, e, evict)
         return ms, nbytes * wl.batch * wl.num_kv_heads / steps
+    finally:
+        cache.close()
+
+
+def stack_trajectory(wl, layers: int, steps: int, prompt: int, segment: int = 1024):
+    """A whole generation through a `layers`-layer stack: every sequence of
+    every layer starts from a `prompt`-token prompt, then `steps` model steps
+    (one lf_decode_step per layer each) fill the cache to the budget and evict
+    from then on. One event pair per `segment` model steps, each printed to
+    stderr as it ends. Returns a dict: ms per model step over the whole run,
+    algorithmic bytes per model step, and the fill and evict phases apart."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import device_prefill
+    e = 2 if wl.dtype == "bf16" else 4
+    torch.cuda.empty_cache()
+    cache = LongFlowCache(layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                          dtype=wl.dtype)
+    try:
+        for layer in range(layers):
+            k, v = device_prefill(wl, prompt, seed=17 * 1000 + layer)
+            cache.prefill(layer, k, v, np.full(wl.batch, prompt, dtype=np.int32))
+            del k, v
+        ring = make_ring(wl, wl.dtype)
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=ring[0][0].dtype,
+                          device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        args = prepared_ring(cache, ring, out, ev, layers)
+        step = cache.step_prepared
+        torch.cuda.synchronize()
+        seg_ms = []
+        for s0 in range(0, steps, segment):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record()
+            for t in range(s0, min(steps, s0 + segment)):
+                for a in args[t % RING]:
+                    step(a)
+            end.record()
+            torch.cuda.synchronize()
+            seg_ms.append(start.elapsed_time(end))
+            print(f"[stack] B={wl.budget}: model steps {s0}-{min(steps, s0 + segment) - 1}: "
+                  f"{seg_ms[-1] / (min(steps, s0 + segment) - s0):.3f} ms each", file=sys.stderr, flush=True)
+        per_pair = [algorithmic_bytes_per_pair(min(prompt + t, wl.budget), wl.group, wl.head_dim, e,
+                                               prompt + t >= wl.budget) for t in range(steps)]
+        pairs = wl.batch * wl.num_kv_heads
+        fill_steps = max(0, min(steps, wl.budget - prompt))
+        total_ms = float(sum(seg_ms))
+        res = {"ms_per_model_step": total_ms / steps,
+               "bytes_per_model_step": float(np.mean(per_pair)) * pairs * layers,
+               "fill_steps": fill_steps, "segment_ms_per_model_step":
+               [round(m / min(segment, steps - i * segment), 4) for i, m in enumerate(seg_ms)]}
+        # phases apart, from the segments wholly inside each phase
+        fill_segs = [m / segment for i, m in enumerate(seg_ms) if (i + 1) * segment <= fill_steps]
+        evict_segs = [m / min(segment, steps - i * segment) for i, m in enumerate(seg_ms)
+                      if i * segment >= fill_steps]
+        if evict_segs:
+            res["evict_ms_per_model_step"] = float(np.mean(evict_segs))
+            res["evict_bytes_per_model_step"] = per_pair[-1] * pairs * layers
+        if fill_segs:
+            res["fill_ms_per_model_step"] = float(np.mean(fill_segs))
+        return res
     finally:
         cache.close()
 
@@ -925,6 +990,23 @@ def main():
         import torch
         torch.cuda.set_device(0)
         wg_timing(args)
+        return
+    if args.stack_trajectory:
+        import torch
+        torch.cuda.set_device(0)
+        from decode_kv_cache_02_amd.synth import WORKLOADS
+        w = WORKLOADS["qwen3_8b_stack36_ties"].with_(budget=args.stack_trajectory)
+        r = stack_trajectory(w, 36, w.steps, w.prefill)
+        ms = r["ms_per_model_step"]
+        line = {"workload": f"qwen3_8b_stack36 B={w.budget}, whole generation: prompt {w.prefill} + "
+                            f"{w.steps} model steps", "batch": w.batch, "layers": 36, "budget": w.budget,
+                "ms_per_model_step": ms, "tokens_per_s": w.batch / ms * 1e3,
+                "achieved_GBs": r["bytes_per_model_step"] / ms / 1e6,
+                "frac_of_peak": r["bytes_per_model_step"] / ms / 1e6 / HBM_PEAK_GBS}
+        line.update({k: v for k, v in r.items() if k != "ms_per_model_step"})
+        if "evict_ms_per_model_step" in r:
+            line["evict_achieved_GBs"] = r["evict_bytes_per_model_step"] / r["evict_ms_per_model_step"] / 1e6
+        print(json.dumps(line), flush=True)
         return
     if args.phases:
         # the measurement build: the library with phase stamps compiled in
