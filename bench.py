@@ -730,6 +730,11 @@ def suite_part(part, args):
         wl2 = WORKLOADS["qwen3_0p6b_layer"]
         ms, nb, win = steady_state(wl2, steps, warmup)
         emit("qwen3_0p6b_layer", wl2, ms, nb, windows=win, steps=steps)
+        # the workload's whole run: a full 1024-token prompt, 4096 evicting
+        # steps (5 consecutive windows; the mean of the windows is the run)
+        ms, nb, win = steady_state(wl2, wl2.steps, 0)
+        emit(f"qwen3_0p6b_layer whole run: {wl2.steps} evicting steps", wl2, float(np.mean(win)), nb,
+             windows=win, steps=wl2.steps)
     elif part == "llama":
         for fill in (512, 1638, 3000):
             ms, nb, win = steady_state(wl3, steps, warmup, fill=fill)
