@@ -101,6 +101,8 @@ def parse_args():
                     help="per-workgroup timing records: how each launch spreads over the XCDs")
     ap.add_argument("--phases", action="store_true",
                     help="per-workgroup phase records: where one launch's time goes")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="the Llama-8B layer at batches 1-256 with the automatic launch")
     ap.add_argument("--stack-trajectory", type=int, default=0, metavar="B",
                     help="time the 36-layer Qwen3-8B stack at budget B over its whole run "
                          "(512-token prompt, 16,384 model steps)")
@@ -559,6 +561,48 @@ def stack_trajectory(wl, layers: int, steps: int, prompt: int, segment: int = 10
         cache.close()
 
 
+SWEEP_BATCHES = (1, 2, 4, 8, 12, 16, 24, 31, 32, 33, 36, 40, 48, 56, 64, 65, 68, 72, 80, 88, 96,
+                 102, 112, 120, 127, 128, 129, 136, 144, 160, 192, 193, 200, 224, 256)
+
+
+def launch_workgroups(wl):
+    """Workgroups of the automatic launch of one step of `wl` with every pair
+    full (one lf_probe_decode_timing call on a fresh cache)."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache, lf_probe_decode_timing
+    from decode_kv_cache_02_amd.synth import device_prefill, device_steps
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                          dtype=wl.dtype)
+    try:
+        k, v = device_prefill(wl, wl.budget, seed=3)
+        cache.prefill(0, k, v, np.full(wl.batch, wl.budget, dtype=np.int32))
+        del k, v
+        Q, KN, VN = device_steps(wl, 1, seed=3)
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=Q.dtype, device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        rec = torch.zeros((max(4096, wl.batch * wl.num_kv_heads), 4), dtype=torch.int64, device="cuda")
+        n = lf_probe_decode_timing(cache.handle, 0, Q[0], KN[0], VN[0], out, ev, rec)
+        torch.cuda.synchronize()
+        return n
+    finally:
+        cache.close()
+
+
+def batch_sweep(args):
+    """The Llama-8B layer (B = 3277, every pair full) at every batch of
+    SWEEP_BATCHES with the automatic launch: one JSON line per batch (median
+    of 5 windows x 200 steps, and the launch's workgroup count)."""
+    from decode_kv_cache_02_amd.synth import WORKLOADS
+    w3 = WORKLOADS["llama8b_layer"]
+    for b in SWEEP_BATCHES:
+        w = w3.with_(batch=b)
+        ms, nb, win = steady_state(w, 200, 20)
+        print(json.dumps({"batch": b, "pairs": b * w.num_kv_heads, "workgroups": launch_workgroups(w),
+                          "us_per_step": ms * 1e3, "us_per_pair": ms * 1e3 / (b * w.num_kv_heads),
+                          "tokens_per_s": b / ms * 1e3, "achieved_GBs": nb / ms / 1e6,
+                          "frac_of_peak": nb / ms / 1e6 / HBM_PEAK_GBS, "ms_windows": win}), flush=True)
+
+
 def tiny_latency(wl, steps: int = 2000, per_graph: int = 64):
     """The launch-latency-bound tiny workload (one pair, B = 64, fp32): steps/s
     with one lf_decode_step call per step, and with 64 steps captured in one
@@ -995,6 +1039,11 @@ def main():
         import torch
         torch.cuda.set_device(0)
         wg_timing(args)
+        return
+    if args.batch_sweep:
+        import torch
+        torch.cuda.set_device(0)
+        batch_sweep(args)
         return
     if args.stack_trajectory:
         import torch
