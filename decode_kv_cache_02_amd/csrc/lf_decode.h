@@ -387,7 +387,8 @@ __device__ __forceinline__ void phase_stamp(const DecodeParams& P, int tid, int 
 // atomic accesses: each is coherent across the XCDs on its own, so no
 // whole-cache writeback or invalidate is needed. The writer drains its
 // stores before it takes its ticket, and the last split reads only after
-// its ticket says every other split has arrived.
+// its ticket says every other split has arrived. tests/test_asm_ordering.py
+// checks that order on every path of every built kernel.
 __device__ __forceinline__ void ws_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1485,6 +1486,14 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
         for (int w = 1; w < WAVES; ++w)
           key_min(bh, bl, __float_as_uint(sh_best_score[w]), static_cast<uint32_t>(sh_best_slot[w]));
         choice = static_cast<int>(bl);
+        // Heads past the first NT have their ||v_new|| read and stored here,
+        // inside the decision, so every read of another workgroup's data
+        // follows the ticket on every path through the code (the first NT
+        // were prefetched above and are stored with the rows below).
+        if (!deferred && choice >= 0 && choice < P.budget)
+          for (int hh = tid + NT; hh < hk; hh += NT)
+            P.vnorm[(static_cast<int64_t>(b) * hk + hh) * slots_pad + choice] =
+                ws_load(P.ws_nnorm + static_cast<int64_t>(b) * hk + hh);
         if (tid == 0)
           __hip_atomic_store(P.seq_arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -1521,11 +1530,9 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
                                : load16(static_cast<const T*>(P.v_new) + pr * D + (j - kRowLoads) * EPL));
           }
         }
-        // Every head's ||v_new|| at the victim slot (heads past the first NT
-        // read theirs now; the first NT were prefetched).
-        for (int hh = tid; hh < hk; hh += NT)
-          P.vnorm[(static_cast<int64_t>(b) * hk + hh) * slots_pad + choice] =
-              hh == tid ? pre_norm : ws_load(P.ws_nnorm + static_cast<int64_t>(b) * hk + hh);
+        // The first NT heads' ||v_new|| at the victim slot (prefetched).
+        if (tid < hk)
+          P.vnorm[(static_cast<int64_t>(b) * hk + tid) * slots_pad + choice] = pre_norm;
       }
       for (int hh = tid; hh < hk; hh += NT) P.evicted[static_cast<int64_t>(b) * hk + hh] = choice;
       return;
