@@ -6,7 +6,9 @@ launches (no memset, no host synchronisation), and its cross-workgroup
 counters are reset by the kernel itself, so it can be captured. The shapes
 cover one workgroup per pair (Llama-8B layer at batch 8), split-K (64 pairs
 of one KV head), a stream launch with cut pairs (520 pairs) and two whole
-pairs per workgroup (816 pairs).
+pairs per workgroup (816 pairs). The split-K shape is also captured through
+lf_decode_step_noalloc, whose workspace is the library's static scratch
+array, against lf_decode_step on the twin.
 """
 import numpy as np
 import pytest
@@ -26,7 +28,8 @@ def _dev(x, dtype):
     return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
 
 
-@pytest.mark.parametrize("shape", ["llama_batch8", "tp8_split", "stream_b65", "units_b102"])
+@pytest.mark.parametrize("shape", ["llama_batch8", "tp8_split", "stream_b65", "units_b102",
+                                   "tp8_split_noalloc"])
 def test_graph_replay_matches_eager(shape):
     import torch
     if not torch.cuda.is_available():
@@ -35,7 +38,7 @@ def test_graph_replay_matches_eager(shape):
     if shape == "llama_batch8":
         wl = WORKLOADS["llama8b_layer"].with_(batch=8, prefill=3277)
         layers = 3
-    elif shape == "tp8_split":   # 64 pairs of one KV head: split-K launch with counters
+    elif shape in ("tp8_split", "tp8_split_noalloc"):  # 64 pairs of one KV head: split-K with counters
         wl = WORKLOADS["llama8b_layer"].with_(batch=64, num_q_heads=4, num_kv_heads=1,
                                               prefill=3277)
         layers = 2
@@ -45,6 +48,7 @@ def test_graph_replay_matches_eager(shape):
     else:                        # 816 pairs: two whole pairs per workgroup
         wl = WORKLOADS["llama8b_layer"].with_(batch=102, budget=512, prefill=512)
         layers = 2
+    noalloc = shape.endswith("_noalloc")  # the captured cache steps without allocating
     _say(f"graph capture, {shape}: {layers} layers, 12 replays")
     caches = [LongFlowCache(layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                             wl.budget, dtype=wl.dtype) for _ in range(2)]
@@ -79,7 +83,8 @@ def test_graph_replay_matches_eager(shape):
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for layer in range(layers):
-                caches[0].decode_step(layer, q_s, kn_s, vn_s, outs[layer], evs[layer])
+                caches[0].decode_step(layer, q_s, kn_s, vn_s, outs[layer], evs[layer],
+                                      noalloc=noalloc)
         torch.cuda.current_stream().wait_stream(side)
         for layer in range(layers):
             caches[1].decode_step(layer, q_s, kn_s, vn_s, out_e, ev_e)
@@ -88,7 +93,8 @@ def test_graph_replay_matches_eager(shape):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for layer in range(layers):
-                caches[0].decode_step(layer, q_s, kn_s, vn_s, outs[layer], evs[layer])
+                caches[0].decode_step(layer, q_s, kn_s, vn_s, outs[layer], evs[layer],
+                                      noalloc=noalloc)
 
         for t in range(1, 13):
             load(steps[t])
