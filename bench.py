@@ -366,6 +366,57 @@ def steady_state(wl, steps, warmup, fill=None, mode="evict", layers=1, capacity=
         cache.close()
 
 
+COLD_STEPS = 60
+
+
+def warm_vs_cold(wl, steps: int = COLD_STEPS, read_bytes: int = 1 << 30):
+    """Every pair full; each decode step timed alone by an event pair, (a) back
+    to back and (b) after a read of `read_bytes` queued just before it (a max
+    reduction over an unrelated buffer: its reads replace what the last-level
+    cache held, and it writes nothing back). Returns (median us back to back,
+    median us after the read, algorithmic bytes per step). The per-step events
+    cost a little, so both figures sit slightly above the windowed
+    steady-state line."""
+    import torch
+    from decode_kv_cache_02_amd.native import LongFlowCache
+    from decode_kv_cache_02_amd.synth import device_prefill
+    e = 2 if wl.dtype == "bf16" else 4
+    src = torch.ones(read_bytes // 2, dtype=torch.float16, device="cuda")
+    sink = torch.empty((), dtype=torch.float16, device="cuda")
+    cache = LongFlowCache(1, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.budget,
+                          dtype=wl.dtype)
+    try:
+        k, v = device_prefill(wl, wl.budget, seed=5)
+        cache.prefill(0, k, v, np.full(wl.batch, wl.budget, dtype=np.int32))
+        del k, v
+        ring = make_ring(wl, wl.dtype)
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=ring[0][0].dtype,
+                          device="cuda")
+        ev = torch.empty((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+        args = prepared_ring(cache, ring, out, ev)
+        med = {}
+        for cold in (False, True, False, True):
+            for t in range(10):
+                cache.step_prepared(args[t % RING][0])
+            marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(steps)]
+            torch.cuda.synchronize()
+            for t, (a, b) in enumerate(marks):
+                if cold:
+                    torch.amax(src, dim=0, out=sink)
+                a.record()
+                cache.step_prepared(args[t % RING][0])
+                b.record()
+            torch.cuda.synchronize()
+            med.setdefault(cold, []).append(float(np.median([a.elapsed_time(b) * 1e3 for a, b in marks])))
+        nb = wl.batch * wl.num_kv_heads * algorithmic_bytes_per_pair(wl.budget, wl.group, wl.head_dim,
+                                                                       e, True)
+        return float(np.mean(med[False])), float(np.mean(med[True])), nb
+    finally:
+        cache.close()
+        del src, sink
+
+
 def churn(wl, steps, warmup, every=16, per_event=4, prompt=512):
     """Serving churn over the static buffer: start with every pair full; every
     `every` steps, `per_event` sequences (round robin) finish and their slots
@@ -715,7 +766,7 @@ def batch_gain(wl, model_steps):
 
 
 SUITE_PARTS = ("tiny", "qwen06", "llama", "generation", "variants", "churn", "small", "ragged",
-               "gain", "qwen_b512", "qwen_b1024", "qwen_b2048", "qwen_b4096", "qwen_graph")
+               "gain", "qwen_b512", "qwen_b1024", "qwen_b2048", "qwen_b4096", "qwen_graph", "cold")
 
 
 def suite(args):
@@ -845,6 +896,21 @@ def suite_part(part, args):
         w = wl5.with_(budget=budget)
         ms, nb, win = steady_state(w, 512, 3, layers=36, seed=5)
         emit(f"qwen3_8b_stack36 B={budget}", w, ms, nb, 36, windows=win, steps=512)
+    elif part == "cold":
+        # one layer stepped back to back can keep part of its bytes in the
+        # 256 MB last-level cache; in a model the other layers' reads replace
+        # them between two steps of one layer
+        for label, w in (("llama8b_layer", wl3), ("llama8b_layer tp8 shard", wl3.with_(num_q_heads=4, num_kv_heads=1)),
+                         ("llama8b_layer batch 1", wl3.with_(batch=1)),
+                         ("llama8b_layer batch 4", wl3.with_(batch=4)),
+                         ("llama8b_layer batch 16", wl3.with_(batch=16)),
+                         ("qwen3_0p6b_layer", WORKLOADS["qwen3_0p6b_layer"]),
+                         ("qwen3_8b layer B=512", wl5.with_(budget=512))):
+            warm_us, cold_us, nb = warm_vs_cold(w)
+            emit(f"{label}, each step timed alone after a 1 GiB read (last-level cache cold)", w,
+                 cold_us * 1e-3, nb, extra={"back_to_back_us_each_step_timed_alone": warm_us,
+                                            "cold_over_back_to_back": cold_us / warm_us},
+                 steps=COLD_STEPS)
     elif part == "qwen_graph":
         w = wl5.with_(budget=512)
         ms, nb, win = stack_graph(w, 36, 512, seed=5)
