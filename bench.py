@@ -1211,9 +1211,20 @@ def main():
     ceiling = stream_read_ceiling(int(bytes_launch))
     print(f"[bench] streaming-read ceiling: {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
     full = None
+    llc = None
     if not args.no_full_kv:
         full = full_kv_baseline(wl, min(args.steps, 200), 10)
         print(f"[bench] full-KV: {json.dumps(full['at_fill'])}", file=sys.stderr, flush=True)
+        # does the measured layer owe anything to the last-level cache? (in a
+        # model, other layers' reads pass between two steps of one layer)
+        warm_us, cold_us, _ = warm_vs_cold(wl)
+        llc = {"back_to_back_us": warm_us, "after_1GiB_read_us": cold_us,
+               "ratio": cold_us / warm_us,
+               "note": "each step timed alone by an event pair, back to back and right after a "
+                       "1 GiB read of an unrelated buffer (256 MB last-level cache cold); "
+                       "not part of value"}
+        print(f"[bench] last-level cache: {warm_us:.1f} us back to back, {cold_us:.1f} us cold",
+              file=sys.stderr, flush=True)
     mem_clock_khz, bus_bits = lf_probe_hbm_attributes()
     per_transfer = mem_clock_khz * 1e3 * bus_bits / 8 / 1e9     # GB/s at one transfer per clock
     line = {
@@ -1257,6 +1268,7 @@ def main():
             "kernel": "lf_probe_stream_read: the decode kernel's 16-byte non-temporal buffer loads, "
                       "512 workgroups over the same bytes as one launch"},
         "full_kv": full,
+        "last_level_cache_check": llc,
     }
     print(json.dumps(line), flush=True)
 
