@@ -55,3 +55,16 @@ def test_committed_counters_match_the_current_kernel_source():
         "profiles/traffic_decode_llama8b_layer.json was measured on another kernel source"
     # calibrated traffic of the Llama-8B layer: within 2% above the algorithmic bytes
     assert 1.0 <= t["hbm_bytes_per_launch"] / 860_622_848 < 1.02
+
+
+def test_every_profile_names_the_current_kernel_source():
+    import glob
+    import os
+    import re
+    stale = []
+    for path in sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "*.md"))):
+        text = open(path).read()
+        for sha in re.findall(r"sha256\[:16\]\s*=\s*([0-9a-f]{16})", text):
+            if sha != bench.kernel_sha():
+                stale.append((os.path.basename(path), sha))
+    assert not stale, f"profiles taken on another kernel source: {stale}"
