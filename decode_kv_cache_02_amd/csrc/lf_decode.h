@@ -108,16 +108,23 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, POLICY);
 }
 
-// K is stored in 16-slot tiles laid out in the order the MFMA B operand is
-// loaded: within tile t (16 rows of D elements), 1 KB block c holds, at byte
-// 16 * (16 * j + r), the 16 bytes of slot 16t + r that cover 16-byte chunk
-// 4c + j of the row. One wave-wide 16-byte load per block then reads 1 KB
-// contiguously and lands in operand order. V stays row-major.
+// K is stored in 16-slot tiles of 1 KB blocks: within tile t (16 rows of D
+// elements), block c holds, at byte 64 * r + 16 * j, the 16 bytes of slot
+// 16t + r that cover 16-byte chunk 4c + j of the row. One wave-wide 16-byte
+// load per block reads the block's 1 KB, and lane l takes byte
+// k_lane_offset(l) = 64 * (l % 16) + 16 * (l / 16), which lands the block
+// in MFMA B-operand order (slot l % 16, k-group l / 16). A slot's row is 4
+// contiguous 64-byte pieces per 4 KB tile (D = 128, bf16), so replacing it
+// in place touches 4 places, not one 16-byte chunk in each of 16 cache
+// lines. V stays row-major.
 template <int ROW_BYTES>
 __device__ __forceinline__ uint32_t k_chunk_offset(int slot, int chunk) {
   return static_cast<uint32_t>(slot >> 4) * (16u * ROW_BYTES) +
          static_cast<uint32_t>(chunk >> 2) * 1024u +
-         static_cast<uint32_t>(((chunk & 3) << 4) + (slot & 15)) * 16u;
+         static_cast<uint32_t>(slot & 15) * 64u + static_cast<uint32_t>(chunk & 3) * 16u;
+}
+__device__ __forceinline__ uint32_t k_lane_offset(int lane) {
+  return 64u * static_cast<uint32_t>(lane & 15) + 16u * static_cast<uint32_t>(lane >> 4);
 }
 
 // G consecutive floats of LDS as one vector access.
@@ -628,7 +635,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
     const __amdgpu_buffer_rsrc_t rK =
         make_rsrc(K, static_cast<uint32_t>((hi + 15) >> 4) * kTileBytes);
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(V, static_cast<uint32_t>(hi) * kRowBytes);
-    const uint32_t kbase = static_cast<uint32_t>(lo >> 4) * kTileBytes + lane * 16u;
+    const uint32_t kbase = static_cast<uint32_t>(lo >> 4) * kTileBytes + k_lane_offset(lane);
     const uint32_t vbase = static_cast<uint32_t>(lo + vsub) * kRowBytes + vcol * kBytes;
     // One set = UA tiles: their K (kChunks loads each) and the V rows of the
     // same slots (kVLoads loads each).
@@ -943,7 +950,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
     // First K tiles go out before anything else.
     u32x4_t kr[UA][kChunks];
     {
-      const uint32_t off0 = static_cast<uint32_t>(lo >> 4) * kTileBytes + lane * 16u;
+      const uint32_t off0 = static_cast<uint32_t>(lo >> 4) * kTileBytes + k_lane_offset(lane);
 #pragma unroll
       for (int u = 0; u < UA; ++u)
 #pragma unroll
@@ -995,7 +1002,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& P, const int uni
       float wmax[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) wmax[g] = -INFINITY;
-      const uint32_t base_off = static_cast<uint32_t>(c0 >> 4) * kTileBytes + lane * 16u;
+      const uint32_t base_off = static_cast<uint32_t>(c0 >> 4) * kTileBytes + k_lane_offset(lane);
       if (c0 > lo) {  // first tiles of a later chunk (the first chunk's are already in flight)
         rK = make_rsrc(K, static_cast<uint32_t>((c0 + cn + 15) >> 4) * kTileBytes);
         rV = make_rsrc(V, static_cast<uint32_t>(c0 + cn) * kRowBytes);

@@ -400,9 +400,9 @@ def untile_k(k_tiled, head_dim: int):
     blocks = head_dim * elem_bytes // 64          # 1 KB blocks per 16-slot tile
     lead = tuple(k_tiled.shape[:-1])
     tiles = k_tiled.shape[-1] // (16 * head_dim)
-    t = k_tiled.reshape(lead + (tiles, blocks, 4, 16, per_chunk))
+    t = k_tiled.reshape(lead + (tiles, blocks, 16, 4, per_chunk))   # tile, block, slot, j, elem
     nd = len(lead)
-    t = t.permute(*range(nd), nd, nd + 3, nd + 1, nd + 2, nd + 4)   # tile, slot, block, j, elem
+    t = t.permute(*range(nd), nd, nd + 2, nd + 1, nd + 3, nd + 4)   # tile, slot, block, j, elem
     return t.reshape(lead + (tiles * 16, head_dim))
 
 

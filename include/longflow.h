@@ -132,11 +132,13 @@ typedef struct {
 
 /* Device addresses and strides of one layer's region (for tests, snapshots).
  *
- * K layout (MFMA operand order). Each pair's K region holds slots_padded/16
- * tiles of 16 slots x head_dim elements (16 * head_dim * elem_bytes bytes).
- * A row is cut into 16-byte chunks (E = 16/elem_bytes elements each). Inside
- * tile t, chunk k of slot 16t + r (r in 0..15) is stored at byte offset
- *     1024 * (k / 4) + 16 * (16 * (k % 4) + r).
+ * K layout (16-slot tiles of 1 KB blocks). Each pair's K region holds
+ * slots_padded/16 tiles of 16 slots x head_dim elements (16 * head_dim *
+ * elem_bytes bytes). A row is cut into 16-byte chunks (E = 16/elem_bytes
+ * elements each). Inside tile t, chunk k of slot 16t + r (r in 0..15) is
+ * stored at byte offset
+ *     1024 * (k / 4) + 64 * r + 16 * (k % 4),
+ * so each 1 KB block holds 16 slots x 64 contiguous bytes of their rows.
  * V is row-major: element (slot i, dim d) of a pair is at i * head_dim + d. */
 typedef struct {
   void* k;              /* [batch][num_kv_heads][slots_padded/16 tiles] cfg.dtype, tiled as above */
